@@ -5,14 +5,12 @@ The compute runs in the HIP library ``libcnhwc.so`` behind a C ABI
 Importing this package loads nothing; the binding is loaded on first use and
 raises if the library has not been built.
 """
+import importlib
+
 __all__ = ["api", "synth"]
 
 
 def __getattr__(name):
-    if name == "api":
-        from . import api
-        return api
-    if name == "synth":
-        from . import synth
-        return synth
+    if name in __all__:
+        return importlib.import_module("." + name, __name__)
     raise AttributeError(name)

@@ -1,0 +1,508 @@
+// Depthwise backward-data convolution (groups = C = K) on the vector ALUs,
+// in the two forms of "feat(rocke): channel-packed and large-filter depthwise
+// dgrad":
+//
+//  * dw_stream (row streaming, small filters, stride 1 or 2): every lane owns
+//    `cpl` adjacent channels of a strip of TW output columns and streams the dY
+//    rows of a TH-row band through registers.  Each dY row feeds the dX rows it
+//    touches; a dX row is rounded and stored as soon as no later dY row reaches
+//    it, so only about R + stride rows of accumulators are live at once (the
+//    loop is fully unrolled and the register allocator recycles the flushed
+//    rows: the circular accumulator slots of the pages, kept in registers).
+//    dY moves as one cpl-wide vector per lane per column, lanes run along the
+//    flattened (column strip, channel) index so a wave's loads are contiguous.
+//  * dw_rotated (stride 1, filters up to 64 a side, non-square, per-axis
+//    padding): a stride-1 depthwise dgrad is the forward correlation of dY with
+//    the filter turned by 180 degrees at padding R-1-pad_h / S-1-pad_w.  A block
+//    owns a tile of dX rows x columns x 8 channels; the dY window of the tile
+//    and the rotated filter are staged in LDS, and each lane accumulates 2 rows
+//    x 8 columns x 2 channels, walking the filter one row pair and 8 columns at
+//    a time so only that slice of the filter sits in registers.  Filter rows
+//    whose dY rows are all padding for a wave's rows are skipped.
+//
+// Arithmetic: pairs of taps along the filter's rows go through one
+// v_dot2_f32_{f16,bf16} (two products of the 16-bit inputs added to an fp32
+// accumulator), so each lane-op does two multiply-adds without packed-fp32
+// instructions; each output is rounded once (RNE) to fp16/bf16.
+#include "device.h"
+#include "internal.h"
+
+#include <string>
+
+namespace cnhwc {
+namespace {
+
+// ============================ row streaming =================================
+
+struct StreamArgs {
+    const void* dy;
+    const void* w;
+    void* dx;
+    uint32_t dy_bytes, w_bytes, dx_bytes;
+    int N, H, W, C, Ho, Wo, pad_h, pad_w;
+    int ncv;          // C / cpl
+    int nstrips;      // column strips of TW
+    int nbands;       // row bands of TH
+    int64_t nthreads;
+};
+
+template <int CPL>
+struct VecT;
+template <> struct VecT<1> { using type = unsigned short; };
+template <> struct VecT<2> { using type = uint32_t; };
+template <> struct VecT<4> { using type = i32x2; };
+template <> struct VecT<8> { using type = i32x4; };
+
+template <int CPL>
+__device__ inline typename VecT<CPL>::type vload(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+    if constexpr (CPL == 1) return buf_load2(r, off);
+    else if constexpr (CPL == 2) return uint32_t(buf_load4(r, off));
+    else if constexpr (CPL == 4) return buf_load8(r, off);
+    else return buf_load16(r, off);
+}
+
+// 16-bit word j of a cpl-wide vector
+template <int CPL>
+__device__ inline uint32_t word_of(const typename VecT<CPL>::type& v, int d) {
+    if constexpr (CPL == 1) return uint32_t(v);
+    else if constexpr (CPL == 2) return v;
+    else return uint32_t(v[d]);
+}
+
+template <typename T, int R, int S, int ST, int CPL, int TW, int TH>
+__global__ __launch_bounds__(256, 2) void dw_stream_kernel(const StreamArgs a) {
+    // leaders: filter rows r with (r mod 2*ST) < ST; each pairs with r + ST
+    constexpr int NL = (R / (2 * ST)) * ST + ((R % (2 * ST)) < ST ? (R % (2 * ST)) : ST);
+    constexpr int VOFF = (S - 1) / ST;               // dY columns left of the strip
+    constexpr int NV = (TW - 1) / ST + VOFF + 1;     // dY columns per strip
+    constexpr int UL0 = -((R - 1) / ST);             // first pair step (relative)
+    constexpr int UL1 = (TH - 1) / ST;               // last pair step
+    constexpr int ND = CPL > 1 ? CPL / 2 : 1;        // 32-bit words per vector
+    using V = typename VecT<CPL>::type;
+
+    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (gid >= a.nthreads) return;
+    const int cv = int(gid % a.ncv);
+    int64_t rest = gid / a.ncv;
+    const int band = int(rest % a.nbands);
+    rest /= a.nbands;
+    const int strip = int(rest % a.nstrips);
+    const int n = int(rest / a.nstrips);
+    const int c0 = cv * CPL;
+
+    // tile origin aligned so (h0 + pad_h) and (w0 + pad_w) are multiples of ST
+    const int h0 = band * TH - (ST > 1 ? (a.pad_h % ST) : 0);
+    const int w0 = strip * TW - (ST > 1 ? (a.pad_w % ST) : 0);
+    const int ub = (h0 + a.pad_h) / ST;
+    const int vb = (w0 + a.pad_w) / ST - VOFF;
+
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
+
+    // weight pairs (W[c][r][t], W[c][r+ST][t]) per leader r, tap t, channel
+    uint32_t wp[NL][S][CPL];
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        const int r = (i / ST) * 2 * ST + (i % ST);
+#pragma unroll
+        for (int t = 0; t < S; ++t)
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) {
+                const uint32_t base = uint32_t(c0 + ch) * (R * S);
+                const uint32_t lo = buf_load2(rw, (base + r * S + t) * 2u);
+                const uint32_t hi = r + ST < R ? uint32_t(buf_load2(rw, (base + (r + ST) * S + t) * 2u)) : 0u;
+                wp[i][t][ch] = lo | (hi << 16);
+            }
+    }
+
+    auto load_row = [&](int u, V (&row)[NV]) {
+        const bool uv = u >= 0 && u < a.Ho;
+#pragma unroll
+        for (int vl = 0; vl < NV; ++vl) {
+            const int v = vb + vl;
+            uint32_t off = kOob;
+            if (uv && v >= 0 && v < a.Wo) off = uint32_t(((n * a.Ho + u) * a.Wo + v) * a.C + c0) * 2u;
+            row[vl] = vload<CPL>(rdy, off);
+        }
+    };
+
+    float acc[TH][TW][CPL];
+#pragma unroll
+    for (int i = 0; i < TH; ++i)
+#pragma unroll
+        for (int j = 0; j < TW; ++j)
+#pragma unroll
+            for (int ch = 0; ch < CPL; ++ch) acc[i][j][ch] = 0.f;
+
+    V prev[NV], cur[NV];
+    load_row(ub + UL0 - 1, prev);
+#pragma unroll
+    for (int ul = UL0; ul <= UL1; ++ul) {
+        load_row(ub + ul, cur);
+        // pairs (dY[u], dY[u-1]) per column and channel
+        uint32_t pr[NV][CPL];
+#pragma unroll
+        for (int vl = 0; vl < NV; ++vl)
+#pragma unroll
+            for (int d = 0; d < ND; ++d) {
+                const uint32_t cw = word_of<CPL>(cur[vl], d), pw = word_of<CPL>(prev[vl], d);
+                if constexpr (CPL == 1) {
+                    pr[vl][0] = (cw & 0xffffu) | (pw << 16);
+                } else {
+                    pr[vl][2 * d] = pair_lo(cw, pw);
+                    pr[vl][2 * d + 1] = pair_hi(cw, pw);
+                }
+            }
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int r = (i / ST) * 2 * ST + (i % ST);
+            const int hl = ST * ul + r;
+            if (hl < 0 || hl >= TH) continue;
+#pragma unroll
+            for (int wl = 0; wl < TW; ++wl)
+#pragma unroll
+                for (int t = 0; t < S; ++t) {
+                    if (((wl - t) % ST + ST) % ST != 0) continue;
+                    const int vl = (wl - t) / ST + VOFF - (((wl - t) < 0 && ((wl - t) % ST) != 0) ? 1 : 0);
+#pragma unroll
+                    for (int ch = 0; ch < CPL; ++ch)
+                        acc[hl][wl][ch] = dot2<T>(pr[vl][ch], wp[i][t][ch], acc[hl][wl][ch]);
+                }
+        }
+        // flush the dX rows no later dY row reaches
+#pragma unroll
+        for (int j = 0; j < ST; ++j) {
+            const int hl = ST * ul + j;
+            if (hl < 0 || hl >= TH) continue;
+            const int h = h0 + hl;
+            if (h < 0 || h >= a.H) continue;
+#pragma unroll
+            for (int wl = 0; wl < TW; ++wl) {
+                const int w = w0 + wl;
+                if (w < 0 || w >= a.W) continue;
+                const uint32_t off = uint32_t(((n * a.H + h) * a.W + w) * a.C + c0) * 2u;
+                if constexpr (CPL == 1) {
+                    buf_store2(pack1<T>(acc[hl][wl][0]), rdx, off);
+                } else if constexpr (CPL == 2) {
+                    buf_store4(int(pack2<T>(acc[hl][wl][0], acc[hl][wl][1])), rdx, off);
+                } else if constexpr (CPL == 4) {
+                    i32x2 o = {int(pack2<T>(acc[hl][wl][0], acc[hl][wl][1])),
+                               int(pack2<T>(acc[hl][wl][2], acc[hl][wl][3]))};
+                    buf_store8(o, rdx, off);
+                } else {
+                    i32x4 o = {int(pack2<T>(acc[hl][wl][0], acc[hl][wl][1])),
+                               int(pack2<T>(acc[hl][wl][2], acc[hl][wl][3])),
+                               int(pack2<T>(acc[hl][wl][4], acc[hl][wl][5])),
+                               int(pack2<T>(acc[hl][wl][6], acc[hl][wl][7]))};
+                    buf_store16(o, rdx, off);
+                }
+            }
+        }
+#pragma unroll
+        for (int vl = 0; vl < NV; ++vl) prev[vl] = cur[vl];
+    }
+}
+
+// The instance table: filter (R = S), stride, channels per lane, strip width
+// and band height.  Register budgets keep every instance free of scratch.
+struct StreamCfg {
+    int r, st, cpl, tw, th;
+};
+constexpr StreamCfg kStream[] = {
+    {3, 1, 8, 2, 16}, {3, 1, 4, 4, 16}, {3, 1, 2, 4, 16}, {3, 1, 1, 8, 16},
+    {5, 1, 4, 2, 16}, {5, 1, 2, 4, 16}, {5, 1, 1, 4, 16},
+    {7, 1, 2, 4, 16}, {7, 1, 1, 4, 16},
+    {3, 2, 8, 2, 16}, {3, 2, 4, 4, 16}, {3, 2, 2, 4, 16}, {3, 2, 1, 8, 16},
+    {5, 2, 4, 2, 16}, {5, 2, 2, 4, 16}, {5, 2, 1, 4, 16},
+    {7, 2, 2, 4, 16}, {7, 2, 1, 4, 16},
+};
+
+const StreamCfg* find_stream(const Prob& p, int cpl) {
+    for (const StreamCfg& c : kStream)
+        if (c.r == p.r && c.r == p.s && c.st == p.stride && c.cpl == cpl) return &c;
+    return nullptr;
+}
+
+template <typename T, int R, int ST, int CPL, int TW, int TH>
+void launch_stream_t(const StreamArgs& a, hipStream_t st) {
+    const int64_t blocks = (a.nthreads + 255) / 256;
+    hipLaunchKernelGGL((dw_stream_kernel<T, R, R, ST, CPL, TW, TH>), dim3(blocks), dim3(256), 0, st, a);
+}
+
+template <typename T>
+bool dispatch_stream(const StreamCfg& c, const StreamArgs& a, hipStream_t st) {
+#define CNHWC_DWS(R_, ST_, CPL_, TW_, TH_)                                                  \
+    if (c.r == R_ && c.st == ST_ && c.cpl == CPL_ && c.tw == TW_ && c.th == TH_) {          \
+        launch_stream_t<T, R_, ST_, CPL_, TW_, TH_>(a, st);                                 \
+        return true;                                                                        \
+    }
+    CNHWC_DWS(3, 1, 8, 2, 16) CNHWC_DWS(3, 1, 4, 4, 16) CNHWC_DWS(3, 1, 2, 4, 16) CNHWC_DWS(3, 1, 1, 8, 16)
+    CNHWC_DWS(5, 1, 4, 2, 16) CNHWC_DWS(5, 1, 2, 4, 16) CNHWC_DWS(5, 1, 1, 4, 16)
+    CNHWC_DWS(7, 1, 2, 4, 16) CNHWC_DWS(7, 1, 1, 4, 16)
+    CNHWC_DWS(3, 2, 8, 2, 16) CNHWC_DWS(3, 2, 4, 4, 16) CNHWC_DWS(3, 2, 2, 4, 16) CNHWC_DWS(3, 2, 1, 8, 16)
+    CNHWC_DWS(5, 2, 4, 2, 16) CNHWC_DWS(5, 2, 2, 4, 16) CNHWC_DWS(5, 2, 1, 4, 16)
+    CNHWC_DWS(7, 2, 2, 4, 16) CNHWC_DWS(7, 2, 1, 4, 16)
+#undef CNHWC_DWS
+    return false;
+}
+
+// ============================ rotated filter ================================
+
+constexpr int kRotCB = 8;      // channels per block
+constexpr int kRotTHT = 2;     // output rows per lane
+constexpr int kRotTWT = 8;     // output columns per lane
+constexpr int kRotTB = 8;      // filter columns per register slice
+constexpr int kRotMaxF = 64;   // largest filter side
+
+struct RotArgs {
+    const void* dy;
+    const void* w;
+    void* dx;
+    uint32_t dy_bytes, w_bytes, dx_bytes;
+    int N, H, W, C, Ho, Wo, R, S;
+    int ph2, pw2;          // rotated padding R-1-pad_h, S-1-pad_w
+    int OHB, OWB;          // output tile of a block
+    int IHB, IWB;          // staged dY window (rows padded to pairs, columns to slices)
+    int rpairs, tslices;   // ceil(R/2), ceil(S/8)
+    int tiles_h, tiles_w, cblocks;
+    int row_dw;            // LDS row stride in 32-bit words
+};
+
+// Block: 256 lanes = 4 channel pairs x 4 column groups (8 columns) x 16 row
+// groups (2 rows): a 32 x 32 x 8 output tile.
+template <typename T>
+__global__ __launch_bounds__(256, 1) void dw_rotated_kernel(const RotArgs a) {
+    extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+    const int tid = threadIdx.x;
+    const int cp = tid & 3, cg = (tid >> 2) & 3, rg = tid >> 4;
+    int bid = blockIdx.x;
+    const int cb = bid % a.cblocks;
+    bid /= a.cblocks;
+    const int tw_ = bid % a.tiles_w;
+    bid /= a.tiles_w;
+    const int th_ = bid % a.tiles_h;
+    const int n = bid / a.tiles_h;
+    const int h0 = th_ * a.OHB, w0 = tw_ * a.OWB, c0 = cb * kRotCB;
+
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
+
+    // ---- stage the dY window: rows h0 - ph2 .., columns w0 - pw2 .., 8 channels ----
+    // word layout: [row][col][4 channel pairs], row stride a.row_dw words
+    uint32_t* win = smem;
+    const int npix = a.IHB * a.IWB;
+    for (int q = tid; q < npix; q += 256) {
+        const int ih = q / a.IWB, iw = q - (q / a.IWB) * a.IWB;
+        const int u = h0 - a.ph2 + ih, v = w0 - a.pw2 + iw;
+        uint32_t off = kOob;
+        if (u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
+            off = uint32_t(((n * a.Ho + u) * a.Wo + v) * a.C + c0) * 2u;
+        const i32x4 val = buf_load16(rdy, off);
+        *reinterpret_cast<i32x4*>(win + ih * a.row_dw + iw * 4) = val;
+    }
+    // ---- stage rotated weight pairs: [rp][t][8 channels] words ----
+    uint32_t* wpl = smem + a.IHB * a.row_dw;
+    const int tpad = a.tslices * kRotTB;
+    const int nwp = a.rpairs * tpad * kRotCB;
+    for (int q = tid; q < nwp; q += 256) {
+        const int ch = q % kRotCB;
+        const int t = (q / kRotCB) % tpad;
+        const int rp = q / (kRotCB * tpad);
+        uint32_t v = 0;
+        if (t < a.S) {
+            const int r0 = 2 * rp, r1 = 2 * rp + 1;   // rotated rows
+            const uint32_t base = uint32_t(c0 + ch) * (a.R * a.S);
+            const uint32_t lo = r0 < a.R ? buf_load2(rw, (base + (a.R - 1 - r0) * a.S + (a.S - 1 - t)) * 2u) : 0u;
+            const uint32_t hi = r1 < a.R ? buf_load2(rw, (base + (a.R - 1 - r1) * a.S + (a.S - 1 - t)) * 2u) : 0u;
+            v = lo | (hi << 16);
+        }
+        wpl[q] = v;
+    }
+    __syncthreads();
+
+    float acc[kRotTHT][kRotTWT][2];
+#pragma unroll
+    for (int i = 0; i < kRotTHT; ++i)
+#pragma unroll
+        for (int j = 0; j < kRotTWT; ++j) acc[i][j][0] = acc[i][j][1] = 0.f;
+
+    // rows of this wave: 4 row groups x 2 rows; skip row pairs that only meet padding
+    const int wave_row0 = (rg & ~3) * kRotTHT;     // first tile row of the wave
+    const int wave_rows = 4 * kRotTHT;
+    int rp_lo = 0, rp_hi = a.rpairs;
+    {
+        // dY row of (tile row i, rotated row r) is h0 - ph2 + i + r; need some in [0, Ho)
+        const int base = h0 + wave_row0 - a.ph2;
+        // largest r with base + wave_rows - 1 + r < 0 -> all below
+        while (rp_lo < rp_hi && base + wave_rows - 1 + 2 * rp_lo + 1 < 0) ++rp_lo;
+        while (rp_hi > rp_lo && base + 2 * (rp_hi - 1) >= a.Ho) --rp_hi;
+    }
+    int ts_lo = 0, ts_hi = a.tslices;
+    {
+        const int base = w0 - a.pw2;
+        while (ts_lo < ts_hi && base + a.OWB - 1 + (ts_lo + 1) * kRotTB - 1 < 0) ++ts_lo;
+        while (ts_hi > ts_lo && base + (ts_hi - 1) * kRotTB >= a.Wo) --ts_hi;
+    }
+    const int orow = rg * kRotTHT, ocol = cg * kRotTWT;
+#pragma unroll 1
+    for (int rp = rp_lo; rp < rp_hi; ++rp) {
+#pragma unroll 1
+        for (int ts = ts_lo; ts < ts_hi; ++ts) {
+            uint32_t w0v[kRotTB], w1v[kRotTB];
+#pragma unroll
+            for (int t = 0; t < kRotTB; ++t) {
+                const i32x2 v = *reinterpret_cast<const i32x2*>(
+                    wpl + (rp * tpad + ts * kRotTB + t) * kRotCB + cp * 2);
+                w0v[t] = uint32_t(v[0]);
+                w1v[t] = uint32_t(v[1]);
+            }
+#pragma unroll
+            for (int i = 0; i < kRotTHT; ++i) {
+                const uint32_t* r0 = win + (orow + i + 2 * rp) * a.row_dw + (ocol + ts * kRotTB) * 4 + cp;
+                const uint32_t* r1 = r0 + a.row_dw;
+                uint32_t p0[kRotTWT + kRotTB - 1], p1[kRotTWT + kRotTB - 1];
+#pragma unroll
+                for (int vl = 0; vl < kRotTWT + kRotTB - 1; ++vl) {
+                    const uint32_t x0 = r0[vl * 4], x1 = r1[vl * 4];
+                    p0[vl] = pair_lo(x0, x1);   // channel 2cp: (row u, row u+1)
+                    p1[vl] = pair_hi(x0, x1);   // channel 2cp+1
+                }
+#pragma unroll
+                for (int j = 0; j < kRotTWT; ++j)
+#pragma unroll
+                    for (int t = 0; t < kRotTB; ++t) {
+                        acc[i][j][0] = dot2<T>(p0[j + t], w0v[t], acc[i][j][0]);
+                        acc[i][j][1] = dot2<T>(p1[j + t], w1v[t], acc[i][j][1]);
+                    }
+            }
+        }
+    }
+    // ---- store: 2 channels per lane ----
+#pragma unroll
+    for (int i = 0; i < kRotTHT; ++i) {
+        const int h = h0 + orow + i;
+        if (orow + i >= a.OHB || h >= a.H) continue;
+#pragma unroll
+        for (int j = 0; j < kRotTWT; ++j) {
+            const int w = w0 + ocol + j;
+            if (ocol + j >= a.OWB || w >= a.W) continue;
+            buf_store4(int(pack2<T>(acc[i][j][0], acc[i][j][1])), rdx,
+                       uint32_t(((n * a.H + h) * a.W + w) * a.C + c0 + cp * 2) * 2u);
+        }
+    }
+}
+
+bool rot_geometry(const Prob& p, RotArgs* a, size_t* lds) {
+    a->OHB = int(std::min<int64_t>(32, p.h));
+    a->OWB = int(std::min<int64_t>(32, p.w));
+    a->rpairs = int((p.r + 1) / 2);
+    a->tslices = int((p.s + kRotTB - 1) / kRotTB);
+    // rows: tile rows + 2*rpairs (pairs reach row i + 2rp + 1); columns: tile + padded slices
+    a->IHB = 32 + 2 * a->rpairs;
+    a->IWB = 32 + a->tslices * kRotTB;
+    a->row_dw = a->IWB * 4 + 4;
+    const size_t win = size_t(a->IHB) * a->row_dw * 4;
+    const size_t wts = size_t(a->rpairs) * a->tslices * kRotTB * kRotCB * 4;
+    *lds = win + wts;
+    return *lds <= 160 * 1024;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+
+int dw_stream_best_cpl(const Prob& p) {
+    // widest vector that divides the channels, preferring the table's order
+    static const int order[] = {8, 4, 2, 1};
+    for (int c : order)
+        if (p.c % c == 0 && find_stream(p, c)) return c;
+    return 0;
+}
+
+std::string dw_stream_reason(const Prob& p, int cpl) {
+    if (!(p.groups == p.c && p.groups == p.k)) return "depthwise kernels need groups == C == K";
+    if (cpl != 1 && cpl != 2 && cpl != 4 && cpl != 8) return "cpl must be 1, 2, 4 or 8";
+    if (p.c % cpl != 0) return "channels must be a multiple of cpl";
+    if (p.r != p.s) return "row-streaming instances are square filters";
+    if (p.stride > 2) return "row streaming supports stride 1 or 2";
+    if (!find_stream(p, cpl))
+        return "no row-streaming instance for filter " + std::to_string(p.r) + " stride " +
+               std::to_string(p.stride) + " cpl " + std::to_string(cpl) +
+               " (register budget: filter <= 7; cpl 8 only at 3x3, cpl 4 up to 5x5)";
+    if (p.n * p.h * p.w * p.c > (int64_t(1) << 30)) return "tensor exceeds the 32-bit element range";
+    return "";
+}
+
+std::string dw_rotated_reason(const Prob& p) {
+    if (!(p.groups == p.c && p.groups == p.k)) return "depthwise kernels need groups == C == K";
+    if (p.stride != 1) return "the rotated-filter dgrad needs stride 1";
+    if (p.r > kRotMaxF || p.s > kRotMaxF) return "the rotated-filter dgrad takes filters up to 64 a side";
+    if (p.pad_h > p.r - 1 || p.pad_w > p.s - 1)
+        return "the rotated-filter dgrad needs pad_h <= R-1 and pad_w <= S-1";
+    if (p.c % kRotCB != 0) return "the rotated-filter dgrad needs C a multiple of 8";
+    RotArgs a{};
+    size_t lds;
+    if (!rot_geometry(p, &a, &lds)) return "staged dY window exceeds LDS";
+    if (p.n * p.h * p.w * p.c > (int64_t(1) << 30)) return "tensor exceeds the 32-bit element range";
+    return "";
+}
+
+int launch_dgrad_dw_stream(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
+                           hipStream_t st) {
+    const StreamCfg* c = find_stream(p, pl.cpl);
+    if (!c) return CNHWC_UNSUPPORTED;
+    StreamArgs a{};
+    a.dy = dy; a.w = w; a.dx = dx;
+    a.dy_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
+    a.w_bytes = uint32_t(p.k * p.r * p.s * 2);
+    a.dx_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
+    a.N = int(p.n); a.H = int(p.h); a.W = int(p.w); a.C = int(p.c); a.Ho = int(p.ho); a.Wo = int(p.wo);
+    a.pad_h = p.pad_h; a.pad_w = p.pad_w;
+    a.ncv = int(p.c / c->cpl);
+    const int st_ = p.stride;
+    const int wext = int(p.w) + (st_ > 1 ? p.pad_w % st_ : 0);
+    const int hext = int(p.h) + (st_ > 1 ? p.pad_h % st_ : 0);
+    a.nstrips = (wext + c->tw - 1) / c->tw;
+    a.nbands = (hext + c->th - 1) / c->th;
+    a.nthreads = int64_t(a.N) * a.nstrips * a.nbands * a.ncv;
+    const bool ok = p.dtype == CNHWC_BF16 ? dispatch_stream<BF16>(*c, a, st) : dispatch_stream<F16>(*c, a, st);
+    return ok ? CNHWC_OK : CNHWC_UNSUPPORTED;
+}
+
+int launch_dgrad_dw_rotated(const Prob& p, const Plan&, const void* dy, const void* w, void* dx,
+                            hipStream_t st) {
+    RotArgs a{};
+    size_t lds;
+    if (!rot_geometry(p, &a, &lds)) return CNHWC_UNSUPPORTED;
+    a.dy = dy; a.w = w; a.dx = dx;
+    a.dy_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
+    a.w_bytes = uint32_t(p.k * p.r * p.s * 2);
+    a.dx_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
+    a.N = int(p.n); a.H = int(p.h); a.W = int(p.w); a.C = int(p.c); a.Ho = int(p.ho); a.Wo = int(p.wo);
+    a.R = int(p.r); a.S = int(p.s);
+    a.ph2 = int(p.r) - 1 - p.pad_h;
+    a.pw2 = int(p.s) - 1 - p.pad_w;
+    a.tiles_h = int((p.h + a.OHB - 1) / a.OHB);
+    a.tiles_w = int((p.w + a.OWB - 1) / a.OWB);
+    a.cblocks = int(p.c / kRotCB);
+    const int64_t blocks = int64_t(a.N) * a.tiles_h * a.tiles_w * a.cblocks;
+    // dynamic LDS above 64 KiB must be opted into per kernel
+    static bool attr_set[2] = {false, false};
+    const int which = p.dtype == CNHWC_BF16 ? 1 : 0;
+    if (!attr_set[which]) {
+        const void* fn = which ? reinterpret_cast<const void*>(&dw_rotated_kernel<BF16>)
+                               : reinterpret_cast<const void*>(&dw_rotated_kernel<F16>);
+        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+            return CNHWC_HIP_ERROR;
+        attr_set[which] = true;
+    }
+    if (which)
+        hipLaunchKernelGGL(dw_rotated_kernel<BF16>, dim3(blocks), dim3(256), lds, st, a);
+    else
+        hipLaunchKernelGGL(dw_rotated_kernel<F16>, dim3(blocks), dim3(256), lds, st, a);
+    return CNHWC_OK;
+}
+
+}  // namespace cnhwc

@@ -1,0 +1,656 @@
+// Direct forward convolution on the gfx950 matrix cores with the input tile and
+// its halo staged in LDS ("feat(rocke): split-C and grouped LDS-halo direct
+// conv fwd kernels"):
+//
+//  * fwd_direct: a block owns an output tile of NB images x TH rows x TW
+//    columns (<= 128 pixels, the MFMA M side) and BN = 64 output channels.
+//    Per 64-channel chunk the input window ((TH-1)*s+R) x ((TW-1)*s+S) of those
+//    channels is loaded into LDS once and every filter tap reads a shifted
+//    window of it; the weight slice of the tap streams through LDS.  Both
+//    operands are channel-contiguous, which is what the MFMA reduction wants,
+//    so nothing is transposed.
+//  * split_c: the same kernel with the channel loop split across blocks
+//    (grid axis = split index); each split writes its fp32 partial tile to a
+//    workspace [split][pixel][k] and a second pass, split_reduce, sums the
+//    splits in ascending order and rounds once.  This fills the GPU when the
+//    output has too few tiles (small maps, deep channels).
+//  * grouped merge: with few channels per group, G_m = 32/Cg groups are merged
+//    into one MFMA problem -- 32 input channels x G_m*Kg output channels --
+//    whose per-tap weight tile is block-diagonal (zero off the group blocks),
+//    so one MFMA covers several groups instead of leaving most of the tile idle.
+//
+// Block ids are remapped so that the blocks sharing one weight slice run on the
+// same XCD (blocks are dealt to the 8 XCDs round-robin; each XCD has its own
+// L2).  Out-of-image pixels and out-of-range channels read zero through the
+// buffer descriptors' range check.
+#include "device.h"
+#include "internal.h"
+
+#include <algorithm>
+#include <string>
+
+namespace cnhwc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kBM = 128;          // output pixels per block (MFMA M)
+constexpr int kBN = 64;           // output channels per block (direct)
+constexpr int kBKc = 64;          // input channels per LDS stage (direct)
+constexpr int kHaloMax = 336;     // halo pixels per stage (42 KiB at 128 B/pixel)
+constexpr int kHaloSlots = (kHaloMax * 8 + kThreads - 1) / kThreads;
+
+struct Geo {
+    int NB, TH, TW;   // tile: images x rows x columns
+    int IH, IW;       // halo rows / columns
+    int ptiles_h, ptiles_w, ptiles_n;
+};
+
+struct FwdArgs {
+    const void* x;
+    const void* w;
+    void* y;          // output (unsplit) or fp32 workspace (split)
+    uint32_t x_bytes, w_bytes, y_bytes;
+    int N, H, W, C, K, R, S, stride, pad_h, pad_w, Ho, Wo, Cg, Kg, G;
+    Geo geo;
+    int ntiles;       // output-channel tiles per group
+    int splits, csplit;   // channel splits and channels per split
+    int nblocks;
+    int remap;
+};
+
+__device__ inline uint32_t swz(int row, int chunk) { return uint32_t((chunk ^ (row & 7)) * 16); }
+
+// Decode a tile index into its first image / output row / output column.
+__device__ inline void tile_origin(const Geo& g, int pt, int& n0, int& ho0, int& wo0) {
+    const int tw = pt % g.ptiles_w;
+    const int rest = pt / g.ptiles_w;
+    const int th = rest % g.ptiles_h;
+    n0 = (rest / g.ptiles_h) * g.NB;
+    ho0 = th * g.TH;
+    wo0 = tw * g.TW;
+}
+
+template <typename T, bool SPLIT>
+__global__ __launch_bounds__(kThreads, 2) void fwd_direct_kernel(const FwdArgs a) {
+    constexpr int HALO_BYTES = kHaloMax * 128;
+    constexpr int B_BYTES = kBN * 128;
+    constexpr int STAGE = HALO_BYTES + B_BYTES;
+    constexpr int WM = kBM / 2, WN = kBN / 2, FM = WM / 16, FN = WN / 16;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Geo& geo = a.geo;
+
+    int bid = blockIdx.x;
+    if (a.remap) bid = (bid & 7) * (a.nblocks >> 3) + (bid >> 3);
+    const int ptiles = geo.ptiles_n * geo.ptiles_h * geo.ptiles_w;
+    const int pt = bid % ptiles;
+    int rest = bid / ptiles;
+    const int nt = rest % a.ntiles;
+    rest /= a.ntiles;
+    const int g = rest % a.G;
+    const int sp = rest / a.G;
+    int n0, ho0, wo0;
+    tile_origin(geo, pt, n0, ho0, wo0);
+    const int k0 = nt * kBN;                 // within the group
+    const int c_lo = sp * a.csplit;          // within the group
+    const int c_hi = min(a.Cg, c_lo + a.csplit);
+    const int s = a.stride;
+
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
+
+    // halo slots of this thread: chunk (tid & 7) of halo pixels tid/8 + 32 j
+    const int hchunk = tid & 7;
+    const int hpix = geo.NB * geo.IH * geo.IW;
+    int hoff[kHaloSlots];
+#pragma unroll
+    for (int j = 0; j < kHaloSlots; ++j) {
+        const int hp = (tid >> 3) + j * (kThreads / 8);
+        hoff[j] = -1;
+        if (hp < hpix) {
+            const int per = geo.IH * geo.IW;
+            const int nb = hp / per;
+            const int rem = hp - nb * per;
+            const int ih = rem / geo.IW, iw = rem - (rem / geo.IW) * geo.IW;
+            const int n = n0 + nb;
+            const int h = ho0 * s - a.pad_h + ih, w = wo0 * s - a.pad_w + iw;
+            if (n < a.N && h >= 0 && h < a.H && w >= 0 && w < a.W)
+                hoff[j] = ((n * a.H + h) * a.W + w) * a.C + g * a.Cg;
+        }
+    }
+    // weight rows of this thread: chunk (tid & 7) of rows tid/8 + 32 j
+    const int taps = a.R * a.S;
+    const int cchunks = (c_hi - c_lo + kBKc - 1) / kBKc;
+    const int steps = cchunks * taps;
+
+    i32x4 rh[kHaloSlots];
+    i32x4 rb[2];
+
+    auto load_halo = [&](int cc) {
+        const int c = c_lo + cc * kBKc + hchunk * 8;
+#pragma unroll
+        for (int j = 0; j < kHaloSlots; ++j) {
+            const uint32_t off = (hoff[j] >= 0 && c < c_hi) ? uint32_t(hoff[j] + c) * 2u : kOob;
+            rh[j] = buf_load16(rx, off);
+        }
+    };
+    auto load_w = [&](int cc, int tap) {
+        const int c = c_lo + cc * kBKc + hchunk * 8;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int kr = (tid >> 3) + j * 32;
+            const int k = k0 + kr;
+            uint32_t off = kOob;
+            if (k < a.Kg && c < c_hi)
+                off = uint32_t(((g * a.Kg + k) * taps + tap) * a.Cg + c) * 2u;
+            rb[j] = buf_load16(rw, off);
+        }
+    };
+    auto store_halo = [&](int buf) {
+        unsigned char* hs = lds + buf * STAGE;
+#pragma unroll
+        for (int j = 0; j < kHaloSlots; ++j) {
+            const int hp = (tid >> 3) + j * (kThreads / 8);
+            if (hp < hpix) *reinterpret_cast<i32x4*>(hs + hp * 128 + swz(hp, hchunk)) = rh[j];
+        }
+    };
+    auto store_w = [&](int buf) {
+        unsigned char* bs = lds + buf * STAGE + HALO_BYTES;
+#pragma unroll
+        for (int j = 0; j < 2; ++j) {
+            const int kr = (tid >> 3) + j * 32;
+            *reinterpret_cast<i32x4*>(bs + kr * 128 + swz(kr, hchunk)) = rb[j];
+        }
+    };
+
+    // fragment rows: output pixel -> base halo index (tap 0)
+    const int wm = wave >> 1, wn = wave & 1;
+    const int frow = lane & 15, fgrp = lane >> 4;
+    const int tile_pix = geo.NB * geo.TH * geo.TW;
+    int fbase[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        int m = wm * WM + i * 16 + frow;
+        if (m >= tile_pix) m = 0;
+        const int per = geo.TH * geo.TW;
+        const int nb = m / per;
+        const int rem = m - nb * per;
+        const int th = rem / geo.TW, tw = rem - (rem / geo.TW) * geo.TW;
+        fbase[i] = nb * geo.IH * geo.IW + th * s * geo.IW + tw * s;
+    }
+
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto compute = [&](int buf, int tap) {
+        const unsigned char* hs = lds + buf * STAGE;
+        const unsigned char* bs = hs + HALO_BYTES;
+        const int r = tap / a.S, t = tap - (tap / a.S) * a.S;
+        const int toff = r * geo.IW + t;
+#pragma unroll
+        for (int ks = 0; ks < kBKc / 32; ++ks) {
+            const int chunk = ks * 4 + fgrp;
+            i32x4 fa[FM], fb[FN];
+#pragma unroll
+            for (int i = 0; i < FM; ++i) {
+                const int hp = fbase[i] + toff;
+                fa[i] = *reinterpret_cast<const i32x4*>(hs + hp * 128 + swz(hp, chunk));
+            }
+#pragma unroll
+            for (int j = 0; j < FN; ++j) {
+                const int kr = wn * WN + j * 16 + frow;
+                fb[j] = *reinterpret_cast<const i32x4*>(bs + kr * 128 + swz(kr, chunk));
+            }
+#pragma unroll
+            for (int i = 0; i < FM; ++i)
+#pragma unroll
+                for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<T>(fb[j], fa[i], acc[i][j]);
+        }
+    };
+
+    // The halo buffer of a stage is only rewritten at a chunk boundary; the
+    // halo in buffer b stays valid for all taps that use buffer b... so the
+    // halo is kept per chunk parity and the weight slice per step parity.
+    if (steps > 0) {
+        load_halo(0);
+        load_w(0, 0);
+        store_halo(0);
+        store_w(0);
+        __syncthreads();
+#pragma unroll 1
+        for (int st = 0; st < steps; ++st) {
+            const int cc = st / taps, tap = st - cc * taps;
+            const bool more = st + 1 < steps;
+            const bool new_chunk = more && tap + 1 == taps;
+            if (more) {
+                if (new_chunk) load_halo(cc + 1);
+                load_w(tap + 1 == taps ? cc + 1 : cc, tap + 1 == taps ? 0 : tap + 1);
+            }
+            // halo of chunk cc sits in buffer (cc & 1); weights of step st in (st & 1)
+            {
+                const unsigned char* hs = lds + (cc & 1) * STAGE;
+                const unsigned char* bs = lds + (st & 1) * STAGE + HALO_BYTES;
+                const int r = tap / a.S, t = tap - (tap / a.S) * a.S;
+                const int toff = r * geo.IW + t;
+#pragma unroll
+                for (int ks = 0; ks < kBKc / 32; ++ks) {
+                    const int chunk = ks * 4 + fgrp;
+                    i32x4 fa[FM], fb[FN];
+#pragma unroll
+                    for (int i = 0; i < FM; ++i) {
+                        const int hp = fbase[i] + toff;
+                        fa[i] = *reinterpret_cast<const i32x4*>(hs + hp * 128 + swz(hp, chunk));
+                    }
+#pragma unroll
+                    for (int j = 0; j < FN; ++j) {
+                        const int kr = wn * WN + j * 16 + frow;
+                        fb[j] = *reinterpret_cast<const i32x4*>(bs + kr * 128 + swz(kr, chunk));
+                    }
+#pragma unroll
+                    for (int i = 0; i < FM; ++i)
+#pragma unroll
+                        for (int j = 0; j < FN; ++j)
+                            acc[i][j] = mfma16x16x32<T>(fb[j], fa[i], acc[i][j]);
+                }
+            }
+            if (more) {
+                if (new_chunk) store_halo((cc + 1) & 1);
+                store_w((st + 1) & 1);
+            }
+            __syncthreads();
+        }
+    }
+    (void)compute;
+
+    // ---- epilogue through LDS: rows = tile pixels, columns = BN channels ----
+    constexpr int ESZ = SPLIT ? 4 : 2;
+    constexpr int C_STRIDE = kBN * ESZ + 16;
+    static_assert(kBM * C_STRIDE <= 2 * STAGE, "epilogue tile fits");
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = wm * WM + i * 16 + frow;
+            const int col = wn * WN + j * 16 + fgrp * 4;
+            if constexpr (SPLIT) {
+                *reinterpret_cast<f32x4*>(lds + row * C_STRIDE + col * 4) = acc[i][j];
+            } else {
+                i32x2 v = {int(pack2<T>(acc[i][j][0], acc[i][j][1])),
+                           int(pack2<T>(acc[i][j][2], acc[i][j][3]))};
+                *reinterpret_cast<i32x2*>(lds + row * C_STRIDE + col * 2) = v;
+            }
+        }
+    __syncthreads();
+    constexpr int CPR = kBN * ESZ / 16;
+    const int64_t mtotal = int64_t(a.N) * a.Ho * a.Wo;
+    for (int q = tid; q < kBM * CPR; q += kThreads) {
+        const int row = q / CPR, cc = q % CPR;
+        if (row >= tile_pix) continue;
+        const int per = geo.TH * geo.TW;
+        const int nb = row / per;
+        const int rem = row - nb * per;
+        const int th = rem / geo.TW, tw = rem - (rem / geo.TW) * geo.TW;
+        const int n = n0 + nb, ho = ho0 + th, wo = wo0 + tw;
+        if (n >= a.N || ho >= a.Ho || wo >= a.Wo) continue;
+        const int kl = k0 + cc * (16 / ESZ);
+        if (kl >= a.Kg) continue;
+        const int pix = (n * a.Ho + ho) * a.Wo + wo;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(lds + row * C_STRIDE + cc * 16);
+        if constexpr (SPLIT) {
+            const int64_t e = (int64_t(sp) * mtotal + pix) * a.K + g * a.Kg + kl;
+            buf_store16(v, ry, uint32_t(e) * 4u);
+        } else {
+            buf_store16(v, ry, uint32_t(pix * a.K + g * a.Kg + kl) * 2u);
+        }
+    }
+}
+
+// y[i] = round(sum over splits, ascending, of ws[split][i]), 4 elements a lane.
+template <typename T>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restrict__ ws,
+                                                           unsigned short* __restrict__ y,
+                                                           int64_t total4, int64_t stride4,
+                                                           int splits) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total4;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        f32x4 s = reinterpret_cast<const f32x4*>(ws)[i];
+        for (int sp = 1; sp < splits; ++sp) {
+            const f32x4 v = reinterpret_cast<const f32x4*>(ws)[i + sp * stride4];
+            s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+        }
+        i32x2 o = {int(pack2<T>(s[0], s[1])), int(pack2<T>(s[2], s[3]))};
+        reinterpret_cast<i32x2*>(y)[i] = o;
+    }
+}
+
+// ---- grouped merge ----------------------------------------------------------
+constexpr int kGBK = 32;          // merged input channels (MFMA reduction)
+constexpr int kGHaloMax = 336;    // halo pixels (64 B each)
+constexpr int kGHaloSlots = (kGHaloMax * 4 + kThreads - 1) / kThreads;
+constexpr int kMaxTaps = 25;
+
+struct GrpArgs {
+    const void* x;
+    const void* w;
+    void* y;
+    uint32_t x_bytes, w_bytes, y_bytes;
+    int N, H, W, C, K, R, S, stride, pad_h, pad_w, Ho, Wo, Cg, Kg, G;
+    int gm;           // groups merged per block
+    int bn;           // gm * Kg output channels per block (multiple of 16, <= 64)
+    int gsets;        // G / gm
+    Geo geo;
+    int nblocks, remap;
+};
+
+template <typename T, int BN>
+__global__ __launch_bounds__(kThreads, 2) void fwd_grouped_kernel(const GrpArgs a) {
+    constexpr int HALO_BYTES = kGHaloMax * 64;
+    constexpr int W_TAP = BN * 64;              // one tap: BN rows x 32 channels
+    constexpr int FM = kBM / 16 / 4;            // 2 row blocks per wave (waves split M)
+    constexpr int FN = BN / 16;
+    __shared__ __attribute__((aligned(16))) unsigned char lds[HALO_BYTES + kMaxTaps * W_TAP];
+    unsigned char* hs = lds;
+    unsigned char* ws = lds + HALO_BYTES;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const Geo& geo = a.geo;
+    int bid = blockIdx.x;
+    if (a.remap) bid = (bid & 7) * (a.nblocks >> 3) + (bid >> 3);
+    const int ptiles = geo.ptiles_n * geo.ptiles_h * geo.ptiles_w;
+    const int pt = bid % ptiles;
+    const int gs = bid / ptiles;
+    int n0, ho0, wo0;
+    tile_origin(geo, pt, n0, ho0, wo0);
+    const int s = a.stride;
+    const int taps = a.R * a.S;
+    const int cbase = gs * a.gm * a.Cg;         // first input channel of the set
+    const int kbase = gs * a.bn;                // first output channel of the set
+
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
+
+    // halo: 4 chunks of 8 channels per pixel
+    const int hpix = geo.NB * geo.IH * geo.IW;
+    const int hchunk = tid & 3;
+#pragma unroll
+    for (int j = 0; j < kGHaloSlots; ++j) {
+        const int hp = (tid >> 2) + j * (kThreads / 4);
+        if (hp >= hpix) continue;
+        const int per = geo.IH * geo.IW;
+        const int nb = hp / per;
+        const int rem = hp - nb * per;
+        const int ih = rem / geo.IW, iw = rem - (rem / geo.IW) * geo.IW;
+        const int n = n0 + nb;
+        const int h = ho0 * s - a.pad_h + ih, w = wo0 * s - a.pad_w + iw;
+        uint32_t off = kOob;
+        if (n < a.N && h >= 0 && h < a.H && w >= 0 && w < a.W)
+            off = uint32_t(((n * a.H + h) * a.W + w) * a.C + cbase + hchunk * 8) * 2u;
+        const i32x4 v = buf_load16(rx, off);
+        *reinterpret_cast<i32x4*>(hs + hp * 64 + (((hchunk ^ (hp & 3))) * 16)) = v;
+    }
+    // block-diagonal weights: row kk (output channel of the set) has the Cg
+    // weights of its group at columns (kk / Kg) * Cg .. +Cg, zeros elsewhere
+    const int wtotal = taps * BN * kGBK;
+    for (int e = tid; e < wtotal; e += kThreads) {
+        const int col = e % kGBK;
+        const int row = (e / kGBK) % BN;
+        const int tap = e / (kGBK * BN);
+        const int gl = row / a.Kg;              // group within the set
+        unsigned short v = 0;
+        if (col / a.Cg == gl && row < a.bn) {
+            const int k = kbase + row;
+            v = buf_load2(rw, uint32_t((k * taps + tap) * a.Cg + (col - gl * a.Cg)) * 2u);
+        }
+        const int chunk = col >> 3;
+        *reinterpret_cast<unsigned short*>(ws + tap * W_TAP + row * 64 +
+                                           ((chunk ^ (row & 3)) * 16) + (col & 7) * 2) = v;
+    }
+    __syncthreads();
+
+    const int frow = lane & 15, fgrp = lane >> 4;
+    const int tile_pix = geo.NB * geo.TH * geo.TW;
+    int fbase[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        int m = wave * (kBM / 4) + i * 16 + frow;
+        if (m >= tile_pix) m = 0;
+        const int per = geo.TH * geo.TW;
+        const int nb = m / per;
+        const int rem = m - nb * per;
+        const int th = rem / geo.TW, tw = rem - (rem / geo.TW) * geo.TW;
+        fbase[i] = nb * geo.IH * geo.IW + th * s * geo.IW + tw * s;
+    }
+    f32x4 acc[FM][FN];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int tap = 0; tap < taps; ++tap) {
+        const int r = tap / a.S, t = tap - (tap / a.S) * a.S;
+        const int toff = r * geo.IW + t;
+        i32x4 fa[FM], fb[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int hp = fbase[i] + toff;
+            fa[i] = *reinterpret_cast<const i32x4*>(hs + hp * 64 + ((fgrp ^ (hp & 3)) * 16));
+        }
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = j * 16 + frow;
+            fb[j] = *reinterpret_cast<const i32x4*>(ws + tap * W_TAP + row * 64 + ((fgrp ^ (row & 3)) * 16));
+        }
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = mfma16x16x32<T>(fb[j], fa[i], acc[i][j]);
+    }
+    __syncthreads();
+    // epilogue: tile [128 pixels][BN] of 16-bit outputs staged in LDS
+    constexpr int C_STRIDE = BN * 2 + 16;
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int row = wave * (kBM / 4) + i * 16 + frow;
+            const int col = j * 16 + fgrp * 4;
+            i32x2 v = {int(pack2<T>(acc[i][j][0], acc[i][j][1])),
+                       int(pack2<T>(acc[i][j][2], acc[i][j][3]))};
+            *reinterpret_cast<i32x2*>(lds + row * C_STRIDE + col * 2) = v;
+        }
+    __syncthreads();
+    constexpr int CPR = BN / 8;
+    for (int q = tid; q < kBM * CPR; q += kThreads) {
+        const int row = q / CPR, cc = q % CPR;
+        if (row >= tile_pix || cc * 8 >= a.bn) continue;
+        const int per = geo.TH * geo.TW;
+        const int nb = row / per;
+        const int rem = row - nb * per;
+        const int th = rem / geo.TW, tw = rem - (rem / geo.TW) * geo.TW;
+        const int n = n0 + nb, ho = ho0 + th, wo = wo0 + tw;
+        if (n >= a.N || ho >= a.Ho || wo >= a.Wo) continue;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(lds + row * C_STRIDE + cc * 16);
+        buf_store16(v, ry, uint32_t(((n * a.Ho + ho) * a.Wo + wo) * a.K + kbase + cc * 8) * 2u);
+    }
+}
+
+// Tile geometry: up to 128 output pixels as NB whole images or TH x TW rows,
+// with a halo of at most `halo_max` pixels.
+bool pick_geo(const Prob& p, int halo_max, Geo* g) {
+    const int64_t ho = p.ho, wo = p.wo, s = p.stride;
+    auto halo = [&](int64_t nb, int64_t th, int64_t tw) {
+        return nb * ((th - 1) * s + p.r) * ((tw - 1) * s + p.s);
+    };
+    int64_t NB = 1, TH = 1, TW = 1;
+    bool whole = false;
+    if (ho * wo <= kBM) {
+        TH = ho; TW = wo;
+        NB = std::max<int64_t>(1, std::min<int64_t>(kBM / (ho * wo), p.n));
+        while (NB > 1 && halo(NB, TH, TW) > halo_max) --NB;
+        whole = halo(NB, TH, TW) <= halo_max;
+    }
+    if (!whole) {
+        // row bands of TH x TW output pixels, shrinking until the halo fits
+        NB = 1;
+        TW = std::min<int64_t>(wo, kBM);
+        TH = std::max<int64_t>(1, std::min<int64_t>(ho, kBM / TW));
+        while (TH > 1 && halo(1, TH, TW) > halo_max) --TH;
+        while (TW > 8 && halo(1, TH, TW) > halo_max) TW -= 8;
+    }
+    if (halo(NB, TH, TW) > halo_max) return false;
+    g->NB = int(NB); g->TH = int(TH); g->TW = int(TW);
+    g->IH = int((TH - 1) * s + p.r);
+    g->IW = int((TW - 1) * s + p.s);
+    g->ptiles_n = int((p.n + NB - 1) / NB);
+    g->ptiles_h = int((ho + TH - 1) / TH);
+    g->ptiles_w = int((wo + TW - 1) / TW);
+    return true;
+}
+
+int64_t ptiles_of(const Geo& g) { return int64_t(g.ptiles_n) * g.ptiles_h * g.ptiles_w; }
+
+bool grouped_shape(const Prob& p, int* gm, int* bn) {
+    if (p.cg > kGBK || kGBK % p.cg != 0) return false;
+    const int m = int(kGBK / p.cg);
+    if (p.groups % m != 0) return false;
+    const int64_t n = int64_t(m) * p.kg;
+    if (n % 16 != 0 || n > 64) return false;
+    *gm = m;
+    *bn = int(n);
+    return true;
+}
+
+}  // namespace
+
+int fwd_direct_channel_chunk() { return kBKc; }
+
+std::string fwd_direct_reason(const Prob& p, int split_c) {
+    if (p.cg % 8 != 0) return "input channels per group must be a multiple of 8";
+    if (p.kg % 8 != 0) return "output channels per group must be a multiple of 8";
+    if (p.h * p.w * p.c > (int64_t(1) << 30) || p.ho * p.wo * p.k > (int64_t(1) << 30))
+        return "one image exceeds the 32-bit element range";
+    Geo g;
+    if (!pick_geo(p, kHaloMax, &g)) return "input halo of the smallest tile exceeds LDS";
+    if (split_c > 1) {
+        if (p.groups != 1) return "split-C needs groups == 1";
+        if (p.c % split_c != 0 || (p.c / split_c) % 8 != 0)
+            return "split-C needs C/split to be a multiple of 8";
+    }
+    return "";
+}
+
+std::string fwd_grouped_reason(const Prob& p) {
+    if (p.groups < 2) return "grouped merge needs groups > 1";
+    int gm, bn;
+    if (!grouped_shape(p, &gm, &bn))
+        return "grouped merge needs C/groups dividing 32, groups a multiple of 32/(C/groups) and "
+               "(32/(C/groups))*(K/groups) a multiple of 16 up to 64";
+    if (p.r * p.s > kMaxTaps) return "grouped merge stages at most 25 filter taps";
+    if (p.c % 8 != 0) return "input channels must be a multiple of 8";
+    if (p.h * p.w * p.c > (int64_t(1) << 30) || p.ho * p.wo * p.k > (int64_t(1) << 30))
+        return "one image exceeds the 32-bit element range";
+    Geo g;
+    if (!pick_geo(p, kGHaloMax, &g)) return "input halo of the smallest tile exceeds LDS";
+    return "";
+}
+
+int64_t fwd_direct_tiles(const Prob& p) {
+    Geo g;
+    if (!pick_geo(p, kHaloMax, &g)) return 0;
+    return ptiles_of(g) * ((p.kg + kBN - 1) / kBN) * p.groups;
+}
+
+// Split the channel loop when the output alone leaves most CUs idle and there
+// are enough channels to share: the largest power of two that keeps the block
+// count within the CU count and at least 128 channels per split.
+int fwd_direct_auto_split(const Prob& p) {
+    if (p.groups != 1) return 1;
+    const int64_t tiles = fwd_direct_tiles(p);
+    if (tiles <= 0 || tiles * 2 > kNumCUs) {
+        if (tiles <= 0 || tiles >= kNumCUs / 2) return 1;
+    }
+    int best = 1;
+    for (int sc = 2; sc <= 64; sc *= 2) {
+        if (tiles * sc > kNumCUs) break;
+        if (p.c % sc != 0 || p.c / sc < 128 || (p.c / sc) % 8 != 0) break;
+        best = sc;
+    }
+    return best;
+}
+
+int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
+                      void* ws, hipStream_t st) {
+    FwdArgs a{};
+    const bool split = pl.variant == CNHWC_VAR_FWD_SPLITC && pl.split_c > 1;
+    if (!pick_geo(p, kHaloMax, &a.geo)) return CNHWC_UNSUPPORTED;
+    a.x = x; a.w = w; a.y = split ? ws : y;
+    a.x_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
+    a.w_bytes = uint32_t(p.k * p.r * p.s * p.cg * 2);
+    const int64_t m = p.n * p.ho * p.wo;
+    a.y_bytes = split ? uint32_t(int64_t(pl.split_c) * m * p.k * 4) : uint32_t(m * p.k * 2);
+    a.N = int(p.n); a.H = int(p.h); a.W = int(p.w); a.C = int(p.c); a.K = int(p.k);
+    a.R = int(p.r); a.S = int(p.s); a.stride = p.stride; a.pad_h = p.pad_h; a.pad_w = p.pad_w;
+    a.Ho = int(p.ho); a.Wo = int(p.wo); a.Cg = int(p.cg); a.Kg = int(p.kg); a.G = p.groups;
+    a.ntiles = int((p.kg + kBN - 1) / kBN);
+    a.splits = split ? pl.split_c : 1;
+    a.csplit = int(p.cg / a.splits);
+    const int64_t blocks = ptiles_of(a.geo) * a.ntiles * a.G * a.splits;
+    a.nblocks = int(blocks);
+    a.remap = (blocks % 8 == 0) ? 1 : 0;
+    const bool bf = p.dtype == CNHWC_BF16;
+    if (split) {
+        if (bf) hipLaunchKernelGGL((fwd_direct_kernel<BF16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL((fwd_direct_kernel<F16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
+        const int64_t total4 = m * p.k / 4;
+        const int64_t grid = std::min<int64_t>((total4 + 255) / 256, int64_t(kNumCUs) * 8);
+        if (bf)
+            hipLaunchKernelGGL(split_reduce_kernel<BF16>, dim3(grid), dim3(256), 0, st,
+                               static_cast<const float*>(ws), static_cast<unsigned short*>(y),
+                               total4, total4, a.splits);
+        else
+            hipLaunchKernelGGL(split_reduce_kernel<F16>, dim3(grid), dim3(256), 0, st,
+                               static_cast<const float*>(ws), static_cast<unsigned short*>(y),
+                               total4, total4, a.splits);
+    } else {
+        if (bf) hipLaunchKernelGGL((fwd_direct_kernel<BF16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+        else hipLaunchKernelGGL((fwd_direct_kernel<F16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+    }
+    return CNHWC_OK;
+}
+
+int launch_fwd_grouped(const Prob& p, const Plan&, const void* x, const void* w, void* y,
+                       hipStream_t st) {
+    GrpArgs a{};
+    if (!pick_geo(p, kGHaloMax, &a.geo)) return CNHWC_UNSUPPORTED;
+    if (!grouped_shape(p, &a.gm, &a.bn)) return CNHWC_UNSUPPORTED;
+    a.x = x; a.w = w; a.y = y;
+    a.x_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
+    a.w_bytes = uint32_t(p.k * p.r * p.s * p.cg * 2);
+    a.y_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
+    a.N = int(p.n); a.H = int(p.h); a.W = int(p.w); a.C = int(p.c); a.K = int(p.k);
+    a.R = int(p.r); a.S = int(p.s); a.stride = p.stride; a.pad_h = p.pad_h; a.pad_w = p.pad_w;
+    a.Ho = int(p.ho); a.Wo = int(p.wo); a.Cg = int(p.cg); a.Kg = int(p.kg); a.G = p.groups;
+    a.gsets = p.groups / a.gm;
+    const int64_t blocks = ptiles_of(a.geo) * a.gsets;
+    a.nblocks = int(blocks);
+    a.remap = (blocks % 8 == 0) ? 1 : 0;
+    const bool bf = p.dtype == CNHWC_BF16;
+#define CNHWC_GRP(BNV)                                                                          \
+    if (a.bn <= BNV) {                                                                          \
+        if (bf) hipLaunchKernelGGL((fwd_grouped_kernel<BF16, BNV>), dim3(blocks), dim3(kThreads), 0, st, a); \
+        else hipLaunchKernelGGL((fwd_grouped_kernel<F16, BNV>), dim3(blocks), dim3(kThreads), 0, st, a);     \
+        return CNHWC_OK;                                                                        \
+    }
+    CNHWC_GRP(32)
+    CNHWC_GRP(64)
+#undef CNHWC_GRP
+    return CNHWC_UNSUPPORTED;
+}
+
+}  // namespace cnhwc

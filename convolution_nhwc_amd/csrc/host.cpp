@@ -1,0 +1,402 @@
+// C ABI of libcnhwc: descriptor validation, output extents, the dispatcher,
+// the batch-chunk planner and the launch loop.  No device code lives here.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "internal.h"
+
+namespace cnhwc {
+namespace {
+
+thread_local std::string g_err;
+thread_local cnhwc_override g_ov = {0, 0, 0, 0, 0};
+
+int fail(int status, const std::string& why) {
+    g_err = why;
+    return status;
+}
+
+constexpr int64_t kMaxDim = (int64_t(1) << 31) - 1;
+
+// Checks in a fixed order; the first failure is reported ("feat(rocke):
+// channel-packed and large-filter depthwise dgrad", C++ engine: validators
+// refuse with ordered reason text).
+int validate(const cnhwc_problem* in, Prob* out) {
+    if (!in) return fail(CNHWC_INVALID_ARG, "problem descriptor is NULL");
+    const cnhwc_problem& q = *in;
+    if (q.reserved != 0) return fail(CNHWC_INVALID_ARG, "reserved field must be 0");
+    const int64_t dims[7] = {q.n, q.h, q.w, q.c, q.k, q.r, q.s};
+    const char* names[7] = {"n", "h", "w", "c", "k", "r", "s"};
+    for (int i = 0; i < 7; ++i) {
+        if (dims[i] < 1)
+            return fail(CNHWC_INVALID_ARG, std::string(names[i]) + " must be >= 1 (got " +
+                                               std::to_string(dims[i]) + ")");
+        if (dims[i] > kMaxDim)
+            return fail(CNHWC_INVALID_ARG, std::string(names[i]) + " must be < 2^31");
+    }
+    if (q.stride < 1)
+        return fail(CNHWC_INVALID_ARG, "stride must be >= 1 (got " + std::to_string(q.stride) + ")");
+    if (q.pad_h < 0 || q.pad_w < 0)
+        return fail(CNHWC_INVALID_ARG, "padding must be >= 0 (got " + std::to_string(q.pad_h) +
+                                           "x" + std::to_string(q.pad_w) + ")");
+    if (q.groups < 1)
+        return fail(CNHWC_INVALID_ARG, "groups must be >= 1 (got " + std::to_string(q.groups) + ")");
+    if (q.c % q.groups != 0 || q.k % q.groups != 0)
+        return fail(CNHWC_INVALID_ARG, "c and k must be multiples of groups (c=" +
+                                           std::to_string(q.c) + " k=" + std::to_string(q.k) +
+                                           " groups=" + std::to_string(q.groups) + ")");
+    if (q.dtype != CNHWC_F16 && q.dtype != CNHWC_BF16)
+        return fail(CNHWC_INVALID_ARG, "dtype must be CNHWC_F16 or CNHWC_BF16");
+    const int64_t hn = q.h + 2 * int64_t(q.pad_h) - q.r;
+    const int64_t wn = q.w + 2 * int64_t(q.pad_w) - q.s;
+    if (hn < 0 || wn < 0)
+        return fail(CNHWC_INVALID_ARG, "filter larger than the padded input (no output pixel)");
+    Prob& p = *out;
+    p.n = q.n; p.h = q.h; p.w = q.w; p.c = q.c; p.k = q.k; p.r = q.r; p.s = q.s;
+    p.stride = q.stride; p.pad_h = q.pad_h; p.pad_w = q.pad_w; p.groups = q.groups;
+    p.dtype = q.dtype;
+    p.ho = hn / q.stride + 1;
+    p.wo = wn / q.stride + 1;
+    p.cg = q.c / q.groups;
+    p.kg = q.k / q.groups;
+    // keep every element count comfortably inside int64 arithmetic
+    const double elems[3] = {double(p.n) * p.h * p.w * p.c, double(p.n) * p.ho * p.wo * p.k,
+                             double(p.k) * p.r * p.s * p.cg};
+    for (double e : elems)
+        if (e > 4.0e18) return fail(CNHWC_INVALID_ARG, "tensor element count overflows int64");
+    return CNHWC_OK;
+}
+
+bool is_depthwise(const Prob& p) { return p.groups == p.c && p.groups == p.k; }
+
+bool variant_is_dgrad(int v) {
+    return v == CNHWC_VAR_DGRAD_POINTWISE || v == CNHWC_VAR_DGRAD_IGEMM ||
+           v == CNHWC_VAR_DGRAD_DW_STREAM || v == CNHWC_VAR_DGRAD_DW_ROTATED ||
+           v == CNHWC_VAR_DGRAD_GENERIC;
+}
+bool variant_is_fwd(int v) {
+    return v == CNHWC_VAR_FWD_DIRECT || v == CNHWC_VAR_FWD_SPLITC ||
+           v == CNHWC_VAR_FWD_GROUPED || v == CNHWC_VAR_FWD_GENERIC;
+}
+
+const char* dt(const Prob& p) { return p.dtype == CNHWC_F16 ? "f16" : "bf16"; }
+
+// Reason a given variant cannot run the problem ("" if it can).
+std::string variant_reason(const Prob& p, int op, int v, int cpl, int split_c) {
+    if (op == CNHWC_OP_DGRAD && !variant_is_dgrad(v))
+        return "variant " + std::to_string(v) + " is not a dgrad kernel";
+    if (op == CNHWC_OP_FWD && !variant_is_fwd(v))
+        return "variant " + std::to_string(v) + " is not a forward kernel";
+    switch (v) {
+    case CNHWC_VAR_DGRAD_POINTWISE: return dgrad_igemm_reason(p, true);
+    case CNHWC_VAR_DGRAD_IGEMM: return dgrad_igemm_reason(p, false);
+    case CNHWC_VAR_DGRAD_DW_STREAM: return dw_stream_reason(p, cpl);
+    case CNHWC_VAR_DGRAD_DW_ROTATED: return dw_rotated_reason(p);
+    case CNHWC_VAR_FWD_DIRECT: return fwd_direct_reason(p, 1);
+    case CNHWC_VAR_FWD_SPLITC: return fwd_direct_reason(p, split_c);
+    case CNHWC_VAR_FWD_GROUPED: return fwd_grouped_reason(p);
+    case CNHWC_VAR_FWD_GENERIC:
+    case CNHWC_VAR_DGRAD_GENERIC: return "";
+    default: return "unknown variant " + std::to_string(v);
+    }
+}
+
+std::string plan_name(const Prob& p, const Plan& pl) {
+    char buf[160];
+    switch (pl.variant) {
+    case CNHWC_VAR_DGRAD_POINTWISE:
+        std::snprintf(buf, sizeof buf, "dgrad_pointwise_%s", dt(p)); break;
+    case CNHWC_VAR_DGRAD_IGEMM:
+        std::snprintf(buf, sizeof buf, "dgrad_igemm_%s_s%d", dt(p), p.stride); break;
+    case CNHWC_VAR_DGRAD_DW_STREAM:
+        std::snprintf(buf, sizeof buf, "dgrad_dw_stream_%s_f%lldx%lld_s%d_cpl%d", dt(p),
+                      (long long)p.r, (long long)p.s, p.stride, pl.cpl); break;
+    case CNHWC_VAR_DGRAD_DW_ROTATED:
+        std::snprintf(buf, sizeof buf, "dgrad_dw_rot_%s_f%lldx%lld_p%dx%d", dt(p),
+                      (long long)p.r, (long long)p.s, p.pad_h, p.pad_w); break;
+    case CNHWC_VAR_DGRAD_GENERIC:
+        std::snprintf(buf, sizeof buf, "dgrad_generic_%s", dt(p)); break;
+    case CNHWC_VAR_FWD_DIRECT:
+        std::snprintf(buf, sizeof buf, "fwd_direct_%s", dt(p)); break;
+    case CNHWC_VAR_FWD_SPLITC:
+        std::snprintf(buf, sizeof buf, "fwd_direct_splitc%d_%s+split_reduce", pl.split_c, dt(p)); break;
+    case CNHWC_VAR_FWD_GROUPED:
+        std::snprintf(buf, sizeof buf, "fwd_grouped_merge_%s", dt(p)); break;
+    case CNHWC_VAR_FWD_GENERIC:
+        std::snprintf(buf, sizeof buf, "fwd_generic_%s", dt(p)); break;
+    default: std::snprintf(buf, sizeof buf, "none");
+    }
+    return buf;
+}
+
+// Shape -> kernel.  The descriptor alone decides; the override exists for tests.
+int choose(const Prob& p, int op, Plan* out) {
+    Plan pl;
+    const cnhwc_override& ov = g_ov;
+    if (op != CNHWC_OP_FWD && op != CNHWC_OP_DGRAD)
+        return fail(CNHWC_INVALID_ARG, "op must be CNHWC_OP_FWD (1) or CNHWC_OP_DGRAD (2)");
+    if (ov.variant != CNHWC_VAR_AUTO) {
+        pl.variant = ov.variant;
+        pl.cpl = ov.cpl > 0 ? ov.cpl : (ov.variant == CNHWC_VAR_DGRAD_DW_STREAM ? dw_stream_best_cpl(p) : 0);
+        pl.split_c = ov.split_c > 0 ? ov.split_c
+                                    : (ov.variant == CNHWC_VAR_FWD_SPLITC ? fwd_direct_auto_split(p) : 1);
+        if (ov.variant == CNHWC_VAR_FWD_SPLITC && pl.split_c < 2)
+            return fail(CNHWC_UNSUPPORTED, "split-C needs at least 2 channel splits");
+        std::string why = variant_reason(p, op, pl.variant, pl.cpl, pl.split_c);
+        if (!why.empty()) return fail(CNHWC_UNSUPPORTED, why);
+        if (pl.variant != CNHWC_VAR_FWD_SPLITC) pl.split_c = 1;
+        pl.name = plan_name(p, pl);
+        *out = pl;
+        return CNHWC_OK;
+    }
+    std::string tried;
+    auto take = [&](int v, int cpl, int split) -> bool {
+        std::string why = variant_reason(p, op, v, cpl, split);
+        if (!why.empty()) {
+            tried += (tried.empty() ? "" : "; ") + plan_name(p, Plan{v, cpl, split, 0, ""}) + ": " + why;
+            return false;
+        }
+        pl.variant = v; pl.cpl = cpl; pl.split_c = split;
+        return true;
+    };
+    bool ok = false;
+    if (op == CNHWC_OP_DGRAD) {
+        if (is_depthwise(p)) {
+            const bool big = p.r > 11 || p.s > 11 || p.r != p.s || p.pad_h != p.pad_w;
+            if (p.stride == 1 && big) ok = take(CNHWC_VAR_DGRAD_DW_ROTATED, 0, 1);
+            if (!ok) {
+                int cpl = ov.cpl > 0 ? ov.cpl : dw_stream_best_cpl(p);
+                ok = take(CNHWC_VAR_DGRAD_DW_STREAM, cpl > 0 ? cpl : 1, 1);
+            }
+            if (!ok && p.stride == 1) ok = take(CNHWC_VAR_DGRAD_DW_ROTATED, 0, 1);
+        }
+        if (!ok && p.groups == 1 && p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0)
+            ok = take(CNHWC_VAR_DGRAD_POINTWISE, 0, 1);
+        if (!ok) ok = take(CNHWC_VAR_DGRAD_IGEMM, 0, 1);
+        if (!ok) ok = take(CNHWC_VAR_DGRAD_GENERIC, 0, 1);
+    } else {
+        if (p.groups > 1) ok = take(CNHWC_VAR_FWD_GROUPED, 0, 1);
+        if (!ok) {
+            int split = ov.split_c > 0 ? ov.split_c : fwd_direct_auto_split(p);
+            if (split > 1) ok = take(CNHWC_VAR_FWD_SPLITC, 0, split);
+            if (!ok) ok = take(CNHWC_VAR_FWD_DIRECT, 0, 1);
+        }
+        if (!ok) ok = take(CNHWC_VAR_FWD_GENERIC, 0, 1);
+    }
+    if (!ok) return fail(CNHWC_UNSUPPORTED, "no kernel accepts the problem: " + tried);
+    pl.name = plan_name(p, pl);
+    *out = pl;
+    return CNHWC_OK;
+}
+
+struct ChunkBytes {
+    int64_t per_image_max;  // largest per-image view
+    int64_t fixed;          // views that do not scale with the batch (weights)
+    int64_t ws_per_image;   // workspace bytes per image
+};
+
+ChunkBytes chunk_bytes(const Prob& p, int op, const Plan& pl) {
+    const int64_t esz = 2;
+    const int64_t act = p.h * p.w * p.c * esz;
+    const int64_t out = p.ho * p.wo * p.k * esz;
+    ChunkBytes b;
+    b.ws_per_image = 0;
+    if (op == CNHWC_OP_FWD && pl.variant == CNHWC_VAR_FWD_SPLITC)
+        b.ws_per_image = int64_t(pl.split_c) * p.ho * p.wo * p.k * 4;
+    b.per_image_max = std::max(std::max(act, out), b.ws_per_image);
+    b.fixed = p.k * p.r * p.s * p.cg * esz;
+    return b;
+}
+
+int64_t limit_bytes() { return g_ov.chunk_limit_bytes > 0 ? g_ov.chunk_limit_bytes : kBufferLimit; }
+
+// Balanced batch split: the fewest chunks that keep each per-chunk view within
+// the limit, sizes floor(N/chunks) or ceil(N/chunks), larger ones first.
+int plan_chunks(const Prob& p, int op, const Plan& pl, std::vector<int64_t>* counts) {
+    const ChunkBytes b = chunk_bytes(p, op, pl);
+    const int64_t lim = limit_bytes();
+    if (b.fixed > kBufferLimit)
+        return fail(CNHWC_UNSUPPORTED, "weight tensor exceeds the 32-bit buffer range (" +
+                                           std::to_string(b.fixed) + " bytes)");
+    if (b.per_image_max > lim)
+        return fail(CNHWC_UNSUPPORTED, "one image exceeds the 32-bit buffer range (" +
+                                           std::to_string(b.per_image_max) + " bytes per image)");
+    const int64_t max_per = lim / b.per_image_max;
+    const int64_t chunks = (p.n + max_per - 1) / max_per;
+    const int64_t base = p.n / chunks, extra = p.n % chunks;
+    counts->clear();
+    for (int64_t i = 0; i < chunks; ++i) counts->push_back(base + (i < extra ? 1 : 0));
+    return CNHWC_OK;
+}
+
+int check_ptr(const void* ptr, const char* what) {
+    if (!ptr) return fail(CNHWC_INVALID_ARG, std::string(what) + " is NULL");
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+        return fail(CNHWC_MISALIGNED, std::string(what) + " is not 16-byte aligned");
+    return CNHWC_OK;
+}
+
+bool overlap(const void* a, int64_t na, const void* b, int64_t nb) {
+    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+    return x < y + uintptr_t(nb) && y < x + uintptr_t(na);
+}
+
+int run(const cnhwc_problem* prob, int op, const void* in, const void* w, void* out, void* ws,
+        size_t ws_bytes, void* stream) {
+    Prob p;
+    int st = validate(prob, &p);
+    if (st) return st;
+    Plan pl;
+    if ((st = choose(p, op, &pl))) return st;
+    const char* in_name = op == CNHWC_OP_FWD ? "x" : "dy";
+    const char* out_name = op == CNHWC_OP_FWD ? "y" : "dx";
+    if ((st = check_ptr(in, in_name))) return st;
+    if ((st = check_ptr(w, "w"))) return st;
+    if ((st = check_ptr(out, out_name))) return st;
+    const int64_t act_bytes = p.n * p.h * p.w * p.c * 2;
+    const int64_t res_bytes = p.n * p.ho * p.wo * p.k * 2;
+    const int64_t in_bytes = op == CNHWC_OP_FWD ? act_bytes : res_bytes;
+    const int64_t out_bytes = op == CNHWC_OP_FWD ? res_bytes : act_bytes;
+    const int64_t w_bytes = p.k * p.r * p.s * p.cg * 2;
+    if (overlap(out, out_bytes, in, in_bytes) || overlap(out, out_bytes, w, w_bytes))
+        return fail(CNHWC_INVALID_ARG, std::string(out_name) + " overlaps an input");
+    std::vector<int64_t> counts;
+    if ((st = plan_chunks(p, op, pl, &counts))) return st;
+    const ChunkBytes cb = chunk_bytes(p, op, pl);
+    const int64_t max_chunk = *std::max_element(counts.begin(), counts.end());
+    const int64_t need_ws = cb.ws_per_image * max_chunk;
+    if (need_ws > 0) {
+        if ((st = check_ptr(ws, "ws"))) return st;
+        if (int64_t(ws_bytes) < need_ws)
+            return fail(CNHWC_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(need_ws) +
+                                                       " bytes, got " + std::to_string(ws_bytes));
+        if (overlap(ws, need_ws, in, in_bytes) || overlap(ws, need_ws, w, w_bytes) ||
+            overlap(ws, need_ws, out, out_bytes))
+            return fail(CNHWC_INVALID_ARG, "workspace overlaps a tensor");
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();  // a stale error from earlier work must not be blamed on this call
+    int64_t first = 0;
+    const int64_t in_img = in_bytes / p.n, out_img = out_bytes / p.n;
+    for (int64_t cnt : counts) {
+        Prob pc = p;
+        pc.n = cnt;
+        const char* ip = static_cast<const char*>(in) + first * in_img;
+        char* op_ = static_cast<char*>(out) + first * out_img;
+        int rc = CNHWC_OK;
+        switch (pl.variant) {
+        case CNHWC_VAR_DGRAD_POINTWISE:
+        case CNHWC_VAR_DGRAD_IGEMM: rc = launch_dgrad_igemm(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_DGRAD_DW_STREAM: rc = launch_dgrad_dw_stream(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_DGRAD_DW_ROTATED: rc = launch_dgrad_dw_rotated(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_DGRAD_GENERIC: rc = launch_dgrad_generic(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_FWD_DIRECT:
+        case CNHWC_VAR_FWD_SPLITC: rc = launch_fwd_direct(pc, pl, ip, w, op_, ws, s); break;
+        case CNHWC_VAR_FWD_GROUPED: rc = launch_fwd_grouped(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_FWD_GENERIC: rc = launch_fwd_generic(pc, pl, ip, w, op_, s); break;
+        default: rc = CNHWC_UNSUPPORTED;
+        }
+        if (rc) return fail(rc, "launcher for " + pl.name + " refused the chunk");
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(CNHWC_HIP_ERROR, std::string("launch of ") + pl.name + " failed: " +
+                                             hipGetErrorString(e));
+        first += cnt;
+    }
+    g_err.clear();
+    return CNHWC_OK;
+}
+
+}  // namespace
+}  // namespace cnhwc
+
+using namespace cnhwc;
+
+extern "C" {
+
+int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo) {
+    Prob p;
+    int st = validate(prob, &p);
+    if (st) return st;
+    if (ho) *ho = p.ho;
+    if (wo) *wo = p.wo;
+    g_err.clear();
+    return CNHWC_OK;
+}
+
+int cnhwc_workspace_size(const cnhwc_problem* prob, int op, size_t* bytes) {
+    Prob p;
+    int st = validate(prob, &p);
+    if (st) return st;
+    Plan pl;
+    if ((st = choose(p, op, &pl))) return st;
+    std::vector<int64_t> counts;
+    if ((st = plan_chunks(p, op, pl, &counts))) return st;
+    const int64_t mx = *std::max_element(counts.begin(), counts.end());
+    if (bytes) *bytes = size_t(chunk_bytes(p, op, pl).ws_per_image * mx);
+    g_err.clear();
+    return CNHWC_OK;
+}
+
+int cnhwc_plan(const cnhwc_problem* prob, int op, char* name, size_t cap, int32_t* variant) {
+    Prob p;
+    int st = validate(prob, &p);
+    if (st) return st;
+    Plan pl;
+    if ((st = choose(p, op, &pl))) return st;
+    if (name && cap > 0) {
+        std::strncpy(name, pl.name.c_str(), cap - 1);
+        name[cap - 1] = '\0';
+    }
+    if (variant) *variant = pl.variant;
+    g_err.clear();
+    return CNHWC_OK;
+}
+
+int cnhwc_chunk_plan(const cnhwc_problem* prob, int op, int64_t* counts, int64_t cap,
+                     int64_t* nchunks) {
+    Prob p;
+    int st = validate(prob, &p);
+    if (st) return st;
+    Plan pl;
+    if ((st = choose(p, op, &pl))) return st;
+    std::vector<int64_t> c;
+    if ((st = plan_chunks(p, op, pl, &c))) return st;
+    if (nchunks) *nchunks = int64_t(c.size());
+    for (int64_t i = 0; counts && i < cap && i < int64_t(c.size()); ++i) counts[i] = c[i];
+    g_err.clear();
+    return CNHWC_OK;
+}
+
+int cnhwc_fwd(const cnhwc_problem* prob, const void* x, const void* w, void* y, void* ws,
+              size_t ws_bytes, void* hip_stream) {
+    return run(prob, CNHWC_OP_FWD, x, w, y, ws, ws_bytes, hip_stream);
+}
+
+int cnhwc_dgrad(const cnhwc_problem* prob, const void* dy, const void* w, void* dx, void* ws,
+                size_t ws_bytes, void* hip_stream) {
+    return run(prob, CNHWC_OP_DGRAD, dy, w, dx, ws, ws_bytes, hip_stream);
+}
+
+const char* cnhwc_last_error(void) { return g_err.c_str(); }
+
+int cnhwc_set_override(const cnhwc_override* ov) {
+    if (!ov) {
+        g_ov = cnhwc_override{0, 0, 0, 0, 0};
+        return CNHWC_OK;
+    }
+    if (ov->cpl != 0 && ov->cpl != 1 && ov->cpl != 2 && ov->cpl != 4 && ov->cpl != 8)
+        return fail(CNHWC_INVALID_ARG, "cpl must be 1, 2, 4 or 8 (got " + std::to_string(ov->cpl) + ")");
+    if (ov->split_c < 0) return fail(CNHWC_INVALID_ARG, "split_c must be >= 0");
+    if (ov->chunk_limit_bytes < 0) return fail(CNHWC_INVALID_ARG, "chunk_limit_bytes must be >= 0");
+    g_ov = *ov;
+    g_err.clear();
+    return CNHWC_OK;
+}
+
+}  // extern "C"

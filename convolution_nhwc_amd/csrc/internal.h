@@ -1,0 +1,71 @@
+// Host-side internals shared by the C ABI (host.cpp) and the kernel launchers.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+
+#include "../../include/cnhwc.h"
+
+namespace cnhwc {
+
+// A validated problem with its derived extents.
+struct Prob {
+    int64_t n, h, w, c, k, r, s;
+    int64_t ho, wo;   // output rows / columns (floor formula)
+    int64_t cg, kg;   // channels per group of x and of y
+    int32_t stride, pad_h, pad_w, groups;
+    int32_t dtype;    // CNHWC_F16 / CNHWC_BF16
+};
+
+// The dispatcher's decision for one pass.
+struct Plan {
+    int32_t variant = CNHWC_VAR_AUTO;
+    int32_t cpl = 0;      // depthwise channels per lane
+    int32_t split_c = 1;  // channel splits of the split-C forward
+    int32_t tile = 0;     // variant-specific tile selector
+    std::string name;
+};
+
+// Number of compute units the kernels size their grids for (MI355X: 256).
+constexpr int kNumCUs = 256;
+
+// Per-view byte limit of the kernels' 32-bit buffer addressing.
+constexpr int64_t kBufferLimit = (int64_t(1) << 31) - 1;
+
+// ---- launchers (one batch chunk each; p.n is the chunk's batch) -------------
+// Each returns 0 on success or a CNHWC_* status; launch errors are reported by
+// the caller through hipGetLastError.
+int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
+                       hipStream_t st);
+int launch_dgrad_dw_stream(const Prob& p, const Plan& pl, const void* dy, const void* w,
+                           void* dx, hipStream_t st);
+int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const void* w,
+                            void* dx, hipStream_t st);
+int launch_dgrad_generic(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
+                         hipStream_t st);
+int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
+                      void* ws, hipStream_t st);
+int launch_fwd_grouped(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
+                       hipStream_t st);
+int launch_fwd_generic(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
+                       hipStream_t st);
+
+// ---- per-variant acceptance (empty string = accepted, else the reason) ------
+std::string dgrad_igemm_reason(const Prob& p, bool pointwise);
+std::string dw_stream_reason(const Prob& p, int cpl);
+std::string dw_rotated_reason(const Prob& p);
+std::string fwd_direct_reason(const Prob& p, int split_c);
+std::string fwd_grouped_reason(const Prob& p);
+
+// Depthwise row-streaming: the largest channels-per-lane the kernel set has an
+// instance for at this filter/stride (0 if none).
+int dw_stream_best_cpl(const Prob& p);
+// Split-C forward: tile grid size and the automatic split count.
+int64_t fwd_direct_tiles(const Prob& p);
+int fwd_direct_auto_split(const Prob& p);
+int fwd_direct_channel_chunk();
+
+}  // namespace cnhwc

@@ -1,0 +1,152 @@
+/*
+ * cnhwc.h -- C ABI of the gfx950 (MI355X) NHWC convolution library libcnhwc.so.
+ *
+ * Two passes of 2D convolution over fp16 or bf16 tensors with fp32
+ * accumulation and one round-to-nearest-even rounding of each output element:
+ *
+ *   forward   y[n,ho,wo,k] = sum_{r,t,j} x[n, ho*s-pad_h+r, wo*s-pad_w+t, g*Cg+j] * w[k,r,t,j]
+ *   dgrad     dx = the adjoint of that map applied to dy
+ *
+ * (cross-correlation, no filter flip; g = k / Kg, Cg = C/groups, Kg = K/groups;
+ * x is zero outside the image).  The operations are those of three rocKE pull
+ * requests: "perf(rocke/conv): add the pointwise fast path dgrad was missing"
+ * (1x1 and general implicit-GEMM dgrad), "feat(rocke): split-C and grouped
+ * LDS-halo direct conv fwd kernels" (direct forward, split-C with a reduce
+ * pass, small groups merged block-diagonally, batch chunking past the 32-bit
+ * buffer range) and "feat(rocke): channel-packed and large-filter depthwise
+ * dgrad" (row-streaming and rotated-filter depthwise dgrad, per-axis padding).
+ *
+ * Layouts (all dense, row-major, 16-byte-aligned base pointers):
+ *   x, dx  [N][H][W][C]          y, dy  [N][Ho][Wo][K]          w  [K][R][S][C/groups]
+ *   Ho = floor((H + 2*pad_h - R) / stride) + 1,  Wo = floor((W + 2*pad_w - S) / stride) + 1.
+ *
+ * Conventions shared by every entry point:
+ *   - Pointers passed to cnhwc_fwd / cnhwc_dgrad are DEVICE pointers on the
+ *     current HIP device.  The caller allocates and owns every buffer,
+ *     including the workspace; the library never allocates, frees or
+ *     synchronises.  Inputs are read only; outputs are fully overwritten
+ *     (positions no filter tap reaches are written as 0).
+ *   - Work is enqueued asynchronously on `hip_stream` (a hipStream_t; NULL is
+ *     the null stream).  A return of CNHWC_OK means the launches were
+ *     enqueued, not that they finished.
+ *   - A non-zero status leaves the outputs untouched, and cnhwc_last_error()
+ *     returns a reason for it (thread-local, valid until the next call on the
+ *     same thread).  The descriptor is checked in a fixed order and the first
+ *     failing check is reported.
+ *   - Inputs and outputs must not overlap.  Calls on one stream are ordered;
+ *     calls on different streams that share an output race.
+ */
+#ifndef CNHWC_H
+#define CNHWC_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* ---- status codes ------------------------------------------------------- */
+#define CNHWC_OK 0
+#define CNHWC_INVALID_ARG 1          /* descriptor or pointer argument invalid */
+#define CNHWC_UNSUPPORTED 2          /* valid problem no kernel accepts (reason says why) */
+#define CNHWC_WORKSPACE_TOO_SMALL 3  /* ws_bytes below cnhwc_workspace_size() */
+#define CNHWC_MISALIGNED 4           /* a device pointer is not 16-byte aligned */
+#define CNHWC_HIP_ERROR 5            /* the HIP runtime rejected a launch */
+
+/* ---- element types and passes ------------------------------------------- */
+#define CNHWC_F16 0
+#define CNHWC_BF16 1
+
+/* Pass numbers follow MIOpen's -F direction codes the first page's driver
+ * parses: 1 = forward, 2 = backward data. */
+#define CNHWC_OP_FWD 1
+#define CNHWC_OP_DGRAD 2
+
+/* Problem descriptor: the fields rocKE's DirectConvProblem carries (N, H, W,
+ * C, K, filter rows R = KH, filter columns S = KW, stride, padding, groups),
+ * with the column padding explicit rather than the "-1 means PAD" sentinel
+ * ("feat(rocke): channel-packed and large-filter depthwise dgrad", Per-axis
+ * padding).  One stride serves both axes; dilation is 1.
+ * Valid: n,h,w,c,k,r,s >= 1; stride >= 1; pad_h, pad_w >= 0; groups >= 1 with
+ * c % groups == 0 and k % groups == 0; Ho, Wo >= 1; dtype F16 or BF16;
+ * reserved == 0. */
+typedef struct cnhwc_problem {
+    int64_t n, h, w, c, k, r, s;
+    int32_t stride, pad_h, pad_w, groups;
+    int32_t dtype;
+    int32_t reserved;
+} cnhwc_problem;
+
+/* Kernel variants the dispatcher chooses among (cnhwc_plan names them). */
+#define CNHWC_VAR_AUTO 0
+#define CNHWC_VAR_DGRAD_POINTWISE 1  /* 1x1, stride 1, unpadded, ungrouped: dX = dY * W on MFMA */
+#define CNHWC_VAR_DGRAD_IGEMM 2      /* general R x S strided implicit-GEMM dgrad on MFMA */
+#define CNHWC_VAR_DGRAD_DW_STREAM 3  /* depthwise dgrad, row-streaming, cpl channels per lane */
+#define CNHWC_VAR_DGRAD_DW_ROTATED 4 /* depthwise dgrad, stride 1, rotated-filter tiled */
+#define CNHWC_VAR_FWD_DIRECT 5       /* direct LDS-halo forward on MFMA, one pass */
+#define CNHWC_VAR_FWD_SPLITC 6       /* direct forward, channel loop split; fp32 workspace + reduce pass */
+#define CNHWC_VAR_FWD_GROUPED 7      /* grouped forward, small groups merged block-diagonally */
+#define CNHWC_VAR_FWD_GENERIC 8      /* plain one-output-per-lane forward (any valid problem) */
+#define CNHWC_VAR_DGRAD_GENERIC 9    /* plain one-output-per-lane dgrad (any valid problem) */
+
+/* Output dims by the floor formula above.  INVALID_ARG for a bad descriptor. */
+int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo);
+
+/* Workspace bytes the chosen kernel of pass `op` needs (0 for all but the
+ * split-C forward, which needs split_c * N * Ho * Wo * K * 4 bytes of fp32
+ * partial sums).  Pass at least this many bytes to cnhwc_fwd/cnhwc_dgrad. */
+int cnhwc_workspace_size(const cnhwc_problem* prob, int op, size_t* bytes);
+
+/* The dispatcher's choice for pass `op`: writes the kernel name (variant,
+ * element type, tile or channels-per-lane) into name[0..cap) (truncated,
+ * always NUL-terminated when cap > 0) and, if `variant` is not NULL, the
+ * CNHWC_VAR_* number.  UNSUPPORTED with a reason when no kernel accepts. */
+int cnhwc_plan(const cnhwc_problem* prob, int op, char* name, size_t cap, int32_t* variant);
+
+/* Batch split of the launches for pass `op`: every per-image view of x/dx,
+ * y/dy and the workspace must stay within the kernels' 32-bit buffer range
+ * (2^31 - 1 bytes, or the test override's limit), so the batch runs as
+ * balanced chunks of floor(N/chunks) or ceil(N/chunks) images ("feat(rocke):
+ * split-C and grouped LDS-halo direct conv fwd kernels", supporting changes).
+ * Writes up to `cap` chunk sizes (in images, in launch order) into counts and
+ * their number into *nchunks.  UNSUPPORTED when one image alone is over the
+ * limit. */
+int cnhwc_chunk_plan(const cnhwc_problem* prob, int op, int64_t* counts, int64_t cap,
+                     int64_t* nchunks);
+
+/* Forward pass.  x: device [N,H,W,C]; w: device [K,R,S,C/groups];
+ * y: device [N,Ho,Wo,K] (written); ws: device scratch of ws_bytes (may be NULL
+ * when cnhwc_workspace_size() reports 0; its contents on return are
+ * unspecified). */
+int cnhwc_fwd(const cnhwc_problem* prob, const void* x, const void* w, void* y,
+              void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Backward-data pass.  dy: device [N,Ho,Wo,K]; w: device [K,R,S,C/groups];
+ * dx: device [N,H,W,C] (written, every element).  ws as for cnhwc_fwd. */
+int cnhwc_dgrad(const cnhwc_problem* prob, const void* dy, const void* w, void* dx,
+                void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Reason for the last non-zero status on this thread ("" after success). */
+const char* cnhwc_last_error(void);
+
+/* Test-only override of the dispatcher's choices, thread-local.  A zero field
+ * keeps the automatic choice.  variant: a CNHWC_VAR_* to force (the call fails
+ * with UNSUPPORTED and the variant's reason if it cannot run the problem);
+ * cpl: depthwise channels per lane (1, 2, 4 or 8); split_c: number of channel
+ * splits for CNHWC_VAR_FWD_SPLITC; chunk_limit_bytes: the per-view byte limit
+ * of the chunk planner.  Pass NULL to clear. */
+typedef struct cnhwc_override {
+    int32_t variant;
+    int32_t cpl;
+    int32_t split_c;
+    int32_t reserved;
+    int64_t chunk_limit_bytes;
+} cnhwc_override;
+
+int cnhwc_set_override(const cnhwc_override* ov);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* CNHWC_H */

@@ -1,0 +1,99 @@
+"""Helpers for the GPU parity tests: seeded operands, device upload, NaN-poisoned
+outputs, the call through the C ABI binding and the comparison with the oracle.
+
+Tolerance: every element must satisfy |gpu - ref| <= 1e-2 * (1 + |ref|), where
+ref is the fp64 oracle on the exact values of the same 16-bit inputs.
+"""
+import numpy as np
+
+import oracle
+from convolution_nhwc_amd import api, synth
+
+TOL = 1e-2
+NAN_BITS = {"f16": 0x7E00, "bf16": 0x7FC0}
+
+
+def torch():
+    import torch as t
+    return t
+
+
+def to_device(bits):
+    t = torch()
+    return t.from_numpy(np.ascontiguousarray(bits).view(np.int16)).to("cuda")
+
+
+def poisoned(shape, dtype):
+    t = torch()
+    return t.full(shape, NAN_BITS[dtype] - (1 << 16) if NAN_BITS[dtype] >= 1 << 15 else NAN_BITS[dtype],
+                  dtype=t.int16, device="cuda")
+
+
+def from_device(x, dtype):
+    bits = x.cpu().numpy().view(np.uint16)
+    return synth.bits_to_f64(bits, dtype)
+
+
+def operands(p, op, seed, exact=False):
+    """(act_bits, act_f64, w_bits, w_f64) for problem p and pass op."""
+    ho, wo = oracle.out_dims(p)
+    act_shape = (p["n"], p["h"], p["w"], p["c"]) if op == "fwd" else (p["n"], ho, wo, p["k"])
+    w_shape = (p["k"], p["r"], p["s"], p["c"] // p["groups"])
+    if exact:
+        rng = synth.generator(seed)
+        a = synth.draw(rng, act_shape, ("ints", (-1.0, 0.0, 1.0)))
+        w = synth.draw(rng, w_shape, ("ints", (-1.0, 0.0, 1.0)))
+        (ab, af), (wb, wf) = synth.round_to(a, p["dtype"]), synth.round_to(w, p["dtype"])
+    else:
+        fan = p["c"] // p["groups"] * p["r"] * p["s"] if op == "fwd" else p["k"] // p["groups"] * p["r"] * p["s"]
+        (ab, af), (wb, wf) = synth.operands(seed, act_shape, w_shape, p["dtype"], w_fan_in=fan)
+    return ab, af, wb, wf
+
+
+def run_gpu(p, op, act_bits, w_bits):
+    """Run pass op through the C ABI on poisoned outputs; returns the output as f64."""
+    t = torch()
+    ho, wo = api.cnhwc_out_dims(p)
+    a = to_device(act_bits)
+    w = to_device(w_bits)
+    if op == "fwd":
+        out = poisoned((p["n"], ho, wo, p["k"]), p["dtype"])
+        need = api.cnhwc_workspace_size(p, api.OP_FWD)
+        ws = t.full((max(need, 16) // 4,), float("nan"), dtype=t.float32, device="cuda")
+        api.cnhwc_fwd(p, a.data_ptr(), w.data_ptr(), out.data_ptr(), ws.data_ptr(), need,
+                      t.cuda.current_stream().cuda_stream)
+    else:
+        out = poisoned((p["n"], p["h"], p["w"], p["c"]), p["dtype"])
+        api.cnhwc_dgrad(p, a.data_ptr(), w.data_ptr(), out.data_ptr(), None, 0,
+                        t.cuda.current_stream().cuda_stream)
+    t.cuda.synchronize()
+    return out
+
+
+def reference(p, op, act_f64, w_f64):
+    return oracle.conv_fwd(act_f64, w_f64, p) if op == "fwd" else oracle.conv_dgrad(act_f64, w_f64, p)
+
+
+def check_close(got, ref, what=""):
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.all(np.isfinite(got)), "%s: %d non-finite outputs (unwritten?)" % (what, int(np.sum(~np.isfinite(got))))
+    err = np.abs(got - ref)
+    bound = TOL * (1.0 + np.abs(ref))
+    bad = err > bound
+    assert not bad.any(), "%s: %d of %d outside tolerance, max err %.3g at %s (got %r want %r)" % (
+        what, int(bad.sum()), bad.size, float(err.max()), np.unravel_index(np.argmax(err - bound), err.shape),
+        float(got.flat[np.argmax(err - bound)]), float(ref.flat[np.argmax(err - bound)]))
+    return float(err.max())
+
+
+def parity(p, op, seed, exact=False):
+    """Full-tensor parity of one problem; returns (max_err, gpu_bits_tensor)."""
+    ab, af, wb, wf = operands(p, op, seed, exact)
+    out = run_gpu(p, op, ab, wb)
+    got = from_device(out, p["dtype"])
+    ref = reference(p, op, af, wf)
+    if exact:
+        assert np.all(np.isfinite(got))
+        assert np.array_equal(got, ref), "exact mode: %d mismatches" % int(np.sum(got != ref))
+        return 0.0, out
+    return check_close(got, ref, str(p)), out

@@ -1,0 +1,131 @@
+"""GPU parity of the MFMA dgrad kernels (1x1 pointwise fast path and general
+R x S strided implicit GEMM) against the fp64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+
+import oracle
+from convolution_nhwc_amd import api, synth
+
+from gpu_util import check_close, from_device, operands, parity, run_gpu
+
+pytestmark = pytest.mark.gpu
+
+
+def P(n, h, w, c, k, r, s, stride=1, pad_h=0, pad_w=0, groups=1, dtype="f16"):
+    return dict(n=n, h=h, w=w, c=c, k=k, r=r, s=s, stride=stride, pad_h=pad_h, pad_w=pad_w,
+                groups=groups, dtype=dtype)
+
+
+def ident(p):
+    return "n{n}h{h}w{w}c{c}k{k}r{r}s{s}st{stride}p{pad_h}x{pad_w}g{groups}{dtype}".format(**p)
+
+
+POINTWISE = [
+    synth.WORKLOADS["c1_pointwise_tiny"]["prob"],
+    P(2, 9, 7, 64, 256, 1, 1),            # M = 126: one ragged M tile
+    P(3, 17, 13, 136, 72, 1, 1),          # C and K not multiples of the tiles
+    P(1, 8, 8, 16, 16, 1, 1, dtype="bf16"),
+    P(2, 20, 20, 192, 40, 1, 1, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("p", POINTWISE, ids=ident)
+def test_pointwise_parity(p):
+    assert api.cnhwc_plan(p, api.OP_DGRAD)[1] == api.VAR_DGRAD_POINTWISE
+    parity(p, "dgrad", 101)
+
+
+IGEMM = [
+    P(2, 12, 12, 64, 64, 3, 3, 1, 1, 1),
+    P(2, 14, 14, 64, 128, 3, 3, 2, 1, 1),
+    P(1, 15, 13, 128, 64, 3, 3, 2, 1, 1),          # odd extents, ragged classes
+    P(2, 11, 10, 32, 48, 5, 3, 2, 2, 1),           # non-square filter, per-axis pad
+    P(1, 16, 16, 64, 64, 3, 3, 3, 1, 1),           # stride 3: 9 classes
+    P(1, 17, 19, 40, 24, 4, 2, 2, 0, 1),           # even filter
+    P(1, 9, 9, 16, 16, 1, 1, 2, 0, 0),             # stride > filter: classes with no taps
+    P(1, 13, 13, 16, 32, 3, 3, 4, 1, 1),           # stride 4: zero classes
+    P(2, 10, 10, 64, 64, 3, 3, 1, 1, 1, groups=2),
+    P(1, 12, 12, 48, 96, 3, 3, 2, 1, 1, groups=3),
+    P(2, 12, 12, 200, 136, 3, 3, 1, 1, 1),         # C not a tile multiple, K % 64 != 0
+    P(1, 10, 12, 64, 64, 7, 7, 1, 3, 3),
+    P(2, 14, 14, 64, 64, 3, 3, 1, 1, 1, dtype="bf16"),
+    P(1, 16, 16, 64, 64, 3, 3, 2, 1, 1, dtype="bf16"),
+    P(1, 8, 8, 16, 16, 1, 1, 1, 1, 1),             # 1x1 padded: general path
+]
+
+
+@pytest.mark.parametrize("p", IGEMM, ids=ident)
+def test_igemm_parity(p):
+    assert api.cnhwc_plan(p, api.OP_DGRAD)[1] == api.VAR_DGRAD_IGEMM
+    parity(p, "dgrad", 102)
+
+
+@pytest.mark.parametrize("p", [P(1, 12, 12, 64, 64, 3, 3, 2, 1, 1), P(2, 8, 8, 32, 32, 1, 1),
+                               P(1, 10, 10, 32, 64, 3, 3, 1, 1, 1, dtype="bf16")], ids=ident)
+def test_exact_small_integers_bitwise(p):
+    """Inputs in {-1, 0, 1}: every partial sum is exact in fp32, so the rounded
+    result must equal the oracle bit for bit whatever the summation order."""
+    parity(p, "dgrad", 103, exact=True)
+
+
+@pytest.mark.parametrize("p", [synth.WORKLOADS["c2_pointwise"]["prob"] | dict(n=2),
+                               P(2, 30, 30, 64, 256, 1, 1), P(1, 8, 8, 16, 16, 1, 1, dtype="bf16")],
+                         ids=ident)
+def test_pointwise_bit_identical_to_general(p):
+    ab, _, wb, _ = operands(p, "dgrad", 104)
+    fast = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    with api.override(variant=api.VAR_DGRAD_IGEMM):
+        gen = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    assert np.array_equal(fast.view(np.uint16), gen.view(np.uint16))
+
+
+def test_reproducible_bitwise():
+    p = P(2, 14, 14, 64, 128, 3, 3, 2, 1, 1)
+    ab, _, wb, _ = operands(p, "dgrad", 105)
+    a = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    b = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
+def test_chunked_equals_unchunked():
+    p = P(5, 12, 12, 64, 64, 3, 3, 2, 1, 1)
+    ab, _, wb, _ = operands(p, "dgrad", 106)
+    whole = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    img = 12 * 12 * 64 * 2
+    with api.override(chunk_limit_bytes=2 * img):
+        assert api.cnhwc_chunk_plan(p, api.OP_DGRAD) == [2, 2, 1]
+        parts = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    assert np.array_equal(whole, parts)
+
+
+def test_planted_stride_mistake_is_caught():
+    """A dY stride mistake planted in the oracle (K+1 instead of K between
+    pixels) must break parity; shows the comparison is sensitive to it."""
+    p = P(1, 6, 6, 16, 16, 1, 1)
+    ab, af, wb, wf = operands(p, "dgrad", 107)
+    got = from_device(run_gpu(p, "dgrad", ab, wb), "f16")
+    flat = af.reshape(-1)
+    wrong = np.stack([flat[i * 17:i * 17 + 16] if i * 17 + 16 <= flat.size else np.zeros(16)
+                      for i in range(36)]).reshape(af.shape)
+    with pytest.raises(AssertionError):
+        check_close(got, oracle.conv_dgrad(wrong, wf, p))
+
+
+FULL = ["c2_pointwise", "c3a_3x3_s1", "c3b_3x3_s2"]
+
+
+@pytest.mark.parametrize("name", FULL)
+def test_full_size_sampled_images(name):
+    """The workload at its full size in the benchmark's launch configuration;
+    images 0, N/2 and N-1 are checked against the oracle run on that image."""
+    wl = synth.WORKLOADS[name]
+    p = wl["prob"]
+    ho, wo = oracle.out_dims(p)
+    (ab, af), (wb, wf) = synth.operands(wl["seed"], (p["n"], ho, wo, p["k"]),
+                                        (p["k"], p["r"], p["s"], p["c"] // p["groups"]),
+                                        p["dtype"], w_fan_in=wl["fan_in"])
+    got = from_device(run_gpu(p, "dgrad", ab, wb), p["dtype"])
+    one = dict(p, n=1)
+    for img in sorted({0, p["n"] // 2, p["n"] - 1}):
+        ref = oracle.conv_dgrad(af[img:img + 1], wf, one)
+        check_close(got[img:img + 1], ref, "%s image %d" % (name, img))

@@ -1,0 +1,233 @@
+"""CPU tests of the C ABI's host logic: exports, validation order and reasons,
+output extents, the dispatcher's choices, the batch-chunk planner, workspace
+sizing and the pointer checks.  Nothing here launches a kernel."""
+import os
+import re
+
+import pytest
+
+import oracle
+from convolution_nhwc_amd import api, synth
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def P(n, h, w, c, k, r, s, stride=1, pad_h=0, pad_w=0, groups=1, dtype="f16"):
+    return dict(n=n, h=h, w=w, c=c, k=k, r=r, s=s, stride=stride, pad_h=pad_h, pad_w=pad_w,
+                groups=groups, dtype=dtype)
+
+
+def declared_symbols():
+    syms = set()
+    for name in os.listdir(os.path.join(ROOT, "include")):
+        if name.endswith(".h"):
+            text = open(os.path.join(ROOT, "include", name)).read()
+            syms |= set(re.findall(r"^\s*(?:int|const char\*|void)\s+\**(cnhwc_\w+)\s*\(", text, re.M))
+    return syms
+
+
+def test_library_exports_every_declared_symbol():
+    syms = declared_symbols()
+    assert {"cnhwc_fwd", "cnhwc_dgrad", "cnhwc_plan"} <= syms
+    L = api.lib()
+    for s in syms:
+        assert hasattr(L, s), s
+    assert set(api.SYMBOLS) >= syms
+
+
+@pytest.mark.parametrize("p", [P(2, 9, 11, 8, 8, 3, 3, 1, 1, 1), P(1, 56, 56, 64, 64, 3, 3, 2, 1, 1),
+                               P(3, 17, 13, 8, 16, 5, 3, 3, 2, 0), P(1, 32, 32, 8, 8, 51, 5, 1, 25, 2, 8),
+                               P(1, 7, 7, 16, 16, 7, 7, 4, 0, 3), P(1, 24, 24, 8, 8, 3, 3, 1, 1, 0)])
+def test_out_dims_match_oracle(p):
+    assert api.cnhwc_out_dims(p) == oracle.out_dims(p)
+
+
+REFUSALS = [
+    (dict(groups=0), "groups must be >= 1"),
+    (dict(groups=-4), "groups must be >= 1"),
+    (dict(groups=3), "multiples of groups"),
+    (dict(stride=0), "stride must be >= 1"),
+    (dict(pad_h=-1), "padding must be >= 0"),
+    (dict(pad_w=-2), "padding must be >= 0"),
+    (dict(n=0), "n must be >= 1"),
+    (dict(r=9, s=9), "filter larger than the padded input"),
+    (dict(dtype=7), "dtype"),
+]
+
+
+@pytest.mark.parametrize("change,reason", REFUSALS, ids=[r for _, r in REFUSALS])
+def test_validation_refuses_with_reason(change, reason):
+    p = dict(P(1, 6, 6, 8, 8, 3, 3, 1, 1, 1), **change)
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_out_dims(p)
+    assert e.value.status == api.INVALID_ARG
+    assert reason in e.value.reason
+
+
+def test_validation_order_reports_first_failure():
+    p = dict(P(1, 6, 6, 8, 8, 3, 3), stride=0, groups=0)
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_out_dims(p)
+    assert "stride" in e.value.reason
+
+
+def test_reserved_field_must_be_zero():
+    pr = api._problem(P(1, 6, 6, 8, 8, 3, 3))
+    pr.reserved = 1
+    with pytest.raises(api.CnhwcError):
+        api.cnhwc_out_dims(pr)
+
+
+def wl(name):
+    return synth.WORKLOADS[name]
+
+
+EXPECT = {
+    "c1_pointwise_tiny": api.VAR_DGRAD_POINTWISE,
+    "c2_pointwise": api.VAR_DGRAD_POINTWISE,
+    "c3a_3x3_s1": api.VAR_DGRAD_IGEMM,
+    "c3b_3x3_s2": api.VAR_DGRAD_IGEMM,
+    "c4a_splitc_fwd": api.VAR_FWD_SPLITC,
+    "c4b_grouped_fwd": api.VAR_FWD_GROUPED,
+    "c5_dw3x3": api.VAR_DGRAD_DW_STREAM,
+    "c5_dw7x7": api.VAR_DGRAD_DW_STREAM,
+    "c5_dw31x31": api.VAR_DGRAD_DW_ROTATED,
+    "c5_dw51x5": api.VAR_DGRAD_DW_ROTATED,
+    "c5_dw5x51": api.VAR_DGRAD_DW_ROTATED,
+}
+
+
+@pytest.mark.parametrize("name", sorted(EXPECT))
+def test_dispatcher_choice_per_workload(name):
+    w = wl(name)
+    op = api.OP_FWD if w["op"] == "fwd" else api.OP_DGRAD
+    kname, var = api.cnhwc_plan(w["prob"], op)
+    assert var == EXPECT[name], (name, kname)
+
+
+def test_dispatcher_falls_back_to_generic():
+    # channel counts that are not multiples of 8 go to the plain kernels
+    assert api.cnhwc_plan(P(1, 8, 8, 3, 5, 3, 3, 1, 1, 1), api.OP_DGRAD)[1] == api.VAR_DGRAD_GENERIC
+    assert api.cnhwc_plan(P(1, 8, 8, 3, 5, 3, 3, 1, 1, 1), api.OP_FWD)[1] == api.VAR_FWD_GENERIC
+    # strides above 4 exceed the implicit-GEMM class table
+    assert api.cnhwc_plan(P(1, 16, 16, 8, 8, 5, 5, 5, 2, 2), api.OP_DGRAD)[1] == api.VAR_DGRAD_GENERIC
+
+
+def test_pointwise_only_for_its_shape_class():
+    for p in [P(1, 8, 8, 16, 16, 1, 1, 2), P(1, 8, 8, 16, 16, 1, 1, 1, 1, 1),
+              P(1, 8, 8, 16, 16, 1, 1, groups=2), P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1)]:
+        assert api.cnhwc_plan(p, api.OP_DGRAD)[1] != api.VAR_DGRAD_POINTWISE
+
+
+def test_forced_variant_refusals_carry_reasons():
+    p = P(1, 16, 16, 16, 16, 3, 3, 2, 1, 1, groups=16)
+    with api.override(variant=api.VAR_DGRAD_DW_ROTATED):
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_plan(p, api.OP_DGRAD)
+    assert e.value.status == api.UNSUPPORTED and "stride" in e.value.reason
+    big = P(1, 70, 70, 16, 16, 65, 3, 1, 32, 1, groups=16)
+    with api.override(variant=api.VAR_DGRAD_DW_ROTATED):
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_plan(big, api.OP_DGRAD)
+    assert "64" in e.value.reason
+    with api.override(variant=api.VAR_DGRAD_POINTWISE):
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_plan(P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1), api.OP_DGRAD)
+    assert "1x1" in e.value.reason
+    with api.override(variant=api.VAR_FWD_DIRECT):
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_plan(P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1), api.OP_DGRAD)
+    assert "not a dgrad kernel" in e.value.reason
+
+
+def test_override_rejects_bad_cpl():
+    with pytest.raises(api.CnhwcError):
+        api.cnhwc_set_override(cpl=3)
+    api.cnhwc_clear_override()
+
+
+def test_depthwise_stream_cpl_must_divide_channels():
+    p = P(1, 16, 16, 12, 12, 3, 3, 1, 1, 1, groups=12)
+    with api.override(variant=api.VAR_DGRAD_DW_STREAM, cpl=8):
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_plan(p, api.OP_DGRAD)
+    assert "cpl" in e.value.reason
+
+
+@pytest.mark.parametrize("n,limit_images", [(7, 3), (10, 4), (5, 1), (9, 9), (1, 1)])
+def test_chunk_planner_is_balanced(n, limit_images):
+    p = P(n, 8, 8, 16, 16, 3, 3, 1, 1, 1)
+    per_image = 8 * 8 * 16 * 2
+    with api.override(chunk_limit_bytes=per_image * limit_images):
+        counts = api.cnhwc_chunk_plan(p, api.OP_DGRAD)
+    chunks = -(-n // limit_images)
+    assert len(counts) == chunks and sum(counts) == n
+    assert max(counts) - min(counts) <= 1 and max(counts) <= limit_images
+    assert counts == sorted(counts, reverse=True)
+
+
+def test_chunk_planner_default_is_one_chunk_for_every_workload():
+    for name, w in synth.WORKLOADS.items():
+        op = api.OP_FWD if w["op"] == "fwd" else api.OP_DGRAD
+        assert api.cnhwc_chunk_plan(w["prob"], op) == [w["prob"]["n"]], name
+
+
+def test_chunk_planner_refuses_an_oversized_image():
+    p = P(2, 8, 8, 16, 16, 3, 3, 1, 1, 1)
+    with api.override(chunk_limit_bytes=1000):
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_chunk_plan(p, api.OP_DGRAD)
+    assert e.value.status == api.UNSUPPORTED and "one image" in e.value.reason
+
+
+def test_chunk_planner_uses_the_largest_view():
+    # dgrad with stride 2: dx per image is 4x dy per image
+    p = P(6, 16, 16, 8, 8, 3, 3, 2, 1, 1)
+    dx_img = 16 * 16 * 8 * 2
+    with api.override(chunk_limit_bytes=dx_img * 2):
+        assert api.cnhwc_chunk_plan(p, api.OP_DGRAD) == [2, 2, 2]
+
+
+def test_workspace_only_for_split_c():
+    w = wl("c4a_splitc_fwd")
+    p = w["prob"]
+    name, var = api.cnhwc_plan(p, api.OP_FWD)
+    assert var == api.VAR_FWD_SPLITC
+    split = int(re.search(r"splitc(\d+)", name).group(1))
+    assert split >= 2
+    assert api.cnhwc_workspace_size(p, api.OP_FWD) == split * 8 * 7 * 7 * 512 * 4
+    assert api.cnhwc_workspace_size(wl("c3a_3x3_s1")["prob"], api.OP_DGRAD) == 0
+    assert api.cnhwc_workspace_size(wl("c4b_grouped_fwd")["prob"], api.OP_FWD) == 0
+
+
+def test_pointer_checks_precede_any_launch():
+    p = P(1, 8, 8, 16, 16, 1, 1)
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_dgrad(p, None, None, None, None, 0, None)
+    assert e.value.status == api.INVALID_ARG and "NULL" in e.value.reason
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_dgrad(p, 0x10008, 0x20000, 0x30000, None, 0, None)
+    assert e.value.status == api.MISALIGNED
+    with pytest.raises(api.CnhwcError) as e:  # dx overlaps dy
+        api.cnhwc_dgrad(p, 0x100000, 0x200000, 0x100000 + 64, None, 0, None)
+    assert e.value.status == api.INVALID_ARG and "overlaps" in e.value.reason
+
+
+def test_split_c_workspace_checks():
+    w = wl("c4a_splitc_fwd")
+    p = w["prob"]
+    need = api.cnhwc_workspace_size(p, api.OP_FWD)
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_fwd(p, 0x1000000, 0x4000000, 0x8000000, 0x10000000, need - 16, None)
+    assert e.value.status == api.WORKSPACE_TOO_SMALL
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_fwd(p, 0x1000000, 0x4000000, 0x8000000, None, need, None)
+    assert e.value.status == api.INVALID_ARG
+
+
+def test_last_error_clears_after_success():
+    with pytest.raises(api.CnhwcError):
+        api.cnhwc_out_dims(P(0, 8, 8, 8, 8, 1, 1))
+    assert api.last_error() != ""
+    api.cnhwc_out_dims(P(1, 8, 8, 8, 8, 1, 1))
+    assert api.last_error() == ""
