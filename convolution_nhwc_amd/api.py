@@ -44,7 +44,7 @@ class Problem(ctypes.Structure):
 
 class Override(ctypes.Structure):
     _fields_ = [("variant", ctypes.c_int32), ("cpl", ctypes.c_int32), ("split_c", ctypes.c_int32),
-                ("reserved", ctypes.c_int32), ("chunk_limit_bytes", ctypes.c_int64)]
+                ("tune", ctypes.c_int32), ("chunk_limit_bytes", ctypes.c_int64)]
 
 
 _lib = None
@@ -138,8 +138,8 @@ def cnhwc_dgrad(p, dy, w, dx, ws, ws_bytes, stream):
     _check(lib().cnhwc_dgrad(ctypes.byref(_problem(p)), dy, w, dx, ws, ws_bytes, stream))
 
 
-def cnhwc_set_override(variant=0, cpl=0, split_c=0, chunk_limit_bytes=0):
-    _check(lib().cnhwc_set_override(ctypes.byref(Override(variant, cpl, split_c, 0,
+def cnhwc_set_override(variant=0, cpl=0, split_c=0, chunk_limit_bytes=0, tune=0):
+    _check(lib().cnhwc_set_override(ctypes.byref(Override(variant, cpl, split_c, tune,
                                                           chunk_limit_bytes))))
 
 

@@ -74,6 +74,8 @@ struct IgemmArgs {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Asynchronous 16-byte global -> LDS load: lane l writes lds_base + 16*l.
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base, uint32_t voff,

@@ -151,6 +151,7 @@ int choose(const Prob& p, int op, Plan* out) {
         if (!why.empty()) return fail(CNHWC_UNSUPPORTED, why);
         if (pl.variant != CNHWC_VAR_FWD_SPLITC) pl.split_c = 1;
         pl.name = plan_name(p, pl);
+        pl.tune = ov.tune;
         *out = pl;
         return CNHWC_OK;
     }
@@ -158,7 +159,7 @@ int choose(const Prob& p, int op, Plan* out) {
     auto take = [&](int v, int cpl, int split) -> bool {
         std::string why = variant_reason(p, op, v, cpl, split);
         if (!why.empty()) {
-            tried += (tried.empty() ? "" : "; ") + plan_name(p, Plan{v, cpl, split, 0, ""}) + ": " + why;
+            tried += (tried.empty() ? "" : "; ") + plan_name(p, Plan{v, cpl, split, 0, 0, ""}) + ": " + why;
             return false;
         }
         pl.variant = v; pl.cpl = cpl; pl.split_c = split;
@@ -190,6 +191,7 @@ int choose(const Prob& p, int op, Plan* out) {
     }
     if (!ok) return fail(CNHWC_UNSUPPORTED, "no kernel accepts the problem: " + tried);
     pl.name = plan_name(p, pl);
+    pl.tune = ov.tune;
     *out = pl;
     return CNHWC_OK;
 }
@@ -393,6 +395,7 @@ int cnhwc_set_override(const cnhwc_override* ov) {
     if (ov->cpl != 0 && ov->cpl != 1 && ov->cpl != 2 && ov->cpl != 4 && ov->cpl != 8)
         return fail(CNHWC_INVALID_ARG, "cpl must be 1, 2, 4 or 8 (got " + std::to_string(ov->cpl) + ")");
     if (ov->split_c < 0) return fail(CNHWC_INVALID_ARG, "split_c must be >= 0");
+    if (ov->tune < 0) return fail(CNHWC_INVALID_ARG, "tune must be >= 0");
     if (ov->chunk_limit_bytes < 0) return fail(CNHWC_INVALID_ARG, "chunk_limit_bytes must be >= 0");
     g_ov = *ov;
     g_err.clear();

@@ -26,6 +26,7 @@ struct Plan {
     int32_t cpl = 0;      // depthwise channels per lane
     int32_t split_c = 1;  // channel splits of the split-C forward
     int32_t tile = 0;     // variant-specific tile selector
+    int32_t tune = 0;     // test-only launch-shape knob (0 = automatic)
     std::string name;
 };
 

@@ -134,13 +134,14 @@ const char* cnhwc_last_error(void);
  * keeps the automatic choice.  variant: a CNHWC_VAR_* to force (the call fails
  * with UNSUPPORTED and the variant's reason if it cannot run the problem);
  * cpl: depthwise channels per lane (1, 2, 4 or 8); split_c: number of channel
- * splits for CNHWC_VAR_FWD_SPLITC; chunk_limit_bytes: the per-view byte limit
- * of the chunk planner.  Pass NULL to clear. */
+ * splits for CNHWC_VAR_FWD_SPLITC; tune: a launch-shape knob of the chosen
+ * kernel (unused by the current kernels); chunk_limit_bytes: the
+ * per-view byte limit of the chunk planner.  Pass NULL to clear. */
 typedef struct cnhwc_override {
     int32_t variant;
     int32_t cpl;
     int32_t split_c;
-    int32_t reserved;
+    int32_t tune;           /* kernel-specific launch-shape knob for tuning sweeps (0 = automatic) */
     int64_t chunk_limit_bytes;
 } cnhwc_override;
 
