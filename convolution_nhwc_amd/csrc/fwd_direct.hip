@@ -56,6 +56,7 @@ struct FwdArgs {
     int splits, csplit;   // channel splits and channels per split
     int nblocks;
     int remap;
+    int halo_bytes;   // LDS bytes of one halo stage
 };
 
 __device__ inline uint32_t swz(int row, int chunk) { return uint32_t((chunk ^ (row & 7)) * 16); }
@@ -71,12 +72,13 @@ __device__ inline void tile_origin(const Geo& g, int pt, int& n0, int& ho0, int&
 }
 
 template <typename T, bool SPLIT>
-__global__ __launch_bounds__(kThreads, 2) void fwd_direct_kernel(const FwdArgs a) {
-    constexpr int HALO_BYTES = kHaloMax * 128;
+__global__ __launch_bounds__(kThreads) void fwd_direct_kernel(const FwdArgs a) {
     constexpr int B_BYTES = kBN * 128;
-    constexpr int STAGE = HALO_BYTES + B_BYTES;
     constexpr int WM = kBM / 2, WN = kBN / 2, FM = WM / 16, FN = WN / 16;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[2 * STAGE];
+    // dynamic LDS: [halo 0][halo 1][weights 0][weights 1]; halo = a.halo_bytes
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    const int HALO_BYTES = a.halo_bytes;
+    unsigned char* const wbase = lds + 2 * HALO_BYTES;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Geo& geo = a.geo;
@@ -149,7 +151,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_direct_kernel(const FwdArgs a
         }
     };
     auto store_halo = [&](int buf) {
-        unsigned char* hs = lds + buf * STAGE;
+        unsigned char* hs = lds + buf * HALO_BYTES;
 #pragma unroll
         for (int j = 0; j < kHaloSlots; ++j) {
             const int hp = (tid >> 3) + j * (kThreads / 8);
@@ -157,7 +159,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_direct_kernel(const FwdArgs a
         }
     };
     auto store_w = [&](int buf) {
-        unsigned char* bs = lds + buf * STAGE + HALO_BYTES;
+        unsigned char* bs = wbase + buf * B_BYTES;
 #pragma unroll
         for (int j = 0; j < 2; ++j) {
             const int kr = (tid >> 3) + j * 32;
@@ -188,8 +190,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_direct_kernel(const FwdArgs a
         for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
     auto compute = [&](int buf, int tap) {
-        const unsigned char* hs = lds + buf * STAGE;
-        const unsigned char* bs = hs + HALO_BYTES;
+        const unsigned char* hs = lds + buf * HALO_BYTES;
+        const unsigned char* bs = wbase + buf * B_BYTES;
         const int r = tap / a.S, t = tap - (tap / a.S) * a.S;
         const int toff = r * geo.IW + t;
 #pragma unroll
@@ -233,8 +235,8 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_direct_kernel(const FwdArgs a
             }
             // halo of chunk cc sits in buffer (cc & 1); weights of step st in (st & 1)
             {
-                const unsigned char* hs = lds + (cc & 1) * STAGE;
-                const unsigned char* bs = lds + (st & 1) * STAGE + HALO_BYTES;
+                const unsigned char* hs = lds + (cc & 1) * HALO_BYTES;
+                const unsigned char* bs = wbase + (st & 1) * B_BYTES;
                 const int r = tap / a.S, t = tap - (tap / a.S) * a.S;
                 const int toff = r * geo.IW + t;
 #pragma unroll
@@ -270,7 +272,7 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_direct_kernel(const FwdArgs a
     // ---- epilogue through LDS: rows = tile pixels, columns = BN channels ----
     constexpr int ESZ = SPLIT ? 4 : 2;
     constexpr int C_STRIDE = kBN * ESZ + 16;
-    static_assert(kBM * C_STRIDE <= 2 * STAGE, "epilogue tile fits");
+    // the launcher sizes LDS to at least kBM * C_STRIDE for the epilogue tile
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
@@ -345,17 +347,18 @@ struct GrpArgs {
     int gsets;        // G / gm
     Geo geo;
     int nblocks, remap;
+    int halo_bytes;   // LDS bytes of the halo (start of the weight taps)
 };
 
 template <typename T, int BN>
-__global__ __launch_bounds__(kThreads, 2) void fwd_grouped_kernel(const GrpArgs a) {
-    constexpr int HALO_BYTES = kGHaloMax * 64;
+__global__ __launch_bounds__(kThreads) void fwd_grouped_kernel(const GrpArgs a) {
     constexpr int W_TAP = BN * 64;              // one tap: BN rows x 32 channels
     constexpr int FM = kBM / 16 / 4;            // 2 row blocks per wave (waves split M)
     constexpr int FN = BN / 16;
-    __shared__ __attribute__((aligned(16))) unsigned char lds[HALO_BYTES + kMaxTaps * W_TAP];
+    // dynamic LDS: the halo (64 B a pixel) then the block-diagonal taps
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
     unsigned char* hs = lds;
-    unsigned char* ws = lds + HALO_BYTES;
+    unsigned char* ws = lds + a.halo_bytes;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
     const Geo& geo = a.geo;
@@ -395,21 +398,34 @@ __global__ __launch_bounds__(kThreads, 2) void fwd_grouped_kernel(const GrpArgs 
         *reinterpret_cast<i32x4*>(hs + hp * 64 + (((hchunk ^ (hp & 3))) * 16)) = v;
     }
     // block-diagonal weights: row kk (output channel of the set) has the Cg
-    // weights of its group at columns (kk / Kg) * Cg .. +Cg, zeros elsewhere
-    const int wtotal = taps * BN * kGBK;
-    for (int e = tid; e < wtotal; e += kThreads) {
-        const int col = e % kGBK;
-        const int row = (e / kGBK) % BN;
-        const int tap = e / (kGBK * BN);
-        const int gl = row / a.Kg;              // group within the set
-        unsigned short v = 0;
-        if (col / a.Cg == gl && row < a.bn) {
-            const int k = kbase + row;
-            v = buf_load2(rw, uint32_t((k * taps + tap) * a.Cg + (col - gl * a.Cg)) * 2u);
+    // weights of its group at columns (kk / Kg) * Cg .. +Cg, zeros elsewhere.
+    // Staged per 16-byte LDS chunk (8 merged channels of one row and tap).
+    const int nchunks = taps * BN * 4;
+    for (int e = tid; e < nchunks; e += kThreads) {
+        const int c8 = e & 3;
+        const int row = (e >> 2) % BN;
+        const int tap = (e >> 2) / BN;
+        const int gl = row / a.Kg;              // group of this output channel within the set
+        const int k = kbase + row;
+        i32x4 v = {0, 0, 0, 0};
+        if (a.Cg % 8 == 0) {
+            // the chunk lies inside one group's channel block
+            if (row < a.bn && (c8 * 8) / a.Cg == gl)
+                v = buf_load16(rw, uint32_t((k * taps + tap) * a.Cg + c8 * 8 - gl * a.Cg) * 2u);
+        } else {
+            // several groups share the chunk: element by element
+            uint32_t h[8];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int col = c8 * 8 + q;
+                h[q] = (row < a.bn && col / a.Cg == gl)
+                           ? uint32_t(buf_load2(rw, uint32_t((k * taps + tap) * a.Cg + col - gl * a.Cg) * 2u))
+                           : 0u;
+            }
+            v = i32x4{int(h[0] | (h[1] << 16)), int(h[2] | (h[3] << 16)), int(h[4] | (h[5] << 16)),
+                      int(h[6] | (h[7] << 16))};
         }
-        const int chunk = col >> 3;
-        *reinterpret_cast<unsigned short*>(ws + tap * W_TAP + row * 64 +
-                                           ((chunk ^ (row & 3)) * 16) + (col & 7) * 2) = v;
+        *reinterpret_cast<i32x4*>(ws + tap * W_TAP + row * 64 + ((c8 ^ (row & 3)) * 16)) = v;
     }
     __syncthreads();
 
@@ -572,12 +588,11 @@ int64_t fwd_direct_tiles(const Prob& p) {
 int fwd_direct_auto_split(const Prob& p) {
     if (p.groups != 1) return 1;
     const int64_t tiles = fwd_direct_tiles(p);
-    if (tiles <= 0 || tiles * 2 > kNumCUs) {
-        if (tiles <= 0 || tiles >= kNumCUs / 2) return 1;
-    }
+    if (tiles <= 0 || tiles >= kNumCUs / 2) return 1;
+    // two blocks fit a CU (LDS), so aim for up to 2 * CUs blocks
     int best = 1;
     for (int sc = 2; sc <= 64; sc *= 2) {
-        if (tiles * sc > kNumCUs) break;
+        if (tiles * sc > 2 * kNumCUs) break;
         if (p.c % sc != 0 || p.c / sc < 128 || (p.c / sc) % 8 != 0) break;
         best = sc;
     }
@@ -604,9 +619,20 @@ int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* 
     a.nblocks = int(blocks);
     a.remap = (blocks % 8 == 0) ? 1 : 0;
     const bool bf = p.dtype == CNHWC_BF16;
+    a.halo_bytes = a.geo.NB * a.geo.IH * a.geo.IW * 128;
+    const size_t stages = size_t(2) * a.halo_bytes + size_t(2) * kBN * 128;
+    const size_t epi = size_t(kBM) * (kBN * (split ? 4 : 2) + 16);
+    const size_t lds = std::max(stages, epi);
+    const void* fn = split ? (bf ? reinterpret_cast<const void*>(&fwd_direct_kernel<BF16, true>)
+                                 : reinterpret_cast<const void*>(&fwd_direct_kernel<F16, true>))
+                           : (bf ? reinterpret_cast<const void*>(&fwd_direct_kernel<BF16, false>)
+                                 : reinterpret_cast<const void*>(&fwd_direct_kernel<F16, false>));
+    if (lds > 64 * 1024 &&
+        hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+        return CNHWC_HIP_ERROR;
     if (split) {
-        if (bf) hipLaunchKernelGGL((fwd_direct_kernel<BF16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((fwd_direct_kernel<F16, true>), dim3(blocks), dim3(kThreads), 0, st, a);
+        if (bf) hipLaunchKernelGGL((fwd_direct_kernel<BF16, true>), dim3(blocks), dim3(kThreads), lds, st, a);
+        else hipLaunchKernelGGL((fwd_direct_kernel<F16, true>), dim3(blocks), dim3(kThreads), lds, st, a);
         const int64_t total4 = m * p.k / 4;
         const int64_t grid = std::min<int64_t>((total4 + 255) / 256, int64_t(kNumCUs) * 8);
         if (bf)
@@ -618,8 +644,8 @@ int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* 
                                static_cast<const float*>(ws), static_cast<unsigned short*>(y),
                                total4, total4, a.splits);
     } else {
-        if (bf) hipLaunchKernelGGL((fwd_direct_kernel<BF16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
-        else hipLaunchKernelGGL((fwd_direct_kernel<F16, false>), dim3(blocks), dim3(kThreads), 0, st, a);
+        if (bf) hipLaunchKernelGGL((fwd_direct_kernel<BF16, false>), dim3(blocks), dim3(kThreads), lds, st, a);
+        else hipLaunchKernelGGL((fwd_direct_kernel<F16, false>), dim3(blocks), dim3(kThreads), lds, st, a);
     }
     return CNHWC_OK;
 }
@@ -641,10 +667,17 @@ int launch_fwd_grouped(const Prob& p, const Plan&, const void* x, const void* w,
     a.nblocks = int(blocks);
     a.remap = (blocks % 8 == 0) ? 1 : 0;
     const bool bf = p.dtype == CNHWC_BF16;
+    a.halo_bytes = a.geo.NB * a.geo.IH * a.geo.IW * 64;
 #define CNHWC_GRP(BNV)                                                                          \
     if (a.bn <= BNV) {                                                                          \
-        if (bf) hipLaunchKernelGGL((fwd_grouped_kernel<BF16, BNV>), dim3(blocks), dim3(kThreads), 0, st, a); \
-        else hipLaunchKernelGGL((fwd_grouped_kernel<F16, BNV>), dim3(blocks), dim3(kThreads), 0, st, a);     \
+        const size_t lds = size_t(a.halo_bytes) + size_t(p.r * p.s) * BNV * 64;                 \
+        const void* fn = bf ? reinterpret_cast<const void*>(&fwd_grouped_kernel<BF16, BNV>)     \
+                            : reinterpret_cast<const void*>(&fwd_grouped_kernel<F16, BNV>);     \
+        if (lds > 64 * 1024 &&                                                                  \
+            hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess) \
+            return CNHWC_HIP_ERROR;                                                             \
+        if (bf) hipLaunchKernelGGL((fwd_grouped_kernel<BF16, BNV>), dim3(blocks), dim3(kThreads), lds, st, a); \
+        else hipLaunchKernelGGL((fwd_grouped_kernel<F16, BNV>), dim3(blocks), dim3(kThreads), lds, st, a);     \
         return CNHWC_OK;                                                                        \
     }
     CNHWC_GRP(32)
