@@ -15,6 +15,7 @@ the fp64 CPU oracle timed on a bounded sample of the headline workload.
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-shapes]
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -27,6 +28,10 @@ MFMA_PEAK_TFLOPS = 2500.0      # dense fp16 / bf16
 VALU_PEAK_TFLOPS = 157.3       # fp32 vector (two FMAs per lane per cycle)
 HEADLINE = "c2_pointwise"
 ROTATE_BYTES = 1 << 30         # >= 4x the Infinity Cache
+ROOT = os.path.dirname(os.path.abspath(__file__))
+# HBM bytes per launch read from rocprofv3 FETCH_SIZE / WRITE_SIZE counters,
+# keyed by workload, with a hash of the kernel sources they were taken on.
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
 
 
 def parse():
@@ -39,6 +44,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (scales the HBM byte counters)")
+    ap.add_argument("--source-hash", nargs="+", metavar="FILE",
+                    help="print the hash recorded with counter-based traffic for these sources")
     return ap.parse_args()
 
 
@@ -67,6 +74,32 @@ def metrics(name):
     bound = "hbm" if t_hbm >= t_cmp else ("alu" if depthwise else "mfma")
     return dict(bytes=alg_bytes, nominal_flops=nominal, valid_flops=valid, bound=bound,
                 t_ideal_s=max(t_hbm, t_cmp))
+
+
+def source_hash(paths):
+    h = hashlib.sha256()
+    for rel in paths:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def recorded_traffic(workload):
+    """HBM bytes per launch from the committed counter runs, or None when there
+    is no record or the kernel sources changed since the counters were taken."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            ent = json.load(f).get(workload)
+    except (OSError, ValueError):
+        return None
+    if not ent:
+        return None
+    try:
+        if source_hash(ent["sources"]) != ent["sources_sha256"]:
+            return None
+    except OSError:
+        return None
+    return ent["hbm_bytes_per_launch"]
 
 
 class Workload:
@@ -168,6 +201,9 @@ def copy_calibration():
 
 def main():
     args = parse()
+    if args.source_hash:
+        print(source_hash(args.source_hash))
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(each image is independent; see the design notes on sharding over N).",
@@ -189,6 +225,18 @@ def main():
     m = metrics(head.name)
     gbs = m["bytes"] / (ms * 1e-3) / 1e9
     tflops = m["nominal_flops"] / (ms * 1e-3) / 1e12
+    if m["bound"] == "hbm":
+        roof = {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    elif m["bound"] == "mfma":
+        roof = {"bound": "mfma", "achieved": round(tflops, 3), "peak": MFMA_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(tflops / MFMA_PEAK_TFLOPS, 4)}
+    else:
+        vt = m["valid_flops"] / (ms * 1e-3) / 1e12
+        roof = {"bound": "alu", "achieved": round(vt, 3), "peak": VALU_PEAK_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(vt / VALU_PEAK_TFLOPS, 4)}
+    roof["traffic"] = recorded_traffic(head.name)
+    roof["algorithmic_bytes"] = int(m["bytes"])
     line = {
         "metric": "effective conv TFLOP/s and HBM GB/s per shape, % of MI355X roofline",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
@@ -198,8 +246,7 @@ def main():
                    **{k: head.p[k] for k in ("n", "h", "w", "c", "k", "r", "s", "stride",
                                              "pad_h", "pad_w", "groups")}},
         "effective_tflops": round(tflops, 3),
-        "roofline": {"bound": "hbm", "achieved": round(gbs, 2), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None},
+        "roofline": roof,
     }
     del head
     torch.cuda.empty_cache()
