@@ -1,6 +1,7 @@
-// Backward-data convolution as implicit GEMMs on the gfx950 matrix cores,
-// with the 1x1 pointwise fast path as a compile-time specialisation of the
-// same kernel.
+// Backward-data convolution as implicit GEMMs on the gfx950 matrix cores:
+// a ring kernel (both operands streamed per reduction step; also the 1x1
+// pointwise fast path, as a compile-time specialisation) and a dY-window
+// kernel for stride-1 problems whose filters have two or more taps.
 //
 // Strided dgrad splits dX into stride*stride phase classes (h mod s, w mod s)
 // -- the "tilde" decomposition of "perf(rocke/conv): add the pointwise fast
@@ -10,37 +11,41 @@
 // exactly one row per step of i, so each class is a dense GEMM
 //     dX_class[m, c] = sum_{i, j, k} dY[n, u0(m) - i, v0(m) - j, g*Kg + k] * W[g*Kg + k, r_i, t_j, c]
 // with M = the class's pixels, N = Cg, and reduction Kg * taps.  Classes with
-// no tap write zeros.  All classes run in one launch, heaviest first; a block
-// finds its class in a small table in the kernel arguments (a few scalar
-// compares, no divide in the reduction loop).
+// no tap write zeros.  All classes of a kernel run in one launch, heaviest
+// first; a block finds its class in a small table in the kernel arguments (a
+// few scalar compares, no divide in the reduction loop).
 //
 // For 1x1, stride 1, no padding and one group the decomposition is the
 // identity (one class, Hc = H, Wc = W, one tap): the dY offset of GEMM row m is
 // m*K + k and the W offset is k*C + c (same page, the fast-path commit).  The PW
 // specialisation uses exactly those offsets; the reduction order (ascending
 // 32-deep MFMA steps with the same lane/k assignment) and the rounding are the
-// same, so it is bit-identical to the general kernel on the same problem.
+// same, so it is bit-identical to the general kernel on the same problem (the
+// general path runs one-tap classes on this same ring kernel).
 //
-// Data path (gfx950): both operands go global -> LDS with asynchronous
-// buffer loads that write LDS directly (no VGPR staging) into a ring of three
-// stages, so two 64-deep reduction steps are in flight while one is
-// multiplied.  dY tiles are 128-byte k-rows (16-byte chunks XOR-swizzled by
+// Ring kernel data path (gfx950): both operands go global -> LDS with
+// asynchronous buffer loads that write LDS directly (no VGPR staging) into a
+// ring of three stages, so two 64-deep reduction steps are in flight while one
+// is multiplied.  dY tiles are 128-byte k-rows (16-byte chunks XOR-swizzled by
 // row); W tiles keep their natural c-contiguous rows (chunks swizzled by k) and
 // are read as MFMA operands with the LDS transpose read (ds_read_b64_tr_b16),
-// which hands each lane four consecutive k of one channel.  Every per-lane
-// address is computed once: in the loop, the uniform parts of the global
-// offsets go in the scalar offset field and the stage offsets in the LDS
-// instructions' immediate field (the loop is unrolled over the stages).  The
-// MFMA computes the transposed tile (channels x pixels) so each lane ends with
-// four consecutive channels of one pixel; the epilogue rounds to fp16/bf16
-// (RNE) and restages through LDS for full 16-byte row stores.  Out-of-range
-// taps, rows and channels read zero through the buffer descriptors' range check.
+// which hands each lane four consecutive k of one channel.  Per-lane base
+// addresses are computed once; in the loop the uniform parts of the global
+// offsets go in the scalar offset field, the stage offsets in the LDS
+// instructions' immediate field, and a tap's validity per row is one bit of a
+// per-lane mask, folded into bit 31 of the load offset (out of range, so the
+// buffer descriptor returns zeros).  Each step's LDS reads and loads are
+// placed between its matrix instructions.  The MFMA computes the transposed
+// tile (channels x pixels) so each lane ends with four consecutive channels of
+// one pixel; the epilogue rounds to fp16/bf16 (RNE) and restages through LDS
+// for full 16-byte row stores.
 #include "device.h"
 #include "internal.h"
 
 #include <algorithm>
 #include <string>
 #include <type_traits>
+#include <utility>
 
 namespace cnhwc {
 namespace {
@@ -74,8 +79,6 @@ struct IgemmArgs {
 };
 
 typedef __attribute__((address_space(3))) void lds_void;
-typedef short i16x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
 
 // Asynchronous 16-byte global -> LDS load: lane l writes lds_base + 16*l.
 __device__ inline void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base, uint32_t voff,
@@ -110,7 +113,17 @@ __device__ inline uint32_t lds_addr(const void* p) {
 template <int I>
 using IC = std::integral_constant<int, I>;
 
-template <typename T, int WMB, int WNB, bool PW>
+// Compile-time loop: f(IC<0>{}), ..., f(IC<N-1>{}).
+template <typename F, int... I>
+__device__ inline void sfor_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(IC<I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void sfor(F&& f) {
+    sfor_impl(f, std::make_integer_sequence<int, N>{});
+}
+
+template <typename T, int WMB, int WNB, bool PW, bool KR>
 __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArgs a) {
     constexpr int WAVES_M = 2, WAVES_N = 2;
     constexpr int BMC = WAVES_M * WMB * 16;             // tile capacity in pixels
@@ -166,11 +179,13 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
     const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
 
     // ---- per-lane A (dY) sources: region q = wave + 4*i holds rows 8q .. 8q+7 ----
-    // a_base: byte offset of the row's dY pixel at tap (0, 0) plus its chunk,
-    // or -1 past the tile; a_umask / a_vmask: bit i (j) set when tap row i
-    // (column j) of the class lands inside dY for this row.
-    int a_base[A_REG];
-    uint32_t a_umask[A_REG], a_vmask[A_REG];
+    // a_base: byte offset of the row's dY pixel at tap (0, 0) plus its chunk
+    // (kOob past the tile); a_inv: bit ti*nt + tj set when tap (ti, tj) of the
+    // class misses dY for this row.  The load offset of a tap is then
+    // (a_base - tap_bytes) with bit 31 set for a missing tap, which the buffer
+    // range check (views < 2^31 bytes) turns into a zero read.
+    uint32_t a_base[A_REG];
+    uint64_t a_inv[A_REG];
     int a_kq[A_REG];
 #pragma unroll
     for (int i = 0; i < A_REG; ++i) {
@@ -178,13 +193,12 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
         const int chunk = (lane & 7) ^ swz_a(row);
         a_kq[i] = chunk * 8;
         const int m = m_lo + row;
-        a_base[i] = -1;
-        a_umask[i] = 0;
-        a_vmask[i] = 0;
+        a_base[i] = kOob;
+        a_inv[i] = ~uint64_t(0);
         if (row < a.bm && m < m_hi) {
             if (PW) {
-                a_base[i] = (m * a.K + chunk * 8) * 2;
-                a_umask[i] = a_vmask[i] = 1;
+                a_base[i] = uint32_t((m * a.K + chunk * 8) * 2);
+                a_inv[i] = 0;
             } else {
                 const int hw = cl.hc * cl.wc;
                 const int n = m / hw;
@@ -193,13 +207,15 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
                 const int wc = rem - hc * cl.wc;
                 const int u0 = (cl.a + s * hc + a.pad_h - cl.r0) / s;
                 const int v0 = (cl.b + s * wc + a.pad_w - cl.t0) / s;
+                uint64_t vmask = 0, valid = 0;
 #pragma unroll 1
-                for (int t = 0; t < cl.nr && t < 32; ++t)
-                    if (u0 - t >= 0 && u0 - t < a.Ho) a_umask[i] |= 1u << t;
+                for (int t = 0; t < cl.nt; ++t)
+                    if (v0 - t >= 0 && v0 - t < a.Wo) vmask |= uint64_t(1) << t;
 #pragma unroll 1
-                for (int t = 0; t < cl.nt && t < 32; ++t)
-                    if (v0 - t >= 0 && v0 - t < a.Wo) a_vmask[i] |= 1u << t;
-                a_base[i] = (((n * a.Ho + u0) * a.Wo + v0) * a.K + g * a.Kg + chunk * 8) * 2;
+                for (int t = 0; t < cl.nr; ++t)
+                    if (u0 - t >= 0 && u0 - t < a.Ho) valid |= vmask << (t * cl.nt);
+                a_inv[i] = ~valid;
+                a_base[i] = uint32_t((((n * a.Ho + u0) * a.Wo + v0) * a.K + g * a.Kg + chunk * 8) * 2);
             }
         }
     }
@@ -217,45 +233,42 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
         b_krow[i] = krow;
         b_voff[i] = c < a.Cg ? uint32_t((krow * wk_stride + chunk * 8) * 2) : kOob;
     }
-    const bool k_ragged = (a.Kg % kBK) != 0;
 
     const int kchunks = (a.Kg + kBK - 1) / kBK;
     const int steps = cl.nr * cl.nt * kchunks;
 
-    // A offsets of the current tap: recomputed (branch-free per lane) when a
-    // step starts a new tap; the 64-element k offset goes in the scalar offset.
-    uint32_t a_cur[A_REG];
-    auto set_tap = [&](int ti, int tj) {
-        const int tap_bytes = (ti * a.Wo + tj) * a.K * 2;
-#pragma unroll
-        for (int i = 0; i < A_REG; ++i) {
-            const uint32_t bit = (a_umask[i] >> ti) & (a_vmask[i] >> tj) & 1u;
-            a_cur[i] = bit ? uint32_t(a_base[i] - tap_bytes) : kOob;
-        }
+    // Issue cursor (uniform): reduction step = (tap (ti, tj), 64-deep chunk kk).
+    // It runs two steps ahead of the multiply and is advanced without
+    // branches; past the last step it keeps producing offsets whose loads are
+    // either range-checked zeros or in-range data of stages never multiplied.
+    int cur_kk = 0, cur_ti = 0, cur_tj = 0, cur_tap = 0;
+    auto advance = [&]() {
+        cur_kk += kBK;
+        const bool wrap = cur_kk >= a.Kg;
+        cur_kk = wrap ? 0 : cur_kk;
+        cur_tap += wrap ? 1 : 0;
+        cur_tj += wrap ? 1 : 0;
+        const bool wrap2 = cur_tj >= cl.nt;
+        cur_tj = wrap2 ? 0 : cur_tj;
+        cur_ti += wrap2 ? 1 : 0;
     };
-    // issue the async loads of reduction step `step` into stage STG
-    auto issue = [&](auto stg, int step) {
-        constexpr int STG = decltype(stg)::value;
-        const int tap = step / kchunks;
-        const int kk = (step - tap * kchunks) * kBK;
-        const int ti = PW ? 0 : tap / cl.nt;
-        const int tj = PW ? 0 : tap - ti * cl.nt;
-        if (!PW && kk == 0) set_tap(ti, tj);
-        const uint32_t a_soff = uint32_t(kk * 2);
-#pragma unroll
-        for (int i = 0; i < A_REG; ++i) {
-            uint32_t v = a_cur[i];
-            if (k_ragged) v = (kk + a_kq[i] < a.Kg) ? v : kOob;
-            dma16(rdy, lds + STG * A_BYTES + (wave + 4 * i) * 1024, v, a_soff);
-        }
-        int rt = 0;
-        if (!PW) rt = (cl.r0 + s * ti) * a.S + cl.t0 + s * tj;
-        const uint32_t b_soff = uint32_t(((g * a.Kg + kk) * wk_stride + rt * a.Cg + c0) * 2);
-#pragma unroll
-        for (int i = 0; i < B_REG; ++i) {
-            uint32_t v = b_voff[i];
-            if (k_ragged) v = (kk + b_krow[i] < a.Kg) ? v : kOob;
-            dma16(rw, lds + B_BASE + STG * B_BYTES + (wave + 4 * i) * 1024, v, b_soff);
+    // one async 16-byte load per lane into region D of stage STG (D < A_REG:
+    // dY rows, else W k-rows)
+    auto dma_one = [&](auto stg, auto dsc) {
+        constexpr int STG = decltype(stg)::value, D = decltype(dsc)::value;
+        (void)a_base; (void)a_inv; (void)a_kq; (void)b_voff; (void)b_krow;
+        if constexpr (D < A_REG) {
+            const uint32_t tap_bytes = PW ? 0u : uint32_t((cur_ti * a.Wo + cur_tj) * a.K * 2);
+            uint32_t v = (a_base[D] - tap_bytes) | (uint32_t(a_inv[D] >> cur_tap) << 31);
+            if (KR) v = (cur_kk + a_kq[D] < a.Kg) ? v : kOob;
+            dma16(rdy, lds + STG * A_BYTES + (wave + 4 * D) * 1024, v, uint32_t(cur_kk * 2));
+        } else {
+            constexpr int E = D - A_REG;
+            const int rt = PW ? 0 : (cl.r0 + s * cur_ti) * a.S + cl.t0 + s * cur_tj;
+            const uint32_t b_soff = uint32_t(((g * a.Kg + cur_kk) * wk_stride + rt * a.Cg + c0) * 2);
+            uint32_t v = b_voff[E];
+            if (KR) v = (cur_kk + b_krow[E] < a.Kg) ? v : kOob;
+            dma16(rw, lds + B_BASE + STG * B_BYTES + (wave + 4 * E) * 1024, v, b_soff);
         }
     };
 
@@ -291,74 +304,98 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
 #pragma unroll
         for (int j = 0; j < WNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    i32x4 fa[2][WMB], fb[2][WNB];
-    auto read_frags = [&](auto stg, auto ksc) {
+    // fragments: [half of the 64-deep step][tile]; W tiles as two 8-byte halves
+    i32x4 fa[2][WMB];
+    i32x2 fb[2][WNB][2];
+    constexpr int NREAD = 2 * WNB + WMB;   // LDS reads per half step
+    // read R of half KS out of stage STG (R < 2*WNB: W transpose reads)
+    auto read_one = [&](auto stg, auto ksc, auto rc) {
         constexpr int STG = decltype(stg)::value, KS = decltype(ksc)::value;
-#pragma unroll
-        for (int j = 0; j < WNB; ++j) {
-            i32x2 lo, hi;
+        constexpr int R = decltype(rc)::value;
+        (void)fa; (void)fb; (void)fa_addr; (void)fb_addr;   // captured for every instantiation
+        if constexpr (R < 2 * WNB) {
             asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                         : "=v"(lo) : "v"(fb_addr[KS][j][0]), "i"(STG * B_BYTES));
-            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
-                         : "=v"(hi) : "v"(fb_addr[KS][j][1]), "i"(STG * B_BYTES));
-            fb[KS][j] = i32x4{lo[0], lo[1], hi[0], hi[1]};
-        }
-#pragma unroll
-        for (int i = 0; i < WMB; ++i) {
-            i32x4 v;
+                         : "=v"(fb[KS][R / 2][R % 2])
+                         : "v"(fb_addr[KS][R / 2][R % 2]), "i"(STG * B_BYTES));
+        } else {
             asm volatile("ds_read_b128 %0, %1 offset:%2"
-                         : "=v"(v) : "v"(fa_addr[KS][i]), "i"(STG * A_BYTES));
-            fa[KS][i] = v;
+                         : "=v"(fa[KS][R - 2 * WNB])
+                         : "v"(fa_addr[KS][R - 2 * WNB]), "i"(STG * A_BYTES));
         }
     };
-    // the LDS reads above are issued in asm, invisible to the compiler's wait
+    // the LDS reads are issued in asm, invisible to the compiler's wait
     // tracking: wait here and tie the fragments to the wait
     auto wait_frags = [&](auto ksc) {
         constexpr int KS = decltype(ksc)::value;
-        asm volatile("s_waitcnt lgkmcnt(0)"
-                     : "+v"(fa[KS][0]), "+v"(fb[KS][0]));
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[KS][0]), "+v"(fb[KS][0][0]));
 #pragma unroll
         for (int i = 1; i < WMB; ++i) asm volatile("" : "+v"(fa[KS][i]));
 #pragma unroll
-        for (int j = 1; j < WNB; ++j) asm volatile("" : "+v"(fb[KS][j]));
+        for (int j = 0; j < WNB; ++j) asm volatile("" : "+v"(fb[KS][j][0]), "+v"(fb[KS][j][1]));
     };
-    auto mfmas = [&](auto ksc) {
-        constexpr int KS = decltype(ksc)::value;
-#pragma unroll
-        for (int i = 0; i < WMB; ++i)
-#pragma unroll
-            for (int j = 0; j < WNB; ++j)
-                // transposed product: rows = channels (W), columns = pixels (dY)
-                acc[i][j] = mfma16x16x32<T>(fb[KS][j], fa[KS][i], acc[i][j]);
+    auto mfma_one = [&](auto ksc, auto mc) {
+        constexpr int KS = decltype(ksc)::value, M = decltype(mc)::value;
+        constexpr int i = M / WNB, j = M % WNB;
+        const i32x4 b = {fb[KS][j][0][0], fb[KS][j][0][1], fb[KS][j][1][0], fb[KS][j][1][1]};
+        // transposed product: rows = channels (W), columns = pixels (dY)
+        acc[i][j] = mfma16x16x32<T>(b, fa[KS][i], acc[i][j]);
     };
 
-    // one reduction step out of stage STG
-    auto step_fn = [&](auto stg, int st) {
+    // One reduction step out of stage STG, in two halves of 32.  First half:
+    // multiply half 0 while reading half 1's fragments and issuing the loads
+    // of the step two ahead into the stage freed by the previous step.  Then
+    // wait for the next stage to land (own loads + barrier).  Second half:
+    // multiply half 1 while reading half 0 of the next step.  Every LDS read
+    // and load is placed between two matrix instructions (scheduling
+    // barriers keep the order), so they issue under the matrix cores' work.
+    constexpr int NM = WMB * WNB;
+    constexpr int NI0 = NREAD + LOADS;
+    constexpr int PER0 = (NI0 + NM - 1) / NM;
+    constexpr int PER1 = (NREAD + NM - 1) / NM;
+    auto step_fn = [&](auto stg) {
         constexpr int STG = decltype(stg)::value;
-        const int later = min(steps - 1 - st, kStages - 2);   // stages issued after st
-        if (later >= 1) wait_vm<LOADS>();
-        else wait_vm<0>();
-        __builtin_amdgcn_s_barrier();
-        read_frags(stg, IC<0>{});
-        wait_frags(IC<0>{});
-        read_frags(stg, IC<1>{});
-        mfmas(IC<0>{});
-        // the next loads go out while the matrix cores work through the batch
-        if (st + kStages - 1 < steps) issue(IC<(STG + kStages - 1) % kStages>{}, st + kStages - 1);
+        constexpr int NXT = (STG + 1) % kStages, FREE = (STG + kStages - 1) % kStages;
+        sfor<NM>([&](auto mc) {
+            constexpr int M = decltype(mc)::value;
+            mfma_one(IC<0>{}, mc);
+            sfor<PER0>([&](auto pc) {
+                constexpr int X = M * PER0 + decltype(pc)::value;
+                if constexpr (X < NREAD) read_one(stg, IC<1>{}, IC<X>{});
+                else if constexpr (X < NI0) dma_one(IC<FREE>{}, IC<X - NREAD>{});
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        advance();
         wait_frags(IC<1>{});
-        mfmas(IC<1>{});
+        wait_vm<LOADS>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        sfor<NM>([&](auto mc) {
+            constexpr int M = decltype(mc)::value;
+            mfma_one(IC<1>{}, mc);
+            sfor<PER1>([&](auto pc) {
+                constexpr int X = M * PER1 + decltype(pc)::value;
+                if constexpr (X < NREAD) read_one(IC<NXT>{}, IC<0>{}, IC<X>{});
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        wait_frags(IC<0>{});
     };
 
     if (steps > 0) {
-#pragma unroll
-        for (int i = 0; i < A_REG; ++i) a_cur[i] = a_base[i] >= 0 ? uint32_t(a_base[i]) : kOob;
-        issue(IC<0>{}, 0);
-        if (steps > 1) issue(IC<1>{}, 1);
+        sfor<LOADS>([&](auto dc) { dma_one(IC<0>{}, dc); });
+        advance();
+        sfor<LOADS>([&](auto dc) { dma_one(IC<1>{}, dc); });
+        advance();
+        wait_vm<LOADS>();
+        __builtin_amdgcn_s_barrier();
+        sfor<NREAD>([&](auto rc) { read_one(IC<0>{}, IC<0>{}, rc); });
+        wait_frags(IC<0>{});
 #pragma unroll 1
         for (int st = 0; st < steps; st += kStages) {
-            step_fn(IC<0>{}, st);
-            if (st + 1 < steps) step_fn(IC<1>{}, st + 1);
-            if (st + 2 < steps) step_fn(IC<2>{}, st + 2);
+            step_fn(IC<0>{});
+            if (st + 1 < steps) step_fn(IC<1>{});
+            if (st + 2 < steps) step_fn(IC<2>{});
         }
         wait_vm<0>();
         __builtin_amdgcn_s_barrier();
@@ -398,15 +435,417 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
     }
 }
 
+// ---------------------------------------------------------------------------
+// General dgrad with the dY operand staged as an LDS window (classes with at
+// least two filter taps).
+//
+// A block owns a rectangle of th x tw pixels of one phase class of one image
+// (and one 128- or 64-channel slice of dX).  Per 64-deep chunk of K, the dY
+// window those pixels reach -- (th + nr - 1) x (tw + nt - 1) pixels -- is
+// loaded into LDS once and every filter tap of the class reads a shifted view
+// of it, so dY is fetched once per chunk instead of once per tap.  The window
+// is stored as 8 planes, one per 16-byte group of 8 channels, each a dense
+// array of window pixels: a tap shift is then a uniform offset of every lane's
+// read address, and the 16 lanes of an MFMA row group read 16 consecutive
+// 16-byte entries (no bank conflicts).  Two window buffers alternate between
+// chunks; the window of chunk c+2 is requested once the last tap of chunk c
+// has been read.
+//
+// The block runs 8 waves: two groups of 2 x 2 waves that compute the same
+// output tile over alternate reduction steps (group g takes the steps with
+// parity g).  One matrix-core wave per SIMD cannot issue MFMAs back to back;
+// two waves per SIMD can, and each wave's LDS reads then overlap the other's
+// matrix work.  W tiles stream through a 4-stage ring (each group loads its
+// own steps); the groups' fp32 partial sums are added once at the end.  The
+// reduction runs chunk-outer, tap-inner.
+constexpr int kMaxQ = 7;          // 64-pixel groups per window plane (448 pixels)
+constexpr int kHaloThreads = 512;
+constexpr int kRing = 4;          // W ring stages of the window kernel
+constexpr int kLdsMax = 160 * 1024;
+
+struct HaloClass {
+    int a, b;            // phase: h = a + s*hc, w = b + s*wc
+    int hc, wc;          // class extents (rows, columns of dX in the class)
+    int r0, t0, nr, nt;  // first filter row / column touching the class, and their counts
+    int u_off, v_off;    // tap (0, 0) of class pixel (hc, wc) reads dY (hc + u_off, wc + v_off)
+    int th, tw;          // tile rows / columns
+    int bands_h, bands_w;
+    int hw;              // window columns (tw + nt - 1)
+    int hp;              // window plane entries (a multiple of 64)
+    int tile_begin;      // first block of the class
+    int nblocks;         // blocks of the class
+};
+
+struct HaloArgs {
+    const void* dy;
+    const void* w;
+    void* dx;
+    uint32_t dy_bytes, w_bytes, dx_bytes;
+    int N, H, W, C, K, R, S, stride, Ho, Wo, Cg, Kg, G;
+    int ctiles;
+    int nclasses;
+    int remap;
+    uint32_t halo_bytes;  // one window buffer: 8 planes x hp x 16 bytes, maximum over classes
+    HaloClass cls[kMaxClasses];
+};
+
+template <typename T, int WMB, int WNB, bool KR>
+__global__ __launch_bounds__(kHaloThreads, 1) void dgrad_halo_kernel(const HaloArgs a) {
+    constexpr int WAVES_N = 2;
+    constexpr int BMC = 2 * WMB * 16;                   // tile capacity in pixels
+    constexpr int BN = WAVES_N * WNB * 16;              // channels per tile
+    constexpr int B_ROW = BN * 2;
+    constexpr int B_CHUNKS = BN / 8;
+    constexpr int B_BYTES = kBK * B_ROW;
+    constexpr int B_REG = B_BYTES / 1024 / 4;           // loads per lane per stage (4 waves)
+    constexpr int B_ROWS_PER_REG = 1024 / B_ROW;
+    constexpr int C_STRIDE = BN * 2 + 16;
+    static_assert(B_BYTES % 4096 == 0, "W stage splits over 4 waves");
+    static_assert(3 * B_BYTES + 36 * B_ROW < 65536, "stage offsets fit the LDS immediate");
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int grp = wave >> 2;   // reduction-step parity of this wave's group
+    const int lw = wave & 3;     // wave within the group
+
+    // ---- block -> (class, image, tile rectangle, group, channel slice) ----
+    const int bid = blockIdx.x;
+    int ci = 0;
+#pragma unroll 1
+    for (int i = 1; i < a.nclasses; ++i)
+        if (bid >= a.cls[i].tile_begin) ci = i;
+    const HaloClass cl = a.cls[ci];
+    int local = bid - cl.tile_begin;
+    if (a.remap) local = (local & 7) * (cl.nblocks >> 3) + (local >> 3);
+    const int ct = local % a.ctiles;
+    int rest = local / a.ctiles;
+    const int g = rest % a.G;
+    rest /= a.G;
+    const int bw = rest % cl.bands_w;
+    rest /= cl.bands_w;
+    const int bh = rest % cl.bands_h;
+    const int n = rest / cl.bands_h;
+    const int hc0 = bh * cl.th, wc0 = bw * cl.tw;
+    const int c0 = ct * BN;
+    const int s = a.stride;
+    const int nr = cl.nr, nt = cl.nt, hw = cl.hw, hp = cl.hp;
+
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
+
+    // ---- per-lane window sources: lane covers window pixel i*64 + lane ----
+    const int u_top = hc0 + cl.u_off - (nr - 1), v_left = wc0 + cl.v_off - (nt - 1);
+    const int hreal = (cl.th + nr - 1) * hw;
+    const int nq = hp >> 6;
+    uint32_t hoff[kMaxQ];
+#pragma unroll
+    for (int i = 0; i < kMaxQ; ++i) {
+        const int q = i * 64 + lane;
+        hoff[i] = kOob;
+        if (i < nq && q < hreal) {
+            const int hy = q / hw;
+            const int u = u_top + hy, v = v_left + q - hy * hw;
+            if (u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
+                hoff[i] = uint32_t((((n * a.Ho + u) * a.Wo + v) * a.K + g * a.Kg) * 2);
+        }
+    }
+    // window of chunk kc into buffer buf: wave w fills plane w
+    auto issue_window = [&](int buf, int kc) {
+        const int kk = kc * kBK;
+        const int pl = wave;
+        unsigned char* base = lds + buf * a.halo_bytes + pl * hp * 16;
+        const uint32_t soff = uint32_t((kk + pl * 8) * 2);
+        const bool kin = !KR || kk + pl * 8 < a.Kg;
+#pragma unroll
+        for (int i = 0; i < kMaxQ; ++i)
+            if (i < nq) dma16(rdy, base + i * 1024, kin ? hoff[i] : kOob, soff);
+    };
+
+    // ---- per-lane W sources: a group's 4 waves fill one stage ----
+    const int wk_stride = a.R * a.S * a.Cg;
+    uint32_t b_voff[B_REG];
+#pragma unroll
+    for (int i = 0; i < B_REG; ++i) {
+        const int krow = B_ROWS_PER_REG * (lw + 4 * i) + lane / B_CHUNKS;
+        const int chunk = (lane % B_CHUNKS) ^ swz_b<B_CHUNKS>(krow);
+        b_voff[i] = c0 + chunk * 8 < a.Cg ? uint32_t((krow * wk_stride + chunk * 8) * 2) : kOob;
+    }
+
+    const int taps = nr * nt;
+    const int kchunks = (a.Kg + kBK - 1) / kBK;
+    const int steps = taps * kchunks;
+    // With four or more taps, chunk 1 is first read after super-step 0, so its
+    // window is requested then rather than delaying the first multiply.
+    const bool defer1 = taps >= 4;
+    // ring stage of step st is st % 4; this group's steps use stages grp and
+    // grp + 2, so its ring base folds in grp and the rest is an immediate
+    unsigned char* const ring_g = lds + 2 * a.halo_bytes + grp * B_BYTES;
+
+    // W issue cursor of this group (uniform): tap (wi, wj), chunk offset wkk.
+    // Past the last step it keeps producing in-range or range-checked loads
+    // into stages that are never multiplied.
+    int wi = 0, wj = 0, wkk = 0;
+    auto advance_w = [&]() {
+        ++wj;
+        const bool w1 = wj >= nt;
+        wj = w1 ? 0 : wj;
+        wi += w1 ? 1 : 0;
+        const bool w2 = wi >= nr;
+        wi = w2 ? 0 : wi;
+        wkk += w2 ? kBK : 0;
+    };
+    auto dma_w = [&](auto stg, auto ec) {
+        constexpr int STG = decltype(stg)::value, E = decltype(ec)::value;
+        (void)b_voff;
+        const int rt = (cl.r0 + s * wi) * a.S + cl.t0 + s * wj;
+        const uint32_t soff = uint32_t(((g * a.Kg + wkk) * wk_stride + rt * a.Cg + c0) * 2);
+        uint32_t v = b_voff[E];
+        if (KR) {
+            const int krow = B_ROWS_PER_REG * (lw + 4 * E) + lane / B_CHUNKS;
+            v = (wkk + krow < a.Kg) ? v : kOob;
+        }
+        dma16(rw, ring_g + STG * B_BYTES + (lw + 4 * E) * 1024, v, soff);
+    };
+
+    // ---- fragment read addresses ----
+    const int wm = lw / WAVES_N, wn = lw % WAVES_N;
+    const int frow = lane & 15, fgrp = lane >> 4;
+    const uint32_t lds0 = lds_addr(lds);
+    // Half 1 of a step reads planes 4..7 (a uniform offset of 4 planes) and
+    // W k-rows 32..63; the second transpose read of a tile reads k-rows 4..7
+    // further on.  The W swizzle depends only on k-row bits 0, 1 and 3, which
+    // neither step changes, so both are immediate offsets.
+    uint32_t fa_base[WMB];           // window buffer 0, half 0, tap (0, 0)
+    uint32_t fb_addr[WNB];           // this group's first ring stage, half 0
+#pragma unroll
+    for (int i = 0; i < WMB; ++i) {
+        const int m = wm * (WMB * 16) + i * 16 + frow;
+        int q = (nr - 1) * hw + nt - 1;
+        if (m < cl.th * cl.tw) {
+            const int y = m / cl.tw;
+            q += y * hw + m - y * cl.tw;
+        }
+        fa_base[i] = lds0 + uint32_t((fgrp * hp + q) * 16);
+    }
+#pragma unroll
+    for (int j = 0; j < WNB; ++j) {
+        const int k = fgrp * 8 + (frow >> 2);
+        const int c = wn * (WNB * 16) + j * 16 + 4 * (frow & 3);
+        fb_addr[j] = lds_addr(ring_g) + k * B_ROW + (((c >> 3) ^ swz_b<B_CHUNKS>(k)) << 4) +
+                     (c & 7) * 2;
+    }
+    const int plane4 = 4 * hp * 16;
+
+    // read cursor of this group: tap (ri, rj) and chunk rkc of the own step
+    // whose first half is read next; offset = window buffer - tap shift
+    int ri = 0, rj = 0, rkc = 0;
+    auto cursor_off = [&]() {
+        return (rkc & 1) * int(a.halo_bytes) - (ri * hw + rj) * 16;
+    };
+    auto advance_r = [&]() {
+        ++rj;
+        const bool w1 = rj >= nt;
+        rj = w1 ? 0 : rj;
+        ri += w1 ? 1 : 0;
+        const bool w2 = ri >= nr;
+        ri = w2 ? 0 : ri;
+        rkc += w2 ? 1 : 0;
+    };
+
+    f32x4 acc[WMB][WNB];
+#pragma unroll
+    for (int i = 0; i < WMB; ++i)
+#pragma unroll
+        for (int j = 0; j < WNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    i32x4 fa[2][WMB];
+    i32x2 fb[2][WNB][2];
+    constexpr int NREAD = 2 * WNB + WMB;
+    auto read_one = [&](auto stg, auto ksc, auto rc, int aoff) {
+        constexpr int STG = decltype(stg)::value, KS = decltype(ksc)::value;
+        constexpr int R = decltype(rc)::value;
+        (void)fa; (void)fb; (void)fa_base; (void)fb_addr; (void)plane4;
+        if constexpr (R < 2 * WNB) {
+            asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                         : "=v"(fb[KS][R / 2][R % 2])
+                         : "v"(fb_addr[R / 2]),
+                           "i"(STG * B_BYTES + KS * 32 * B_ROW + (R % 2) * 4 * B_ROW));
+        } else {
+            asm volatile("ds_read_b128 %0, %1"
+                         : "=v"(fa[KS][R - 2 * WNB])
+                         : "v"(fa_base[R - 2 * WNB] + uint32_t(aoff + KS * plane4)));
+        }
+    };
+    auto wait_frags = [&](auto ksc) {
+        constexpr int KS = decltype(ksc)::value;
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[KS][0]), "+v"(fb[KS][0][0]));
+#pragma unroll
+        for (int i = 1; i < WMB; ++i) asm volatile("" : "+v"(fa[KS][i]));
+#pragma unroll
+        for (int j = 0; j < WNB; ++j) asm volatile("" : "+v"(fb[KS][j][0]), "+v"(fb[KS][j][1]));
+    };
+    auto mfma_one = [&](auto ksc, auto mc) {
+        constexpr int KS = decltype(ksc)::value, M = decltype(mc)::value;
+        constexpr int i = M / WNB, j = M % WNB;
+        const i32x4 b = {fb[KS][j][0][0], fb[KS][j][0][1], fb[KS][j][1][0], fb[KS][j][1][1]};
+        acc[i][j] = mfma16x16x32<T>(b, fa[KS][i], acc[i][j]);
+    };
+
+    constexpr int NM = WMB * WNB;
+    constexpr int PER0 = (NREAD + NM - 1) / NM;
+    constexpr int NI1 = NREAD + B_REG;
+    constexpr int PER1 = (NI1 + NM - 1) / NM;
+    int off_cur = 0, off_next = 0;   // window offsets of this group's current and next step
+    int end_step = taps - 1;         // last step of chunk end_chunk (block-uniform)
+    int end_chunk = 0;
+    // Super-step j: group g multiplies its step 2j + g.  First half: multiply
+    // half 0 while reading half 1's fragments.  All waves then wait for their
+    // own loads and meet at the barrier, after which every fragment of steps
+    // <= 2j+1 has been read and every load issued before it has landed.
+    // Second half: multiply half 1 while reading half 0 of the group's next
+    // step and loading W of its step after that into the stage just freed.
+    // A chunk whose last step was in this super-step frees its window buffer
+    // for the chunk after next.
+    auto super_fn = [&](auto jc, int j) {
+        constexpr int J = decltype(jc)::value;
+        constexpr int STG = 2 * J, NXT = 2 * (1 - J);
+        const bool active = 2 * j + grp < steps;
+        if (active) {
+            sfor<NM>([&](auto mc) {
+                constexpr int M = decltype(mc)::value;
+                mfma_one(IC<0>{}, mc);
+                sfor<PER0>([&](auto pc) {
+                    constexpr int X = M * PER0 + decltype(pc)::value;
+                    if constexpr (X < NREAD) read_one(IC<STG>{}, IC<1>{}, IC<X>{}, off_cur);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        wait_frags(IC<1>{});
+        wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        if (active) {
+            sfor<NM>([&](auto mc) {
+                constexpr int M = decltype(mc)::value;
+                mfma_one(IC<1>{}, mc);
+                sfor<PER1>([&](auto pc) {
+                    // loads first: they have until the next barrier but one to land
+                    constexpr int X = M * PER1 + decltype(pc)::value;
+                    if constexpr (X < B_REG) dma_w(IC<STG>{}, IC<X>{});
+                    else if constexpr (X < NI1) read_one(IC<NXT>{}, IC<0>{}, IC<X - B_REG>{}, off_next);
+                });
+                __builtin_amdgcn_sched_barrier(0);
+            });
+        }
+        if (defer1 && j == 0) issue_window(1, 1);
+        if (end_step <= 2 * j + 1) {
+            issue_window(end_chunk & 1, end_chunk + 2);
+            ++end_chunk;
+            end_step += taps;
+        }
+        wait_frags(IC<0>{});
+        off_cur = off_next;
+        advance_r();
+        advance_r();
+        off_next = cursor_off();
+        advance_w();
+        advance_w();
+    };
+
+    if (steps > 0) {
+        issue_window(0, 0);
+        if (grp) advance_w();
+        sfor<B_REG>([&](auto ec) { dma_w(IC<0>{}, ec); });
+        advance_w();
+        advance_w();
+        if (!defer1) issue_window(1, 1);
+        sfor<B_REG>([&](auto ec) { dma_w(IC<2>{}, ec); });
+        advance_w();
+        advance_w();
+        wait_vm<B_REG>();   // the group's second stage may still be in flight
+        __builtin_amdgcn_s_barrier();
+        if (grp) advance_r();
+        off_cur = cursor_off();
+        advance_r();
+        advance_r();
+        off_next = cursor_off();
+        sfor<NREAD>([&](auto rc) { read_one(IC<0>{}, IC<0>{}, rc, off_cur); });
+        wait_frags(IC<0>{});
+        const int supers = (steps + 1) / 2;
+#pragma unroll 1
+        for (int j = 0; j < supers; j += 2) {
+            super_fn(IC<0>{}, j);
+            if (j + 1 < supers) super_fn(IC<1>{}, j + 1);
+        }
+        wait_vm<0>();
+        __builtin_amdgcn_s_barrier();
+    }
+
+    // ---- add the odd-step partials into the even-step group's ----
+    constexpr int NT = WMB * WNB;
+    f32x4* part = reinterpret_cast<f32x4*>(lds) + lw * NT * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+        for (int i = 0; i < WMB; ++i)
+#pragma unroll
+            for (int j = 0; j < WNB; ++j) part[(i * WNB + j) * 64] = acc[i][j];
+    }
+    __syncthreads();
+    if (grp == 0) {
+#pragma unroll
+        for (int i = 0; i < WMB; ++i)
+#pragma unroll
+            for (int j = 0; j < WNB; ++j) acc[i][j] += part[(i * WNB + j) * 64];
+    }
+    __syncthreads();
+
+    // ---- epilogue: round, stage the tile in LDS, 16-byte row stores ----
+    if (grp == 0) {
+#pragma unroll
+        for (int i = 0; i < WMB; ++i)
+#pragma unroll
+            for (int j = 0; j < WNB; ++j) {
+                const int row = wm * (WMB * 16) + i * 16 + frow;
+                const int col = wn * (WNB * 16) + j * 16 + fgrp * 4;
+                i32x2 v = {int(pack2<T>(acc[i][j][0], acc[i][j][1])),
+                           int(pack2<T>(acc[i][j][2], acc[i][j][3]))};
+                *reinterpret_cast<i32x2*>(lds + row * C_STRIDE + col * 2) = v;
+            }
+    }
+    __syncthreads();
+    constexpr int CPR = BN / 8;
+    const int tpix = cl.th * cl.tw;
+    for (int q = tid; q < BMC * CPR; q += kHaloThreads) {
+        const int row = q / CPR, cc = q % CPR;
+        const int c = c0 + cc * 8;
+        if (row >= tpix || c >= a.Cg) continue;
+        const int y = row / cl.tw;
+        const int hc = hc0 + y, wc = wc0 + row - y * cl.tw;
+        if (hc >= cl.hc || wc >= cl.wc) continue;
+        const int pix = (n * a.H + cl.a + s * hc) * a.W + cl.b + s * wc;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(lds + row * C_STRIDE + cc * 16);
+        buf_store16(v, rdx, uint32_t(pix * a.C + g * a.Cg + c) * 2u);
+    }
+}
+
 // Tile shapes (M blocks per wave, N blocks per wave) on 2 x 2 waves:
 //   0: 224-pixel capacity x 128 channels (deep channel counts)
 //   1: 128 x 64 (narrow channel counts)
-template <typename T, bool PW>
+template <typename T, bool PW, bool KR>
 void launch_cfg(int cfg, const IgemmArgs& args, int blocks, hipStream_t st) {
     if (cfg == 0)
-        hipLaunchKernelGGL((dgrad_igemm_kernel<T, 7, 4, PW>), dim3(blocks), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((dgrad_igemm_kernel<T, 7, 4, PW, KR>), dim3(blocks), dim3(kThreads), 0, st, args);
     else
-        hipLaunchKernelGGL((dgrad_igemm_kernel<T, 4, 2, PW>), dim3(blocks), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((dgrad_igemm_kernel<T, 4, 2, PW, KR>), dim3(blocks), dim3(kThreads), 0, st, args);
+}
+template <typename T, bool PW>
+void launch_kr(int cfg, bool kr, const IgemmArgs& args, int blocks, hipStream_t st) {
+    if (kr) launch_cfg<T, PW, true>(cfg, args, blocks, st);
+    else launch_cfg<T, PW, false>(cfg, args, blocks, st);
 }
 
 struct Cfg {
@@ -426,14 +865,165 @@ std::string dgrad_igemm_reason(const Prob& p, bool pointwise) {
     if (p.cg % 8 != 0) return "channels per group of dx must be a multiple of 8";
     if (p.kg % 8 != 0) return "channels per group of dy must be a multiple of 8";
     if (p.stride > 4) return "implicit-GEMM dgrad supports stride <= 4 (at most 16 phase classes)";
+    {
+        // the dY window of a one-pixel tile must fit the LDS window buffer
+        const int64_t nr = (p.r + p.stride - 1) / p.stride, nt = (p.s + p.stride - 1) / p.stride;
+        if (nr * nt > 384)
+            return "implicit-GEMM dgrad needs ceil(R/stride)*ceil(S/stride) <= 384 (LDS window)";
+    }
     if (p.ho * p.wo * p.k > (int64_t(1) << 30) || p.h * p.w * p.c > (int64_t(1) << 30))
         return "one image exceeds the 32-bit element range";
     return "";
 }
 
+namespace {
+
+template <typename T, int WMB, int WNB, bool KR>
+void launch_halo_inst(const HaloArgs& a, int blocks, size_t lds, hipStream_t st) {
+    auto kern = dgrad_halo_kernel<T, WMB, WNB, KR>;
+    static bool attr_set = false;   // the attribute is per kernel; idempotent if raced
+    if (!attr_set) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kLdsMax);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(kHaloThreads), lds, st, a);
+}
+
+template <typename T>
+void launch_halo_t(int cfg, bool kr, const HaloArgs& a, int blocks, size_t lds, hipStream_t st) {
+    if (cfg == 0) {
+        if (kr) launch_halo_inst<T, 7, 4, true>(a, blocks, lds, st);
+        else launch_halo_inst<T, 7, 4, false>(a, blocks, lds, st);
+    } else {
+        if (kr) launch_halo_inst<T, 4, 2, true>(a, blocks, lds, st);
+        else launch_halo_inst<T, 4, 2, false>(a, blocks, lds, st);
+    }
+}
+
+// Window plane entries one buffer may hold: two buffers and the W ring share
+// the LDS, and a lane covers at most kMaxQ window pixels.
+int halo_hp_max(int bn) {
+    return std::min(kMaxQ * 64, (kLdsMax - kRing * kBK * bn * 2) / (2 * 8 * 16) / 64 * 64);
+}
+
+// Tile rectangle of a class under a row cap: the widest column band (up to
+// the whole class row) and then the most rows whose dY window fits a buffer.
+bool halo_geometry(int hc, int wc, int nr, int nt, int bmc, int th_cap, int hp_max, int& th,
+                   int& tw, int& hp) {
+    nr = std::max(nr, 1);
+    nt = std::max(nt, 1);
+    for (tw = std::min(wc, bmc); tw >= 1; tw = tw > 8 ? tw - 8 : tw - 1) {
+        for (th = std::min(std::min(hc, bmc / tw), th_cap); th >= 1; --th) {
+            const int hreal = (th + nr - 1) * (tw + nt - 1);
+            hp = (hreal + 63) / 64 * 64;
+            if (hp <= hp_max) return true;
+        }
+    }
+    return false;
+}
+
+// Launch the window kernel over the phase classes with at least two taps.
+int launch_dgrad_halo(const Prob& p, const void* dy, const void* w, void* dx, hipStream_t st) {
+    const int cfg = p.cg > 64 ? 0 : 1;
+    const int BN = kCfgs[cfg].bn, BMC = kCfgs[cfg].bmc;
+    const int hp_max = halo_hp_max(BN);
+    HaloArgs a{};
+    a.dy = dy; a.w = w; a.dx = dx;
+    a.dy_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
+    a.w_bytes = uint32_t(p.k * p.r * p.s * p.cg * 2);
+    a.dx_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
+    a.N = int(p.n); a.H = int(p.h); a.W = int(p.w); a.C = int(p.c); a.K = int(p.k);
+    a.R = int(p.r); a.S = int(p.s); a.stride = p.stride;
+    a.Ho = int(p.ho); a.Wo = int(p.wo); a.Cg = int(p.cg); a.Kg = int(p.kg); a.G = p.groups;
+    a.ctiles = int((p.cg + BN - 1) / BN);
+    const int s = p.stride;
+    const int kchunks = int((p.kg + kBK - 1) / kBK);
+    // phase classes, heaviest reduction first so long tiles start early
+    HaloClass tmp[kMaxClasses];
+    int nc = 0;
+    for (int ca = 0; ca < s; ++ca)
+        for (int cb = 0; cb < s; ++cb) {
+            HaloClass c{};
+            c.a = ca; c.b = cb;
+            c.hc = int((p.h - ca + s - 1) / s);
+            c.wc = int((p.w - cb + s - 1) / s);
+            if (c.hc <= 0 || c.wc <= 0) continue;
+            c.r0 = (ca + p.pad_h) % s;
+            c.t0 = (cb + p.pad_w) % s;
+            c.nr = c.r0 < p.r ? int((p.r - c.r0 + s - 1) / s) : 0;
+            c.nt = c.t0 < p.s ? int((p.s - c.t0 + s - 1) / s) : 0;
+            c.u_off = (ca + p.pad_h - c.r0) / s;
+            c.v_off = (cb + p.pad_w - c.t0) / s;
+            if (c.nr * c.nt >= 2) tmp[nc++] = c;
+        }
+    std::stable_sort(tmp, tmp + nc, [](const HaloClass& x, const HaloClass& y) {
+        return x.nr * x.nt > y.nr * y.nt;
+    });
+    // Row cap: a block's time is set by its reduction (the tile capacity is
+    // multiplied whatever its fill), so minimise the rounds of blocks over the
+    // CUs, weighted by each class's steps; ties go to taller tiles.
+    const int64_t slots = kNumCUs;
+    int best_cap = BMC;
+    int64_t best_cost = INT64_MAX;
+    for (int cap = BMC; cap >= 1; --cap) {
+        int64_t cost = 0;
+        for (int i = 0; i < nc; ++i) {
+            int th, tw, hp;
+            if (!halo_geometry(tmp[i].hc, tmp[i].wc, tmp[i].nr, tmp[i].nt, BMC, cap, hp_max, th,
+                               tw, hp))
+                return CNHWC_UNSUPPORTED;
+            const int64_t blocks = p.n * ((tmp[i].hc + th - 1) / th) * ((tmp[i].wc + tw - 1) / tw) *
+                                   a.ctiles * a.G;
+            cost += (blocks + slots - 1) / slots * std::max(1, tmp[i].nr * tmp[i].nt * kchunks);
+        }
+        if (cost < best_cost) { best_cost = cost; best_cap = cap; }
+    }
+    int total = 0;
+    bool all8 = true;
+    uint32_t halo_bytes = 0;
+    for (int i = 0; i < nc; ++i) {
+        HaloClass& c = tmp[i];
+        halo_geometry(c.hc, c.wc, c.nr, c.nt, BMC, best_cap, hp_max, c.th, c.tw, c.hp);
+        c.bands_h = (c.hc + c.th - 1) / c.th;
+        c.bands_w = (c.wc + c.tw - 1) / c.tw;
+        c.hw = c.tw + std::max(c.nt, 1) - 1;
+        c.tile_begin = total;
+        c.nblocks = int(p.n) * c.bands_h * c.bands_w * a.ctiles * a.G;
+        if (c.nblocks % 8 != 0) all8 = false;
+        total += c.nblocks;
+        halo_bytes = std::max(halo_bytes, uint32_t(8 * c.hp * 16));
+        a.cls[i] = c;
+    }
+    a.nclasses = nc;
+    a.remap = all8 ? 1 : 0;
+    a.halo_bytes = halo_bytes;
+    if (total <= 0) return CNHWC_OK;
+    const size_t ring = size_t(kRing) * kBK * BN * 2;
+    const size_t epi = size_t(BMC) * (BN * 2 + 16);
+    const size_t partials = size_t(BMC) * BN * 4;   // odd-step fp32 partial sums
+    const size_t lds = std::max(std::max(2 * size_t(halo_bytes) + ring, epi), partials);
+    const bool kr = p.kg % kBK != 0;
+    if (p.dtype == CNHWC_BF16) launch_halo_t<BF16>(cfg, kr, a, total, lds, st);
+    else launch_halo_t<F16>(cfg, kr, a, total, lds, st);
+    return CNHWC_OK;
+}
+
+}  // namespace
+
 int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
                        hipStream_t st) {
     const bool pw = pl.variant == CNHWC_VAR_DGRAD_POINTWISE;
+    // Stride 1: classes with two or more taps go to the window kernel, the
+    // rest (and the pointwise fast path) to the ring kernel below.  Strided
+    // problems split into several classes of few taps each, where the window
+    // kernel's fixed cost per block outweighs its dY reuse: ring kernel only.
+    // (tune: 1 forces the ring kernel, 2 the window kernel.)
+    const bool window = !pw && (pl.tune == 2 || (pl.tune != 1 && p.stride == 1));
+    if (window) {
+        const int rc = launch_dgrad_halo(p, dy, w, dx, st);
+        if (rc != CNHWC_OK) return rc;
+    }
     const int cfg = p.cg > 64 ? 0 : 1;
     const int BN = kCfgs[cfg].bn, BMC = kCfgs[cfg].bmc;
     IgemmArgs a{};
@@ -461,7 +1051,8 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
             ci.t0 = (cb + p.pad_w) % s;
             ci.nr = ci.r0 < p.r ? int((p.r - ci.r0 + s - 1) / s) : 0;
             ci.nt = ci.t0 < p.s ? int((p.s - ci.t0 + s - 1) / s) : 0;
-            tmp[nc++] = C{ci, int64_t(ci.nr) * ci.nt, p.n * ci.hc * ci.wc};
+            if (!window || ci.nr * ci.nt <= 1)
+                tmp[nc++] = C{ci, int64_t(ci.nr) * ci.nt, p.n * ci.hc * ci.wc};
         }
     std::stable_sort(tmp, tmp + nc, [](const C& x, const C& y) { return x.work > y.work; });
     // M tile.  A block's time grows with its capacity when the reduction is
@@ -496,8 +1087,9 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
     a.remap = all8 ? 1 : 0;
     if (total <= 0) return CNHWC_OK;
     const bool bf = p.dtype == CNHWC_BF16;
-    if (pw) bf ? launch_cfg<BF16, true>(cfg, a, total, st) : launch_cfg<F16, true>(cfg, a, total, st);
-    else bf ? launch_cfg<BF16, false>(cfg, a, total, st) : launch_cfg<F16, false>(cfg, a, total, st);
+    const bool kr = p.kg % kBK != 0;
+    if (pw) bf ? launch_kr<BF16, true>(cfg, kr, a, total, st) : launch_kr<F16, true>(cfg, kr, a, total, st);
+    else bf ? launch_kr<BF16, false>(cfg, kr, a, total, st) : launch_kr<F16, false>(cfg, kr, a, total, st);
     return CNHWC_OK;
 }
 

@@ -60,6 +60,15 @@ def test_igemm_parity(p):
     parity(p, "dgrad", 102)
 
 
+@pytest.mark.parametrize("tune", [1, 2], ids=["ring", "window"])
+@pytest.mark.parametrize("p", IGEMM, ids=ident)
+def test_igemm_parity_both_kernels(p, tune):
+    """Both implicit-GEMM dgrad kernels (every class on the ring kernel; or
+    classes with two or more taps on the dY-window kernel) on every shape."""
+    with api.override(tune=tune):
+        parity(p, "dgrad", 108)
+
+
 @pytest.mark.parametrize("p", [P(1, 12, 12, 64, 64, 3, 3, 2, 1, 1), P(2, 8, 8, 32, 32, 1, 1),
                                P(1, 10, 10, 32, 64, 3, 3, 1, 1, 1, dtype="bf16")], ids=ident)
 def test_exact_small_integers_bitwise(p):
