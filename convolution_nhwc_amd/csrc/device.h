@@ -6,6 +6,8 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <type_traits>
+#include <utility>
 
 namespace cnhwc {
 
@@ -48,17 +50,21 @@ __device__ inline int buf_load4(__amdgpu_buffer_rsrc_t r, uint32_t off) {
 __device__ inline unsigned short buf_load2(__amdgpu_buffer_rsrc_t r, uint32_t off) {
     return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
 }
+// Stores carry the non-temporal (streaming) cache policy: every kernel writes
+// its outputs once and never reads them back, and streaming lines do not
+// linger dirty in the XCD's L2 for the write-back at the end of the kernel.
+constexpr int kStoreNT = 2;
 __device__ inline void buf_store16(i32x4 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b128(v, r, off, 0, kStoreNT);
 }
 __device__ inline void buf_store8(i32x2 v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b64(v, r, off, 0, kStoreNT);
 }
 __device__ inline void buf_store4(int v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b32(v, r, off, 0, kStoreNT);
 }
 __device__ inline void buf_store2(unsigned short v, __amdgpu_buffer_rsrc_t r, uint32_t off) {
-    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, 0);
+    __builtin_amdgcn_raw_buffer_store_b16(v, r, off, 0, kStoreNT);
 }
 
 // D += A(16x32) * B(32x16) on the matrix cores.  Lane l supplies row l%16 of A
@@ -127,6 +133,59 @@ __device__ inline uint32_t pair_lo(uint32_t a, uint32_t b) {
 }
 __device__ inline uint32_t pair_hi(uint32_t a, uint32_t b) {
     return __builtin_amdgcn_perm(b, a, 0x07060302u);
+}
+
+// ---- asynchronous loads into LDS, waits, compile-time loops ----------------
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+// Asynchronous 16-byte global -> LDS load: lane l writes lds_base + 16*l
+// (lds_base must be wave-uniform: it goes to M0).
+__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base, uint32_t voff,
+                             uint32_t soff) {
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
+}
+
+// s_waitcnt vmcnt(n) (lgkmcnt and expcnt left alone).
+template <int N>
+__device__ inline void wait_vm() {
+    static_assert(N >= 0 && N < 64, "vmcnt");
+    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// LDS byte address (what ds_* instructions take) of a pointer into __shared__.
+__device__ inline uint32_t lds_addr(const void* p) {
+    return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
+}
+
+// Division by a launch-time constant d >= 1 as a multiply and a shift
+// (round-up reciprocal, the "add" form): exact for every dividend below 2^31.
+// The kernels use it for per-lane index arithmetic, where an integer divide
+// would cost tens of VALU instructions.
+struct FastDiv {
+    uint32_t mul, shift;
+};
+inline FastDiv make_fastdiv(uint32_t d) {
+    uint32_t l = 0;
+    while ((uint64_t(1) << l) < d) ++l;
+    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
+    return FastDiv{uint32_t(m), l};
+}
+__device__ inline int fdiv(int q, FastDiv f) {
+    return int((__umulhi(uint32_t(q), f.mul) + uint32_t(q)) >> f.shift);
+}
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+// Compile-time loop: f(IC<0>{}), ..., f(IC<N-1>{}).
+template <typename F, int... I>
+__device__ inline void sfor_impl(F&& f, std::integer_sequence<int, I...>) {
+    (f(IC<I>{}), ...);
+}
+template <int N, typename F>
+__device__ inline void sfor(F&& f) {
+    sfor_impl(f, std::make_integer_sequence<int, N>{});
 }
 
 }  // namespace cnhwc

@@ -78,20 +78,7 @@ struct IgemmArgs {
     ClassInfo cls[kMaxClasses];
 };
 
-typedef __attribute__((address_space(3))) void lds_void;
 
-// Asynchronous 16-byte global -> LDS load: lane l writes lds_base + 16*l.
-__device__ inline void dma16(__amdgpu_buffer_rsrc_t r, unsigned char* lds_base, uint32_t voff,
-                             uint32_t soff) {
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (lds_void*)lds_base, 16, voff, soff, 0, 0);
-}
-
-// s_waitcnt vmcnt(n) (lgkmcnt and expcnt left alone).
-template <int N>
-__device__ inline void wait_vm() {
-    static_assert(N >= 0 && N < 64, "vmcnt");
-    __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
-}
 
 // Chunk swizzles.  dY rows (128 B): 16-byte chunk ^ f(row) so that the 16
 // rows one fragment read touches hit distinct bank groups.  W rows: the
@@ -105,23 +92,6 @@ __device__ inline int swz_b(int k) {
     else return 2 * (((k >> 1) & 1) | ((k >> 2) & 2));
 }
 
-// LDS byte address (what ds_* instructions take) of a pointer into __shared__.
-__device__ inline uint32_t lds_addr(const void* p) {
-    return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
-}
-
-template <int I>
-using IC = std::integral_constant<int, I>;
-
-// Compile-time loop: f(IC<0>{}), ..., f(IC<N-1>{}).
-template <typename F, int... I>
-__device__ inline void sfor_impl(F&& f, std::integer_sequence<int, I...>) {
-    (f(IC<I>{}), ...);
-}
-template <int N, typename F>
-__device__ inline void sfor(F&& f) {
-    sfor_impl(f, std::make_integer_sequence<int, N>{});
-}
 
 template <typename T, int WMB, int WNB, bool PW, bool KR>
 __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArgs a) {
@@ -474,6 +444,7 @@ struct HaloClass {
     int hp;              // window plane entries (a multiple of 64)
     int tile_begin;      // first block of the class
     int nblocks;         // blocks of the class
+    FastDiv fd_hw, fd_tw;  // division by hw and by tw
 };
 
 struct HaloArgs {
@@ -546,7 +517,7 @@ __global__ __launch_bounds__(kHaloThreads, 1) void dgrad_halo_kernel(const HaloA
         const int q = i * 64 + lane;
         hoff[i] = kOob;
         if (i < nq && q < hreal) {
-            const int hy = q / hw;
+            const int hy = fdiv(q, cl.fd_hw);
             const int u = u_top + hy, v = v_left + q - hy * hw;
             if (u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
                 hoff[i] = uint32_t((((n * a.Ho + u) * a.Wo + v) * a.K + g * a.Kg) * 2);
@@ -625,7 +596,7 @@ __global__ __launch_bounds__(kHaloThreads, 1) void dgrad_halo_kernel(const HaloA
         const int m = wm * (WMB * 16) + i * 16 + frow;
         int q = (nr - 1) * hw + nt - 1;
         if (m < cl.th * cl.tw) {
-            const int y = m / cl.tw;
+            const int y = fdiv(m, cl.fd_tw);
             q += y * hw + m - y * cl.tw;
         }
         fa_base[i] = lds0 + uint32_t((fgrp * hp + q) * 16);
@@ -823,7 +794,7 @@ __global__ __launch_bounds__(kHaloThreads, 1) void dgrad_halo_kernel(const HaloA
         const int row = q / CPR, cc = q % CPR;
         const int c = c0 + cc * 8;
         if (row >= tpix || c >= a.Cg) continue;
-        const int y = row / cl.tw;
+        const int y = fdiv(row, cl.fd_tw);
         const int hc = hc0 + y, wc = wc0 + row - y * cl.tw;
         if (hc >= cl.hc || wc >= cl.wc) continue;
         const int pix = (n * a.H + cl.a + s * hc) * a.W + cl.b + s * wc;
@@ -988,6 +959,8 @@ int launch_dgrad_halo(const Prob& p, const void* dy, const void* w, void* dx, hi
         c.bands_h = (c.hc + c.th - 1) / c.th;
         c.bands_w = (c.wc + c.tw - 1) / c.tw;
         c.hw = c.tw + std::max(c.nt, 1) - 1;
+        c.fd_hw = make_fastdiv(uint32_t(c.hw));
+        c.fd_tw = make_fastdiv(uint32_t(c.tw));
         c.tile_begin = total;
         c.nblocks = int(p.n) * c.bands_h * c.bands_w * a.ctiles * a.G;
         if (c.nblocks % 8 != 0) all8 = false;

@@ -326,7 +326,7 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
             s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
         }
         i32x2 o = {int(pack2<T>(s[0], s[1])), int(pack2<T>(s[2], s[3]))};
-        reinterpret_cast<i32x2*>(y)[i] = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<i32x2*>(y) + i);
     }
 }
 
@@ -547,6 +547,7 @@ bool grouped_shape(const Prob& p, int* gm, int* bn) {
 int fwd_direct_channel_chunk() { return kBKc; }
 
 std::string fwd_direct_reason(const Prob& p, int split_c) {
+    if (fwd_window_reason(p, split_c).empty()) return "";
     if (p.cg % 8 != 0) return "input channels per group must be a multiple of 8";
     if (p.kg % 8 != 0) return "output channels per group must be a multiple of 8";
     if (p.h * p.w * p.c > (int64_t(1) << 30) || p.ho * p.wo * p.k > (int64_t(1) << 30))
@@ -587,6 +588,7 @@ int64_t fwd_direct_tiles(const Prob& p) {
 // count within the CU count and at least 128 channels per split.
 int fwd_direct_auto_split(const Prob& p) {
     if (p.groups != 1) return 1;
+    if (fwd_window_reason(p, 1).empty()) return fwd_window_auto_split(p);
     const int64_t tiles = fwd_direct_tiles(p);
     if (tiles <= 0 || tiles >= kNumCUs / 2) return 1;
     // two blocks fit a CU (LDS), so aim for up to 2 * CUs blocks
@@ -599,8 +601,28 @@ int fwd_direct_auto_split(const Prob& p) {
     return best;
 }
 
+int launch_split_reduce(const Prob& p, int splits, const void* ws, void* y, hipStream_t st) {
+    const int64_t total4 = p.n * p.ho * p.wo * p.k / 4;
+    const int64_t grid = std::min<int64_t>((total4 + 255) / 256, int64_t(kNumCUs) * 8);
+    if (p.dtype == CNHWC_BF16)
+        hipLaunchKernelGGL(split_reduce_kernel<BF16>, dim3(grid), dim3(256), 0, st,
+                           static_cast<const float*>(ws), static_cast<unsigned short*>(y), total4,
+                           total4, splits);
+    else
+        hipLaunchKernelGGL(split_reduce_kernel<F16>, dim3(grid), dim3(256), 0, st,
+                           static_cast<const float*>(ws), static_cast<unsigned short*>(y), total4,
+                           total4, splits);
+    return CNHWC_OK;
+}
+
+// Direct forward (split or not): the window kernel when it accepts the
+// problem, else the register-staged kernel above.  (tune: 1 forces the
+// register-staged kernel, 2 the window kernel.)
 int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                       void* ws, hipStream_t st) {
+    if (pl.tune != 1 && fwd_window_reason(p, pl.split_c).empty())
+        return launch_fwd_window(p, pl, x, w, y, ws, st);
+    if (pl.tune == 2) return CNHWC_UNSUPPORTED;
     FwdArgs a{};
     const bool split = pl.variant == CNHWC_VAR_FWD_SPLITC && pl.split_c > 1;
     if (!pick_geo(p, kHaloMax, &a.geo)) return CNHWC_UNSUPPORTED;

@@ -49,6 +49,10 @@ int launch_dgrad_generic(const Prob& p, const Plan& pl, const void* dy, const vo
                          hipStream_t st);
 int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                       void* ws, hipStream_t st);
+int launch_fwd_window(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
+                      void* ws, hipStream_t st);
+// Second pass of split-C: y = round(sum over splits of ws[split]), ascending.
+int launch_split_reduce(const Prob& p, int splits, const void* ws, void* y, hipStream_t st);
 int launch_fwd_grouped(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                        hipStream_t st);
 int launch_fwd_generic(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
@@ -60,6 +64,8 @@ std::string dw_stream_reason(const Prob& p, int cpl);
 std::string dw_rotated_reason(const Prob& p);
 std::string fwd_direct_reason(const Prob& p, int split_c);
 std::string fwd_grouped_reason(const Prob& p);
+std::string fwd_window_reason(const Prob& p, int split_c);
+int fwd_window_auto_split(const Prob& p);
 
 // Depthwise row-streaming: the largest channels-per-lane the kernel set has an
 // instance for at this filter/stride (0 if none).

@@ -34,9 +34,14 @@ DIRECT = [
 ]
 
 
+# tune 1: the register-staged direct kernel; 2: the pipelined input-window kernel
+KERNELS = pytest.mark.parametrize("tune", [1, 2], ids=["staged", "window"])
+
+
+@KERNELS
 @pytest.mark.parametrize("p", DIRECT, ids=ident)
-def test_direct_parity(p):
-    with api.override(variant=api.VAR_FWD_DIRECT):
+def test_direct_parity(p, tune):
+    with api.override(variant=api.VAR_FWD_DIRECT, tune=tune):
         parity(p, "fwd", 201)
 
 
@@ -48,9 +53,10 @@ SPLIT = [
 ]
 
 
+@KERNELS
 @pytest.mark.parametrize("p,split", SPLIT, ids=[ident(p) + "x%d" % s for p, s in SPLIT])
-def test_split_c_parity(p, split):
-    with api.override(variant=api.VAR_FWD_SPLITC, split_c=split):
+def test_split_c_parity(p, split, tune):
+    with api.override(variant=api.VAR_FWD_SPLITC, split_c=split, tune=tune):
         assert "splitc%d" % split in api.cnhwc_plan(p, api.OP_FWD)[0]
         parity(p, "fwd", 202)
 
