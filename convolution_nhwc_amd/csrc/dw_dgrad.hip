@@ -27,6 +27,7 @@
 #include "device.h"
 #include "internal.h"
 
+#include <algorithm>
 #include <string>
 
 namespace cnhwc {
@@ -247,6 +248,187 @@ bool dispatch_stream(const StreamCfg& c, const StreamArgs& a, hipStream_t st) {
     return false;
 }
 
+// ============================ LDS-tiled (small filters) =====================
+//
+// Stride-1 depthwise dgrad for R x S <= 7 x 7 with the dY window of a tile
+// staged in LDS.  A block owns 8 x 28 dX pixels x 64 channels: the window (one
+// guard row above, R-1 rows and S-1 columns of halo) is loaded with 16-byte
+// asynchronous loads straight into LDS, 128 bytes per pixel, and the block's
+// weights go to LDS as row pairs.  Each lane then owns 4 x 7 pixels x 2
+// channels: it walks the window rows once, makes the vertical pairs
+// (dY[u][v], dY[u-1][v]) of its two channels with one byte permute each, and
+// feeds every pair to all the outputs and taps that use it
+// (dX[h][w] += pair . (W[r][t], W[r+1][t]) with u = h + R - r, v = w + S-1-t in
+// window coordinates) -- all indices compile-time, so the inner loop is a
+// straight line of dot2 instructions.
+constexpr int kTileTWL = 7;                  // lane tile columns
+constexpr int kTilePBH = 2, kTilePBW = 4;    // lane tiles per block tile
+constexpr int kTileTW = kTileTWL * kTilePBW; // 28
+constexpr int kTileCB = 64;                  // channels per block
+// lane tile rows: 4, or 2 for 7x7 (its 7 x 4 weight pairs and accumulators
+// must stay in registers)
+constexpr int tile_thl(int r) { return r >= 7 ? 2 : 4; }
+constexpr int tile_th(int r) { return tile_thl(r) * kTilePBH; }
+
+struct TileArgs {
+    const void* dy;
+    const void* w;
+    void* dx;
+    uint32_t dy_bytes, w_bytes, dx_bytes;
+    int N, H, W, C, Ho, Wo, pad_h, pad_w;
+    int tiles_h, tiles_w, cblocks;
+};
+
+template <int R, int S>
+struct TileGeo {
+    static constexpr int NL = (R + 1) / 2;                    // filter row pairs
+    static constexpr int THL = tile_thl(R);
+    static constexpr int TH = THL * kTilePBH;
+    static constexpr int WR = TH + R;                         // window rows (guard row first)
+    static constexpr int WC = kTileTW + S - 1;                // window columns
+    static constexpr int NPIX = WR * WC;
+    static constexpr int WIN_BYTES = (NPIX + 7) / 8 * 1024;   // whole 8-pixel loads
+    static constexpr int RAW_BYTES = (kTileCB * R * S * 2 + 1023) / 1024 * 1024;
+    static constexpr int WTS = NL * S * kTileCB;              // weight pair words
+    static constexpr int LDS = WIN_BYTES + RAW_BYTES + WTS * 4;
+};
+
+template <typename T, int R, int S>
+__global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
+    using G = TileGeo<R, S>;
+    constexpr int NL = G::NL, WC = G::WC, NPIX = G::NPIX;
+    constexpr int kTileTHL = G::THL, kTileTH = G::TH;
+    constexpr int LOADS = (NPIX + 31) / 32;                   // 8-pixel loads per wave
+    constexpr int RV = kTileTWL + S - 1;                      // window columns a lane reads
+    __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
+    const unsigned short* const raw = reinterpret_cast<const unsigned short*>(lds + G::WIN_BYTES);
+    uint32_t* const wts = reinterpret_cast<uint32_t*>(lds + G::WIN_BYTES + G::RAW_BYTES);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    int bid = blockIdx.x;
+    const int cb = bid % a.cblocks;
+    bid /= a.cblocks;
+    const int tw_i = bid % a.tiles_w;
+    bid /= a.tiles_w;
+    const int th_i = bid % a.tiles_h;
+    const int n = bid / a.tiles_h;
+    const int h0 = th_i * kTileTH, w0 = tw_i * kTileTW, c0 = cb * kTileCB;
+
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
+
+    // ---- window: pixel q = (row, col) holds dY(h0 + pad_h - R + row, w0 + pad_w - (S-1) + col) ----
+    {
+        const int chunk = lane & 7;
+        const bool cin = c0 + chunk * 8 < a.C;
+#pragma unroll
+        for (int i = 0; i < LOADS; ++i) {
+            const int q0 = (wave + 4 * i) * 8;
+            if (q0 < NPIX) {
+                const int q = q0 + (lane >> 3);
+                const int row = q / WC, col = q - (q / WC) * WC;
+                const int u = h0 + a.pad_h - R + row, v = w0 + a.pad_w - (S - 1) + col;
+                uint32_t off = kOob;
+                if (cin && q < NPIX && u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
+                    off = uint32_t((((n * a.Ho + u) * a.Wo + v) * a.C + c0 + chunk * 8) * 2);
+                dma16(rdy, lds + q0 * 128, off, 0);
+            }
+        }
+    }
+    // ---- the block's filters: 64 channels x R*S taps, contiguous in W ----
+#pragma unroll
+    for (int i = 0; i < G::RAW_BYTES / 1024; ++i)
+        if ((i & 3) == wave)
+            dma16(rw, lds + G::WIN_BYTES + i * 1024, uint32_t(i * 1024 + lane * 16),
+                  uint32_t(c0 * R * S * 2));
+    wait_vm<0>();
+    __syncthreads();
+    // ---- weight pairs: word (i, t, ch) = (W[c][2i][t], W[c][2i+1][t]) ----
+#pragma unroll
+    for (int k = 0; k < (G::WTS + 255) / 256; ++k) {
+        const int e = tid + k * 256;
+        if (e < G::WTS) {
+            const int ch = e % kTileCB;
+            const int t = (e / kTileCB) % S;
+            const int i = e / (kTileCB * S);
+            const uint32_t lo = raw[ch * R * S + (2 * i) * S + t];
+            const uint32_t hi = 2 * i + 1 < R ? uint32_t(raw[ch * R * S + (2 * i + 1) * S + t]) : 0u;
+            wts[e] = lo | (hi << 16);
+        }
+    }
+    __syncthreads();
+
+    const int cp = lane & 31;                                 // channel pair
+    const int pb = 2 * wave + (lane >> 5);
+    const int lr0 = (pb / kTilePBW) * kTileTHL, lc0 = (pb % kTilePBW) * kTileTWL;
+
+    uint32_t wp[NL][S][2];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            const i32x2 v = *reinterpret_cast<const i32x2*>(wts + (i * S + t) * kTileCB + cp * 2);
+            wp[i][t][0] = uint32_t(v[0]);
+            wp[i][t][1] = uint32_t(v[1]);
+        }
+
+    float acc[kTileTHL][kTileTWL][2];
+#pragma unroll
+    for (int h = 0; h < kTileTHL; ++h)
+#pragma unroll
+        for (int w = 0; w < kTileTWL; ++w) acc[h][w][0] = acc[h][w][1] = 0.f;
+
+    const uint32_t* const win = reinterpret_cast<const uint32_t*>(lds) + (lr0 * WC + lc0) * 32 + cp;
+    uint32_t prev[RV], cur[RV];
+#pragma unroll
+    for (int v = 0; v < RV; ++v) prev[v] = win[v * 32];
+#pragma unroll
+    for (int ul = 1; ul < kTileTHL + R; ++ul) {
+#pragma unroll
+        for (int v = 0; v < RV; ++v) cur[v] = win[(ul * WC + v) * 32];
+        uint32_t p0[RV], p1[RV];
+#pragma unroll
+        for (int v = 0; v < RV; ++v) {
+            p0[v] = pair_lo(cur[v], prev[v]);   // channel 2cp: (row ul, row ul-1)
+            p1[v] = pair_hi(cur[v], prev[v]);   // channel 2cp+1
+        }
+#pragma unroll
+        for (int hl = 0; hl < kTileTHL; ++hl) {
+            const int r = hl + R - ul;         // first tap row of the pair
+            if (r < 0 || r >= R || (r & 1)) continue;
+            // tap-outer: consecutive dot2s update different accumulators
+#pragma unroll
+            for (int t = 0; t < S; ++t)
+#pragma unroll
+                for (int wl = 0; wl < kTileTWL; ++wl) {
+                    const int v = wl + S - 1 - t;
+                    acc[hl][wl][0] = dot2<T>(p0[v], wp[r / 2][t][0], acc[hl][wl][0]);
+                    acc[hl][wl][1] = dot2<T>(p1[v], wp[r / 2][t][1], acc[hl][wl][1]);
+                }
+        }
+#pragma unroll
+        for (int v = 0; v < RV; ++v) prev[v] = cur[v];
+    }
+
+    // ---- store: 2 channels (4 bytes) per lane and pixel ----
+    const int c = c0 + 2 * cp;
+    if (c < a.C) {
+#pragma unroll
+        for (int hl = 0; hl < kTileTHL; ++hl) {
+            const int h = h0 + lr0 + hl;
+#pragma unroll
+            for (int wl = 0; wl < kTileTWL; ++wl) {
+                const int w = w0 + lc0 + wl;
+                if (h < a.H && w < a.W)
+                    buf_store4(int(pack2<T>(acc[hl][wl][0], acc[hl][wl][1])), rdx,
+                               uint32_t(((n * a.H + h) * a.W + w) * a.C + c) * 2u);
+            }
+        }
+    }
+}
+
 // ============================ rotated filter ================================
 
 constexpr int kRotCB = 8;      // channels per block
@@ -436,6 +618,17 @@ std::string dw_stream_reason(const Prob& p, int cpl) {
     return "";
 }
 
+std::string dw_tiled_reason(const Prob& p) {
+    if (!(p.groups == p.c && p.groups == p.k)) return "depthwise kernels need groups == C == K";
+    if (p.stride != 1) return "the LDS-tiled depthwise dgrad needs stride 1";
+    if (p.r != p.s || (p.r != 3 && p.r != 5 && p.r != 7))
+        return "the LDS-tiled depthwise dgrad has 3x3, 5x5 and 7x7 instances";
+    if (p.c % 8 != 0) return "the LDS-tiled depthwise dgrad needs C a multiple of 8";
+    if (p.n * p.h * p.w * p.c > (int64_t(1) << 30) || p.n * p.ho * p.wo * p.c > (int64_t(1) << 30))
+        return "tensor exceeds the 32-bit element range";
+    return "";
+}
+
 std::string dw_rotated_reason(const Prob& p) {
     if (!(p.groups == p.c && p.groups == p.k)) return "depthwise kernels need groups == C == K";
     if (p.stride != 1) return "the rotated-filter dgrad needs stride 1";
@@ -470,6 +663,36 @@ int launch_dgrad_dw_stream(const Prob& p, const Plan& pl, const void* dy, const 
     a.nthreads = int64_t(a.N) * a.nstrips * a.nbands * a.ncv;
     const bool ok = p.dtype == CNHWC_BF16 ? dispatch_stream<BF16>(*c, a, st) : dispatch_stream<F16>(*c, a, st);
     return ok ? CNHWC_OK : CNHWC_UNSUPPORTED;
+}
+
+namespace {
+template <typename T>
+int launch_tile_t(const Prob& p, const TileArgs& a, int blocks, hipStream_t st) {
+    switch (p.r) {
+    case 3: hipLaunchKernelGGL((dw_tile_kernel<T, 3, 3>), dim3(blocks), dim3(256), 0, st, a); return CNHWC_OK;
+    case 5: hipLaunchKernelGGL((dw_tile_kernel<T, 5, 5>), dim3(blocks), dim3(256), 0, st, a); return CNHWC_OK;
+    case 7: hipLaunchKernelGGL((dw_tile_kernel<T, 7, 7>), dim3(blocks), dim3(256), 0, st, a); return CNHWC_OK;
+    default: return CNHWC_UNSUPPORTED;
+    }
+}
+}  // namespace
+
+int launch_dgrad_dw_tiled(const Prob& p, const Plan&, const void* dy, const void* w, void* dx,
+                          hipStream_t st) {
+    TileArgs a{};
+    a.dy = dy; a.w = w; a.dx = dx;
+    a.dy_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
+    a.w_bytes = uint32_t(p.k * p.r * p.s * 2);
+    a.dx_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
+    a.N = int(p.n); a.H = int(p.h); a.W = int(p.w); a.C = int(p.c); a.Ho = int(p.ho); a.Wo = int(p.wo);
+    a.pad_h = p.pad_h; a.pad_w = p.pad_w;
+    const int th = tile_th(int(p.r));
+    a.tiles_h = int((p.h + th - 1) / th);
+    a.tiles_w = int((p.w + kTileTW - 1) / kTileTW);
+    a.cblocks = int((p.c + kTileCB - 1) / kTileCB);
+    const int64_t blocks = int64_t(a.N) * a.tiles_h * a.tiles_w * a.cblocks;
+    return p.dtype == CNHWC_BF16 ? launch_tile_t<BF16>(p, a, int(blocks), st)
+                                 : launch_tile_t<F16>(p, a, int(blocks), st);
 }
 
 int launch_dgrad_dw_rotated(const Prob& p, const Plan&, const void* dy, const void* w, void* dx,

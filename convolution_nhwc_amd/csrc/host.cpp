@@ -77,7 +77,7 @@ bool is_depthwise(const Prob& p) { return p.groups == p.c && p.groups == p.k; }
 bool variant_is_dgrad(int v) {
     return v == CNHWC_VAR_DGRAD_POINTWISE || v == CNHWC_VAR_DGRAD_IGEMM ||
            v == CNHWC_VAR_DGRAD_DW_STREAM || v == CNHWC_VAR_DGRAD_DW_ROTATED ||
-           v == CNHWC_VAR_DGRAD_GENERIC;
+           v == CNHWC_VAR_DGRAD_DW_TILED || v == CNHWC_VAR_DGRAD_GENERIC;
 }
 bool variant_is_fwd(int v) {
     return v == CNHWC_VAR_FWD_DIRECT || v == CNHWC_VAR_FWD_SPLITC ||
@@ -97,6 +97,7 @@ std::string variant_reason(const Prob& p, int op, int v, int cpl, int split_c) {
     case CNHWC_VAR_DGRAD_IGEMM: return dgrad_igemm_reason(p, false);
     case CNHWC_VAR_DGRAD_DW_STREAM: return dw_stream_reason(p, cpl);
     case CNHWC_VAR_DGRAD_DW_ROTATED: return dw_rotated_reason(p);
+    case CNHWC_VAR_DGRAD_DW_TILED: return dw_tiled_reason(p);
     case CNHWC_VAR_FWD_DIRECT: return fwd_direct_reason(p, 1);
     case CNHWC_VAR_FWD_SPLITC: return fwd_direct_reason(p, split_c);
     case CNHWC_VAR_FWD_GROUPED: return fwd_grouped_reason(p);
@@ -119,6 +120,9 @@ std::string plan_name(const Prob& p, const Plan& pl) {
     case CNHWC_VAR_DGRAD_DW_ROTATED:
         std::snprintf(buf, sizeof buf, "dgrad_dw_rot_%s_f%lldx%lld_p%dx%d", dt(p),
                       (long long)p.r, (long long)p.s, p.pad_h, p.pad_w); break;
+    case CNHWC_VAR_DGRAD_DW_TILED:
+        std::snprintf(buf, sizeof buf, "dgrad_dw_tiled_%s_f%lldx%lld", dt(p), (long long)p.r,
+                      (long long)p.s); break;
     case CNHWC_VAR_DGRAD_GENERIC:
         std::snprintf(buf, sizeof buf, "dgrad_generic_%s", dt(p)); break;
     case CNHWC_VAR_FWD_DIRECT:
@@ -170,6 +174,7 @@ int choose(const Prob& p, int op, Plan* out) {
         if (is_depthwise(p)) {
             const bool big = p.r > 11 || p.s > 11 || p.r != p.s || p.pad_h != p.pad_w;
             if (p.stride == 1 && big) ok = take(CNHWC_VAR_DGRAD_DW_ROTATED, 0, 1);
+            if (!ok && p.stride == 1) ok = take(CNHWC_VAR_DGRAD_DW_TILED, 0, 1);
             if (!ok) {
                 int cpl = ov.cpl > 0 ? ov.cpl : dw_stream_best_cpl(p);
                 ok = take(CNHWC_VAR_DGRAD_DW_STREAM, cpl > 0 ? cpl : 1, 1);
@@ -296,6 +301,7 @@ int run(const cnhwc_problem* prob, int op, const void* in, const void* w, void* 
         case CNHWC_VAR_DGRAD_IGEMM: rc = launch_dgrad_igemm(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_DGRAD_DW_STREAM: rc = launch_dgrad_dw_stream(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_DGRAD_DW_ROTATED: rc = launch_dgrad_dw_rotated(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_DGRAD_DW_TILED: rc = launch_dgrad_dw_tiled(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_DGRAD_GENERIC: rc = launch_dgrad_generic(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_FWD_DIRECT:
         case CNHWC_VAR_FWD_SPLITC: rc = launch_fwd_direct(pc, pl, ip, w, op_, ws, s); break;

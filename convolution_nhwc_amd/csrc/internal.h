@@ -45,6 +45,8 @@ int launch_dgrad_dw_stream(const Prob& p, const Plan& pl, const void* dy, const 
                            void* dx, hipStream_t st);
 int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const void* w,
                             void* dx, hipStream_t st);
+int launch_dgrad_dw_tiled(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
+                          hipStream_t st);
 int launch_dgrad_generic(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
                          hipStream_t st);
 int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
@@ -62,6 +64,7 @@ int launch_fwd_generic(const Prob& p, const Plan& pl, const void* x, const void*
 std::string dgrad_igemm_reason(const Prob& p, bool pointwise);
 std::string dw_stream_reason(const Prob& p, int cpl);
 std::string dw_rotated_reason(const Prob& p);
+std::string dw_tiled_reason(const Prob& p);
 std::string fwd_direct_reason(const Prob& p, int split_c);
 std::string fwd_grouped_reason(const Prob& p);
 std::string fwd_window_reason(const Prob& p, int split_c);

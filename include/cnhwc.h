@@ -89,6 +89,7 @@ typedef struct cnhwc_problem {
 #define CNHWC_VAR_FWD_GROUPED 7      /* grouped forward, small groups merged block-diagonally */
 #define CNHWC_VAR_FWD_GENERIC 8      /* plain one-output-per-lane forward (any valid problem) */
 #define CNHWC_VAR_DGRAD_GENERIC 9    /* plain one-output-per-lane dgrad (any valid problem) */
+#define CNHWC_VAR_DGRAD_DW_TILED 10  /* depthwise dgrad, stride 1, 3x3/5x5/7x7, dY window tiled in LDS */
 
 /* Output dims by the floor formula above.  INVALID_ARG for a bad descriptor. */
 int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo);

@@ -1,6 +1,6 @@
 """GPU parity of the depthwise dgrad kernels (row streaming with cpl channels
-per lane; rotated-filter tiled for large / non-square filters with per-axis
-padding) against the fp64 oracle."""
+per lane; LDS-tiled for stride-1 3x3/5x5/7x7; rotated-filter tiled for large /
+non-square filters with per-axis padding) against the fp64 oracle."""
 import numpy as np
 import pytest
 
@@ -66,11 +66,43 @@ def test_rotated_parity(p):
         parity(p, "dgrad", 302)
 
 
+TILED = [
+    DW(2, 19, 30, 64, 3, 3, 1, 1, 1),          # ragged rows and columns of tiles
+    DW(1, 8, 28, 128, 3, 3, 1, 1, 1),          # exactly one tile row / column
+    DW(1, 17, 57, 72, 3, 3, 1, 0, 1),          # C not a multiple of 64, pads differ
+    DW(2, 23, 17, 32, 5, 5, 1, 2, 2),
+    DW(1, 12, 31, 24, 5, 5, 1, 4, 0),          # pad > R-1 on one axis
+    DW(1, 20, 22, 64, 7, 7, 1, 3, 3),
+    DW(1, 9, 12, 16, 7, 7, 1, 2, 5),           # short image, odd pads
+    DW(1, 5, 6, 8, 7, 7, 1, 3, 3),             # image smaller than the filter
+    DW(2, 19, 29, 64, 3, 3, 1, 1, 1, dtype="bf16"),
+    DW(1, 20, 22, 40, 7, 7, 1, 3, 3, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("p", TILED, ids=ident)
+def test_tiled_parity(p):
+    with api.override(variant=api.VAR_DGRAD_DW_TILED):
+        assert "dw_tiled" in api.cnhwc_plan(p, api.OP_DGRAD)[0]
+        parity(p, "dgrad", 306)
+
+
+def test_tiled_and_stream_agree_on_exact_inputs():
+    p = DW(1, 21, 30, 64, 7, 7, 1, 3, 3)
+    ab, af, wb, wf = operands(p, "dgrad", 307, exact=True)
+    with api.override(variant=api.VAR_DGRAD_DW_TILED):
+        a = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    with api.override(variant=api.VAR_DGRAD_DW_STREAM, cpl=2):
+        b = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    assert np.array_equal(a, b)
+
+
 @pytest.mark.parametrize("p,var,cpl", [(DW(1, 17, 19, 32, 3, 3, 1, 1, 1), api.VAR_DGRAD_DW_STREAM, 8),
+                                       (DW(1, 17, 30, 64, 5, 5, 1, 2, 2), api.VAR_DGRAD_DW_TILED, 0),
                                        (DW(1, 17, 19, 32, 7, 7, 2, 3, 3), api.VAR_DGRAD_DW_STREAM, 2),
                                        (DW(1, 20, 20, 8, 13, 9, 1, 6, 2), api.VAR_DGRAD_DW_ROTATED, 0),
                                        (DW(1, 20, 20, 16, 5, 5, 1, 2, 2, dtype="bf16"), api.VAR_DGRAD_DW_STREAM, 4)],
-                         ids=["s3x3", "s7x7st2", "rot13x9", "s5x5bf16"])
+                         ids=["s3x3", "t5x5", "s7x7st2", "rot13x9", "s5x5bf16"])
 def test_exact_small_integers_bitwise(p, var, cpl):
     with api.override(variant=var, cpl=cpl):
         parity(p, "dgrad", 303, exact=True)

@@ -89,8 +89,8 @@ EXPECT = {
     "c3b_3x3_s2": api.VAR_DGRAD_IGEMM,
     "c4a_splitc_fwd": api.VAR_FWD_SPLITC,
     "c4b_grouped_fwd": api.VAR_FWD_GROUPED,
-    "c5_dw3x3": api.VAR_DGRAD_DW_STREAM,
-    "c5_dw7x7": api.VAR_DGRAD_DW_STREAM,
+    "c5_dw3x3": api.VAR_DGRAD_DW_TILED,
+    "c5_dw7x7": api.VAR_DGRAD_DW_TILED,
     "c5_dw31x31": api.VAR_DGRAD_DW_ROTATED,
     "c5_dw51x5": api.VAR_DGRAD_DW_ROTATED,
     "c5_dw5x51": api.VAR_DGRAD_DW_ROTATED,
