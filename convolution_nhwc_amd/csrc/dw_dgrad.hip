@@ -265,9 +265,12 @@ constexpr int kTileTWL = 7;                  // lane tile columns
 constexpr int kTilePBH = 2, kTilePBW = 4;    // lane tiles per block tile
 constexpr int kTileTW = kTileTWL * kTilePBW; // 28
 constexpr int kTileCB = 64;                  // channels per block
-// lane tile rows: 4, or 2 for 7x7 (its 7 x 4 weight pairs and accumulators
-// must stay in registers)
+// lane tile rows
+// (2 for 7x7: its 7 x 4 weight pairs and 2 x 7 x 2 accumulators fill the
+// register file)
 constexpr int tile_thl(int r) { return r >= 7 ? 2 : 4; }
+// weight pairs held in registers (else read from LDS at each use)
+constexpr bool tile_wreg(int) { return true; }
 constexpr int tile_th(int r) { return tile_thl(r) * kTilePBH; }
 
 struct TileArgs {
@@ -277,6 +280,7 @@ struct TileArgs {
     uint32_t dy_bytes, w_bytes, dx_bytes;
     int N, H, W, C, Ho, Wo, pad_h, pad_w;
     int tiles_h, tiles_w, cblocks;
+    int nblocks, remap;
 };
 
 template <int R, int S>
@@ -306,13 +310,17 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // Blocks are dealt to the 8 XCDs round-robin; remap so each XCD walks
+    // whole (image, channel block) groups in raster order and vertically
+    // neighbouring tiles, which share halo rows, meet in the same L2.
     int bid = blockIdx.x;
-    const int cb = bid % a.cblocks;
-    bid /= a.cblocks;
+    if (a.remap) bid = (bid & 7) * (a.nblocks >> 3) + (bid >> 3);
     const int tw_i = bid % a.tiles_w;
     bid /= a.tiles_w;
     const int th_i = bid % a.tiles_h;
-    const int n = bid / a.tiles_h;
+    bid /= a.tiles_h;
+    const int cb = bid % a.cblocks;
+    const int n = bid / a.cblocks;
     const int h0 = th_i * kTileTH, w0 = tw_i * kTileTW, c0 = cb * kTileCB;
 
     const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
@@ -364,15 +372,18 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
     const int pb = 2 * wave + (lane >> 5);
     const int lr0 = (pb / kTilePBW) * kTileTHL, lc0 = (pb % kTilePBW) * kTileTWL;
 
-    uint32_t wp[NL][S][2];
+    constexpr bool WREG = tile_wreg(R);
+    uint32_t wp[WREG ? NL : 1][WREG ? S : 1][2];
+    if constexpr (WREG) {
 #pragma unroll
-    for (int i = 0; i < NL; ++i)
+        for (int i = 0; i < NL; ++i)
 #pragma unroll
-        for (int t = 0; t < S; ++t) {
-            const i32x2 v = *reinterpret_cast<const i32x2*>(wts + (i * S + t) * kTileCB + cp * 2);
-            wp[i][t][0] = uint32_t(v[0]);
-            wp[i][t][1] = uint32_t(v[1]);
-        }
+            for (int t = 0; t < S; ++t) {
+                const i32x2 v = *reinterpret_cast<const i32x2*>(wts + (i * S + t) * kTileCB + cp * 2);
+                wp[i][t][0] = uint32_t(v[0]);
+                wp[i][t][1] = uint32_t(v[1]);
+            }
+    }
 
     float acc[kTileTHL][kTileTWL][2];
 #pragma unroll
@@ -400,13 +411,23 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
             if (r < 0 || r >= R || (r & 1)) continue;
             // tap-outer: consecutive dot2s update different accumulators
 #pragma unroll
-            for (int t = 0; t < S; ++t)
+            for (int t = 0; t < S; ++t) {
+                uint32_t w0, w1;
+                if constexpr (WREG) {
+                    w0 = wp[r / 2][t][0];
+                    w1 = wp[r / 2][t][1];
+                } else {
+                    const i32x2 v = *reinterpret_cast<const i32x2*>(wts + ((r / 2) * S + t) * kTileCB + cp * 2);
+                    w0 = uint32_t(v[0]);
+                    w1 = uint32_t(v[1]);
+                }
 #pragma unroll
                 for (int wl = 0; wl < kTileTWL; ++wl) {
                     const int v = wl + S - 1 - t;
-                    acc[hl][wl][0] = dot2<T>(p0[v], wp[r / 2][t][0], acc[hl][wl][0]);
-                    acc[hl][wl][1] = dot2<T>(p1[v], wp[r / 2][t][1], acc[hl][wl][1]);
+                    acc[hl][wl][0] = dot2<T>(p0[v], w0, acc[hl][wl][0]);
+                    acc[hl][wl][1] = dot2<T>(p1[v], w1, acc[hl][wl][1]);
                 }
+            }
         }
 #pragma unroll
         for (int v = 0; v < RV; ++v) prev[v] = cur[v];
@@ -691,6 +712,8 @@ int launch_dgrad_dw_tiled(const Prob& p, const Plan&, const void* dy, const void
     a.tiles_w = int((p.w + kTileTW - 1) / kTileTW);
     a.cblocks = int((p.c + kTileCB - 1) / kTileCB);
     const int64_t blocks = int64_t(a.N) * a.tiles_h * a.tiles_w * a.cblocks;
+    a.nblocks = int(blocks);
+    a.remap = blocks % 8 == 0 ? 1 : 0;
     return p.dtype == CNHWC_BF16 ? launch_tile_t<BF16>(p, a, int(blocks), st)
                                  : launch_tile_t<F16>(p, a, int(blocks), st);
 }

@@ -348,6 +348,7 @@ struct GrpArgs {
     Geo geo;
     int nblocks, remap;
     int halo_bytes;   // LDS bytes of the halo (start of the weight taps)
+    FastDiv fd_img, fd_iw, fd_per, fd_tw;   // division by IH*IW, IW, TH*TW, TW
 };
 
 template <typename T, int BN>
@@ -378,29 +379,45 @@ __global__ __launch_bounds__(kThreads) void fwd_grouped_kernel(const GrpArgs a) 
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
 
-    // halo: 4 chunks of 8 channels per pixel
+    // halo: 4 chunks of 8 channels per pixel, loaded straight into LDS (one
+    // 16-pixel load per wave instruction; the chunk swizzle is applied on the
+    // source side: lane -> (pixel, physical chunk), reading logical chunk
+    // physical ^ (pixel & 3))
     const int hpix = geo.NB * geo.IH * geo.IW;
-    const int hchunk = tid & 3;
-#pragma unroll
-    for (int j = 0; j < kGHaloSlots; ++j) {
-        const int hp = (tid >> 2) + j * (kThreads / 4);
-        if (hp >= hpix) continue;
-        const int per = geo.IH * geo.IW;
-        const int nb = hp / per;
-        const int rem = hp - nb * per;
-        const int ih = rem / geo.IW, iw = rem - (rem / geo.IW) * geo.IW;
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    for (int q0 = wv * 16; q0 < hpix; q0 += (kThreads / 64) * 16) {
+        const int hp = q0 + (lane >> 2);
+        const int hchunk = (lane & 3) ^ (hp & 3);
+        const int nb = fdiv(hp, a.fd_img);
+        const int rem = hp - nb * (geo.IH * geo.IW);
+        const int ih = fdiv(rem, a.fd_iw), iw = rem - ih * geo.IW;
         const int n = n0 + nb;
         const int h = ho0 * s - a.pad_h + ih, w = wo0 * s - a.pad_w + iw;
         uint32_t off = kOob;
-        if (n < a.N && h >= 0 && h < a.H && w >= 0 && w < a.W)
+        if (hp < hpix && n < a.N && h >= 0 && h < a.H && w >= 0 && w < a.W)
             off = uint32_t(((n * a.H + h) * a.W + w) * a.C + cbase + hchunk * 8) * 2u;
-        const i32x4 v = buf_load16(rx, off);
-        *reinterpret_cast<i32x4*>(hs + hp * 64 + (((hchunk ^ (hp & 3))) * 16)) = v;
+        dma16(rx, hs + q0 * 64, off, 0);
     }
     // block-diagonal weights: row kk (output channel of the set) has the Cg
     // weights of its group at columns (kk / Kg) * Cg .. +Cg, zeros elsewhere.
     // Staged per 16-byte LDS chunk (8 merged channels of one row and tap).
     const int nchunks = taps * BN * 4;
+    if (a.Cg % 8 == 0) {
+        // every chunk lies inside one group's channel block or is zero (an
+        // out-of-range load writes zeros): async loads, 16 rows per instruction
+        for (int e0 = wv * 64; e0 < nchunks; e0 += kThreads) {
+            const int e = e0 + lane;
+            const int row = (e >> 2) % BN;
+            const int tap = (e >> 2) / BN;
+            const int c8 = (e & 3) ^ (row & 3);   // logical chunk held by this physical slot
+            const int gl = row / a.Kg;
+            const int k = kbase + row;
+            uint32_t off = kOob;
+            if (row < a.bn && (c8 * 8) / a.Cg == gl)
+                off = uint32_t((k * taps + tap) * a.Cg + c8 * 8 - gl * a.Cg) * 2u;
+            dma16(rw, ws + (e0 >> 2) * 64, off, 0);
+        }
+    } else {
     for (int e = tid; e < nchunks; e += kThreads) {
         const int c8 = e & 3;
         const int row = (e >> 2) % BN;
@@ -408,11 +425,7 @@ __global__ __launch_bounds__(kThreads) void fwd_grouped_kernel(const GrpArgs a) 
         const int gl = row / a.Kg;              // group of this output channel within the set
         const int k = kbase + row;
         i32x4 v = {0, 0, 0, 0};
-        if (a.Cg % 8 == 0) {
-            // the chunk lies inside one group's channel block
-            if (row < a.bn && (c8 * 8) / a.Cg == gl)
-                v = buf_load16(rw, uint32_t((k * taps + tap) * a.Cg + c8 * 8 - gl * a.Cg) * 2u);
-        } else {
+        {
             // several groups share the chunk: element by element
             uint32_t h[8];
 #pragma unroll
@@ -427,6 +440,8 @@ __global__ __launch_bounds__(kThreads) void fwd_grouped_kernel(const GrpArgs a) 
         }
         *reinterpret_cast<i32x4*>(ws + tap * W_TAP + row * 64 + ((c8 ^ (row & 3)) * 16)) = v;
     }
+    }
+    wait_vm<0>();
     __syncthreads();
 
     const int frow = lane & 15, fgrp = lane >> 4;
@@ -486,9 +501,9 @@ __global__ __launch_bounds__(kThreads) void fwd_grouped_kernel(const GrpArgs a) 
         const int row = q / CPR, cc = q % CPR;
         if (row >= tile_pix || cc * 8 >= a.bn) continue;
         const int per = geo.TH * geo.TW;
-        const int nb = row / per;
+        const int nb = fdiv(row, a.fd_per);
         const int rem = row - nb * per;
-        const int th = rem / geo.TW, tw = rem - (rem / geo.TW) * geo.TW;
+        const int th = fdiv(rem, a.fd_tw), tw = rem - th * geo.TW;
         const int n = n0 + nb, ho = ho0 + th, wo = wo0 + tw;
         if (n >= a.N || ho >= a.Ho || wo >= a.Wo) continue;
         const i32x4 v = *reinterpret_cast<const i32x4*>(lds + row * C_STRIDE + cc * 16);
@@ -689,10 +704,16 @@ int launch_fwd_grouped(const Prob& p, const Plan&, const void* x, const void* w,
     a.nblocks = int(blocks);
     a.remap = (blocks % 8 == 0) ? 1 : 0;
     const bool bf = p.dtype == CNHWC_BF16;
-    a.halo_bytes = a.geo.NB * a.geo.IH * a.geo.IW * 64;
+    // the halo is filled 16 pixels per load: round its LDS up to whole loads
+    a.halo_bytes = (a.geo.NB * a.geo.IH * a.geo.IW + 15) / 16 * 16 * 64;
+    a.fd_img = make_fastdiv(uint32_t(a.geo.IH * a.geo.IW));
+    a.fd_iw = make_fastdiv(uint32_t(a.geo.IW));
+    a.fd_per = make_fastdiv(uint32_t(a.geo.TH * a.geo.TW));
+    a.fd_tw = make_fastdiv(uint32_t(a.geo.TW));
 #define CNHWC_GRP(BNV)                                                                          \
     if (a.bn <= BNV) {                                                                          \
-        const size_t lds = size_t(a.halo_bytes) + size_t(p.r * p.s) * BNV * 64;                 \
+        const size_t lds = std::max(size_t(a.halo_bytes) + size_t(p.r * p.s) * BNV * 64,       \
+                                    size_t(kBM) * (BNV * 2 + 16));  /* epilogue tile */       \
         const void* fn = bf ? reinterpret_cast<const void*>(&fwd_grouped_kernel<BF16, BNV>)     \
                             : reinterpret_cast<const void*>(&fwd_grouped_kernel<F16, BNV>);     \
         if (lds > 64 * 1024 &&                                                                  \
