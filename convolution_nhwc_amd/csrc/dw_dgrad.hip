@@ -549,37 +549,63 @@ __global__ __launch_bounds__(256, 1) void dw_rotated_kernel(const RotArgs a) {
         while (ts_hi > ts_lo && base + (ts_hi - 1) * kRotTB >= a.Wo) --ts_hi;
     }
     const int orow = rg * kRotTHT, ocol = cg * kRotTWT;
-#pragma unroll 1
-    for (int rp = rp_lo; rp < rp_hi; ++rp) {
-#pragma unroll 1
-        for (int ts = ts_lo; ts < ts_hi; ++ts) {
-            uint32_t w0v[kRotTB], w1v[kRotTB];
+    // The (row pair, column slice) steps are software-pipelined: the LDS reads
+    // of the next step (3 window rows x 15 columns -- the middle row serves
+    // both output rows -- and 8 weight pairs) are issued before the dot2s of
+    // the current one, so one wave per SIMD keeps its VALU busy.
+    constexpr int NV = kRotTWT + kRotTB - 1;
+    struct Frag {
+        uint32_t x[kRotTHT + 1][NV];
+        uint32_t w0[kRotTB], w1[kRotTB];
+    };
+    const int nts = ts_hi - ts_lo;
+    const int total = (rp_hi - rp_lo) * nts;
+    int lrp = rp_lo, lts = ts_lo;     // load cursor
+    auto load = [&](Frag& f) {
 #pragma unroll
-            for (int t = 0; t < kRotTB; ++t) {
-                const i32x2 v = *reinterpret_cast<const i32x2*>(
-                    wpl + (rp * tpad + ts * kRotTB + t) * kRotCB + cp * 2);
-                w0v[t] = uint32_t(v[0]);
-                w1v[t] = uint32_t(v[1]);
+        for (int t = 0; t < kRotTB; ++t) {
+            const i32x2 v = *reinterpret_cast<const i32x2*>(
+                wpl + (lrp * tpad + lts * kRotTB + t) * kRotCB + cp * 2);
+            f.w0[t] = uint32_t(v[0]);
+            f.w1[t] = uint32_t(v[1]);
+        }
+        const uint32_t* r0 = win + (orow + 2 * lrp) * a.row_dw + (ocol + lts * kRotTB) * 4 + cp;
+#pragma unroll
+        for (int i = 0; i <= kRotTHT; ++i)
+#pragma unroll
+            for (int vl = 0; vl < NV; ++vl) f.x[i][vl] = r0[i * a.row_dw + vl * 4];
+        ++lts;
+        const bool wrap = lts >= ts_hi;
+        lts = wrap ? ts_lo : lts;
+        lrp += wrap ? 1 : 0;
+    };
+    auto compute = [&](const Frag& f) {
+#pragma unroll
+        for (int i = 0; i < kRotTHT; ++i) {
+            uint32_t p0[NV], p1[NV];
+#pragma unroll
+            for (int vl = 0; vl < NV; ++vl) {
+                p0[vl] = pair_lo(f.x[i][vl], f.x[i + 1][vl]);   // channel 2cp: (row u, row u+1)
+                p1[vl] = pair_hi(f.x[i][vl], f.x[i + 1][vl]);   // channel 2cp+1
             }
 #pragma unroll
-            for (int i = 0; i < kRotTHT; ++i) {
-                const uint32_t* r0 = win + (orow + i + 2 * rp) * a.row_dw + (ocol + ts * kRotTB) * 4 + cp;
-                const uint32_t* r1 = r0 + a.row_dw;
-                uint32_t p0[kRotTWT + kRotTB - 1], p1[kRotTWT + kRotTB - 1];
+            for (int t = 0; t < kRotTB; ++t)
 #pragma unroll
-                for (int vl = 0; vl < kRotTWT + kRotTB - 1; ++vl) {
-                    const uint32_t x0 = r0[vl * 4], x1 = r1[vl * 4];
-                    p0[vl] = pair_lo(x0, x1);   // channel 2cp: (row u, row u+1)
-                    p1[vl] = pair_hi(x0, x1);   // channel 2cp+1
+                for (int j = 0; j < kRotTWT; ++j) {
+                    acc[i][j][0] = dot2<T>(p0[j + t], f.w0[t], acc[i][j][0]);
+                    acc[i][j][1] = dot2<T>(p1[j + t], f.w1[t], acc[i][j][1]);
                 }
-#pragma unroll
-                for (int j = 0; j < kRotTWT; ++j)
-#pragma unroll
-                    for (int t = 0; t < kRotTB; ++t) {
-                        acc[i][j][0] = dot2<T>(p0[j + t], w0v[t], acc[i][j][0]);
-                        acc[i][j][1] = dot2<T>(p1[j + t], w1v[t], acc[i][j][1]);
-                    }
-            }
+        }
+    };
+    Frag fa, fb;
+    if (total > 0) load(fa);
+#pragma unroll 1
+    for (int it = 0; it < total; it += 2) {
+        if (it + 1 < total) load(fb);
+        compute(fa);
+        if (it + 1 < total) {
+            if (it + 2 < total) load(fa);
+            compute(fb);
         }
     }
     // ---- store: 2 channels per lane ----
