@@ -1046,6 +1046,8 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
         if (cost < best_cost) { best_cost = cost; best_bm = bm; }
     }
     a.bm = best_bm;
+    // tune >= 16: tile height override (pixels per tile, at most the capacity)
+    if (pl.tune >= 16) a.bm = std::min(pl.tune, BMC);
     int total = 0;
     bool all8 = true;
     for (int i = 0; i < nc; ++i) {

@@ -137,9 +137,11 @@ const char* cnhwc_last_error(void);
  * cpl: depthwise channels per lane (1, 2, 4 or 8); split_c: number of channel
  * splits for CNHWC_VAR_FWD_SPLITC; tune: a launch-shape knob of the chosen
  * kernel (implicit-GEMM dgrad: 1 runs every phase class on the ring kernel,
- * 2 runs classes with two or more taps on the dY-window kernel; other
- * kernels ignore it); chunk_limit_bytes: the per-view byte limit of the chunk
- * planner.  Pass NULL to clear. */
+ * 2 runs classes with two or more taps on the dY-window kernel, a value of 16
+ * or more sets the ring kernel's pixels per tile; direct forward: 1 forces the
+ * register-staged kernel, 2 the input-window kernel; other kernels ignore it);
+ * chunk_limit_bytes: the per-view byte limit of the chunk planner.  Pass NULL
+ * to clear. */
 typedef struct cnhwc_override {
     int32_t variant;
     int32_t cpl;
