@@ -321,9 +321,18 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total4;
          i += int64_t(gridDim.x) * blockDim.x) {
         f32x4 s = reinterpret_cast<const f32x4*>(ws)[i];
-        for (int sp = 1; sp < splits; ++sp) {
-            const f32x4 v = reinterpret_cast<const f32x4*>(ws)[i + sp * stride4];
-            s[0] += v[0]; s[1] += v[1]; s[2] += v[2]; s[3] += v[3];
+        // eight splits' loads are in flight at once; the adds stay in
+        // ascending split order
+        for (int sp0 = 1; sp0 < splits; sp0 += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (sp0 + j < splits) v[j] = reinterpret_cast<const f32x4*>(ws)[i + (sp0 + j) * stride4];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (sp0 + j < splits) {
+                    s[0] += v[j][0]; s[1] += v[j][1]; s[2] += v[j][2]; s[3] += v[j][3];
+                }
         }
         i32x2 o = {int(pack2<T>(s[0], s[1])), int(pack2<T>(s[2], s[3]))};
         __builtin_nontemporal_store(o, reinterpret_cast<i32x2*>(y) + i);
@@ -617,14 +626,15 @@ int fwd_direct_auto_split(const Prob& p) {
 }
 
 int launch_split_reduce(const Prob& p, int splits, const void* ws, void* y, hipStream_t st) {
+    // 64-lane blocks: a small output still spreads over every CU
     const int64_t total4 = p.n * p.ho * p.wo * p.k / 4;
-    const int64_t grid = std::min<int64_t>((total4 + 255) / 256, int64_t(kNumCUs) * 8);
+    const int64_t grid = std::min<int64_t>((total4 + 63) / 64, int64_t(kNumCUs) * 32);
     if (p.dtype == CNHWC_BF16)
-        hipLaunchKernelGGL(split_reduce_kernel<BF16>, dim3(grid), dim3(256), 0, st,
+        hipLaunchKernelGGL(split_reduce_kernel<BF16>, dim3(grid), dim3(64), 0, st,
                            static_cast<const float*>(ws), static_cast<unsigned short*>(y), total4,
                            total4, splits);
     else
-        hipLaunchKernelGGL(split_reduce_kernel<F16>, dim3(grid), dim3(256), 0, st,
+        hipLaunchKernelGGL(split_reduce_kernel<F16>, dim3(grid), dim3(64), 0, st,
                            static_cast<const float*>(ws), static_cast<unsigned short*>(y), total4,
                            total4, splits);
     return CNHWC_OK;
