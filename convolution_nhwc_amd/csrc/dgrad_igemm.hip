@@ -406,6 +406,273 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
 }
 
 // ---------------------------------------------------------------------------
+// Pointwise (1x1) dgrad for C <= 64: persistent, filter resident in LDS.
+//
+// The operands and the per-output reduction are those of the ring kernel's
+// pointwise specialisation with its 128 x 64 tile (same fragments, same
+// ascending 32-deep MFMA chain per output, same rounding), so the results are
+// bit-identical.  What changes is the schedule around them:
+//   * the whole filter (K x 64 channels, 128-byte k-rows swizzled like a W
+//     stage) is loaded into LDS once per block, so the ring carries dY only;
+//   * one block per CU walks M tiles b, b + G, b + 2G, ... and all their
+//     64-deep reduction steps flow through one ring of NS dY stages, so up to
+//     NS - 1 steps of dY loads stay in flight across tile boundaries;
+//   * a finished tile is rounded into the dY stage it has just consumed (no
+//     other loads target that stage until the next step) and written back as
+//     full 128-byte pixel rows while the next tile's loads are in flight.
+struct PwArgs {
+    const void* dy;
+    const void* w;
+    void* dx;
+    uint32_t dy_bytes, w_bytes, dx_bytes;
+    int M, C, K;       // pixels, channels of dX (<= 64), channels of dY
+    int kpad;          // K rounded up to the 64-deep step
+    int bm;            // pixels per tile (<= 128)
+    int ntiles;        // M tiles
+    int nblocks;       // grid size G (<= ntiles)
+};
+
+constexpr int kPwBM = 128;                  // tile capacity: 2 waves x 4 x 16 pixels
+constexpr int kPwBN = 64;                   // channels: 2 waves x 2 x 16
+constexpr int kPwStage = kPwBM * kARow;     // one 64-deep dY stage (16 KiB)
+constexpr int kPwLds = 160 * 1024;          // LDS per CU
+
+template <typename T, int NS, bool KR>
+__global__ __launch_bounds__(kThreads, 1) void dgrad_pw_persist_kernel(const PwArgs a) {
+    constexpr int WMB = 4, WNB = 2, WAVES_N = 2;
+    constexpr int A_BYTES = kPwStage;
+    constexpr int B_ROW = kPwBN * 2;                 // bytes of one filter k-row
+    constexpr int LOADS = A_BYTES / 1024 / 4;        // async loads per lane per stage
+    constexpr int W_BASE = NS * A_BYTES;             // the filter follows the stages
+    constexpr int NLOW = NS < 4 ? NS : 4;            // stages addressed off the first base
+    static_assert(LOADS * NS < 64, "vmcnt range");
+    static_assert((NLOW - 1) * A_BYTES < 65536, "stage offsets fit the LDS immediate");
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int b = blockIdx.x;
+    const int G = a.nblocks;
+    const int my_tiles = (a.ntiles - b + G - 1) / G;
+    const int steps = my_tiles * (a.kpad / kBK);
+
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
+
+    // ---- filter -> LDS once: 1 KiB regions of 8 k-rows, rows past K and
+    // channels past C read as zeros ----
+#pragma unroll 1
+    for (int q = wave; q < a.kpad / 8; q += 4) {
+        const int row = 8 * q + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz_b<8>(row);
+        const uint32_t v = (row < a.K && chunk * 8 < a.C) ? uint32_t((row * a.C + chunk * 8) * 2) : kOob;
+        dma16(rw, lds + W_BASE + q * 1024, v, 0);
+    }
+
+    // ---- per-lane dY sources (tile-relative): region q = wave + 4*i holds rows 8q .. 8q+7 ----
+    uint32_t a_off[LOADS];
+    int a_row[LOADS], a_kq[LOADS];
+#pragma unroll
+    for (int i = 0; i < LOADS; ++i) {
+        const int row = 8 * (wave + 4 * i) + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz_a(row);
+        a_row[i] = row;
+        a_kq[i] = chunk * 8;
+        a_off[i] = uint32_t((row * a.K + chunk * 8) * 2);
+    }
+    // issue cursor (uniform): tile and 64-deep chunk of the step being loaded
+    int i_mt = b, i_kk = 0;
+    int i_lim = min(a.bm, a.M - i_mt * a.bm);        // valid rows of the tile
+    auto advance_i = [&]() {
+        i_kk += kBK;
+        if (i_kk >= a.kpad) {
+            i_kk = 0;
+            i_mt += G;
+            i_lim = min(a.bm, a.M - i_mt * a.bm);
+        }
+    };
+    auto dma_one = [&](auto stg, auto dsc) {
+        constexpr int STG = decltype(stg)::value, D = decltype(dsc)::value;
+        (void)a_off; (void)a_row; (void)a_kq;
+        uint32_t v = a_row[D] < i_lim ? a_off[D] : kOob;
+        if (KR) v = (i_kk + a_kq[D] < a.K) ? v : kOob;
+        dma16(rdy, lds + STG * A_BYTES + (wave + 4 * D) * 1024, v,
+              uint32_t((i_mt * a.bm * a.K + i_kk) * 2));
+    };
+
+    // ---- per-lane LDS fragment addresses ----
+    const int wm = wave / WAVES_N, wn = wave % WAVES_N;
+    const int frow = lane & 15, fgrp = lane >> 4;
+    uint32_t fa_addr[2][WMB];     // stage 0 (stages 1..NLOW-1 add an immediate)
+    uint32_t fa_hi[2][WMB];       // stage NLOW (stages above add an immediate)
+    uint32_t fb_addr[2][WNB][2];  // filter k-rows 0..63 (a step adds its chunk offset)
+    const uint32_t lds0 = lds_addr(lds);
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+        const int chunk = ks * 4 + fgrp;
+#pragma unroll
+        for (int i = 0; i < WMB; ++i) {
+            const int row = wm * (WMB * 16) + i * 16 + frow;
+            fa_addr[ks][i] = lds0 + row * kARow + ((chunk ^ swz_a(row)) << 4);
+            fa_hi[ks][i] = fa_addr[ks][i] + NLOW * A_BYTES;
+        }
+#pragma unroll
+        for (int j = 0; j < WNB; ++j)
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int k = ks * 32 + fgrp * 8 + 4 * h + (frow >> 2);
+                const int c = wn * (WNB * 16) + j * 16 + 4 * (frow & 3);
+                fb_addr[ks][j][h] = lds0 + W_BASE + k * B_ROW +
+                                    (((c >> 3) ^ swz_b<8>(k)) << 4) + (c & 7) * 2;
+            }
+    }
+
+    f32x4 acc[WMB][WNB];
+#pragma unroll
+    for (int i = 0; i < WMB; ++i)
+#pragma unroll
+        for (int j = 0; j < WNB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    i32x4 fa[2][WMB];
+    i32x2 fb[2][WNB][2];
+    constexpr int NREAD = 2 * WNB + WMB;
+    // read R of half KS: filter rows at byte offset wofs, dY out of stage STG
+    auto read_one = [&](auto stg, auto ksc, auto rc, uint32_t wofs) {
+        constexpr int STG = decltype(stg)::value, KS = decltype(ksc)::value;
+        constexpr int R = decltype(rc)::value;
+        (void)fa; (void)fb; (void)fa_addr; (void)fa_hi; (void)fb_addr;
+        if constexpr (R < 2 * WNB) {
+            asm volatile("ds_read_b64_tr_b16 %0, %1"
+                         : "=v"(fb[KS][R / 2][R % 2])
+                         : "v"(fb_addr[KS][R / 2][R % 2] + wofs));
+        } else if constexpr (STG < NLOW) {
+            asm volatile("ds_read_b128 %0, %1 offset:%2"
+                         : "=v"(fa[KS][R - 2 * WNB])
+                         : "v"(fa_addr[KS][R - 2 * WNB]), "i"(STG * A_BYTES));
+        } else {
+            asm volatile("ds_read_b128 %0, %1 offset:%2"
+                         : "=v"(fa[KS][R - 2 * WNB])
+                         : "v"(fa_hi[KS][R - 2 * WNB]), "i"((STG - NLOW) * A_BYTES));
+        }
+    };
+    auto wait_frags = [&](auto ksc) {
+        constexpr int KS = decltype(ksc)::value;
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[KS][0]), "+v"(fb[KS][0][0]));
+#pragma unroll
+        for (int i = 1; i < WMB; ++i) asm volatile("" : "+v"(fa[KS][i]));
+#pragma unroll
+        for (int j = 0; j < WNB; ++j) asm volatile("" : "+v"(fb[KS][j][0]), "+v"(fb[KS][j][1]));
+    };
+    auto mfma_one = [&](auto ksc, auto mc) {
+        constexpr int KS = decltype(ksc)::value, M = decltype(mc)::value;
+        constexpr int i = M / WNB, j = M % WNB;
+        const i32x4 bb = {fb[KS][j][0][0], fb[KS][j][0][1], fb[KS][j][1][0], fb[KS][j][1][1]};
+        acc[i][j] = mfma16x16x32<T>(bb, fa[KS][i], acc[i][j]);
+    };
+
+    // tile being multiplied and its reduction chunk
+    int x_mt = b, x_kk = 0;
+    // Round the finished tile into stage STG (consumed by every wave once the
+    // step's middle barrier has passed; the next load into it is issued after
+    // the closing barrier below), then store full pixel rows.  Rows are 128 B
+    // with the 16-byte chunk XOR-ed by row & 7.
+    auto epilogue = [&](auto stg) {
+        constexpr int STG = decltype(stg)::value;
+        unsigned char* tile = lds + STG * A_BYTES;
+#pragma unroll
+        for (int i = 0; i < WMB; ++i)
+#pragma unroll
+            for (int j = 0; j < WNB; ++j) {
+                const int row = wm * (WMB * 16) + i * 16 + frow;
+                const int col = wn * (WNB * 16) + j * 16 + fgrp * 4;
+                const i32x2 v = {int(pack2<T>(acc[i][j][0], acc[i][j][1])),
+                                 int(pack2<T>(acc[i][j][2], acc[i][j][3]))};
+                *reinterpret_cast<i32x2*>(tile + row * kARow + (((col >> 3) ^ (row & 7)) << 4) +
+                                          (col & 7) * 2) = v;
+                acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        const int lim = min(a.bm, a.M - x_mt * a.bm);
+        const int m0 = x_mt * a.bm;
+#pragma unroll
+        for (int q = 0; q < kPwBM * 8 / kThreads; ++q) {
+            const int e = tid + q * kThreads;
+            const int row = e >> 3, chunk = e & 7;
+            const i32x4 v = *reinterpret_cast<const i32x4*>(tile + row * kARow + ((chunk ^ (row & 7)) << 4));
+            if (row < lim && chunk * 8 < a.C)
+                buf_store16(v, rdx, uint32_t(((m0 + row) * a.C + chunk * 8) * 2));
+        }
+        asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    // One reduction step out of stage STG, as in the ring kernel: first half
+    // multiplies half 0 while reading half 1 and loading the step NS - 1
+    // ahead into the stage freed by the previous step; wait for the next
+    // stage; second half multiplies half 1 while reading the next step's
+    // half 0.  After a tile's last step, its epilogue.
+    constexpr int NM = WMB * WNB;
+    constexpr int NI0 = NREAD + LOADS;
+    constexpr int PER0 = (NI0 + NM - 1) / NM;
+    constexpr int PER1 = (NREAD + NM - 1) / NM;
+    auto step_fn = [&](auto stg) {
+        constexpr int STG = decltype(stg)::value;
+        constexpr int NXT = (STG + 1) % NS, FREE = (STG + NS - 1) % NS;
+        const int nkk = x_kk + kBK >= a.kpad ? 0 : x_kk + kBK;
+        const uint32_t w_cur = uint32_t(x_kk * B_ROW), w_nxt = uint32_t(nkk * B_ROW);
+        sfor<NM>([&](auto mc) {
+            constexpr int M = decltype(mc)::value;
+            mfma_one(IC<0>{}, mc);
+            sfor<PER0>([&](auto pc) {
+                constexpr int X = M * PER0 + decltype(pc)::value;
+                if constexpr (X < NREAD) read_one(stg, IC<1>{}, IC<X>{}, w_cur);
+                else if constexpr (X < NI0) dma_one(IC<FREE>{}, IC<X - NREAD>{});
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        advance_i();
+        wait_frags(IC<1>{});
+        wait_vm<(NS - 2) * LOADS>();
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        sfor<NM>([&](auto mc) {
+            constexpr int M = decltype(mc)::value;
+            mfma_one(IC<1>{}, mc);
+            sfor<PER1>([&](auto pc) {
+                constexpr int X = M * PER1 + decltype(pc)::value;
+                if constexpr (X < NREAD) read_one(IC<NXT>{}, IC<0>{}, IC<X>{}, w_nxt);
+            });
+            __builtin_amdgcn_sched_barrier(0);
+        });
+        wait_frags(IC<0>{});
+        if (nkk == 0) {
+            epilogue(stg);
+            x_mt += G;
+        }
+        x_kk = nkk;
+    };
+
+    if (steps > 0) {
+        sfor<NS - 1>([&](auto sc) {
+            sfor<LOADS>([&](auto dc) { dma_one(sc, dc); });
+            advance_i();
+        });
+        wait_vm<(NS - 2) * LOADS>();   // the filter and stage 0
+        __builtin_amdgcn_s_barrier();
+        sfor<NREAD>([&](auto rc) { read_one(IC<0>{}, IC<0>{}, rc, 0u); });
+        wait_frags(IC<0>{});
+#pragma unroll 1
+        for (int st = 0; st < steps; st += NS) {
+            sfor<NS>([&](auto sc) {
+                if (st + decltype(sc)::value < steps) step_fn(sc);
+            });
+        }
+    }
+    wait_vm<0>();   // loads issued past the last step still target LDS
+}
+
+// ---------------------------------------------------------------------------
 // General dgrad with the dY operand staged as an LDS window (classes with at
 // least two filter taps).
 //
@@ -824,6 +1091,67 @@ struct Cfg {
 };
 constexpr Cfg kCfgs[2] = {{224, 128, 1}, {128, 64, 2}};
 
+template <typename T, int NS, bool KR>
+void launch_pw_inst(const PwArgs& a, size_t lds, hipStream_t st) {
+    auto kern = dgrad_pw_persist_kernel<T, NS, KR>;
+    static bool attr_set = false;   // the attribute is per kernel; idempotent if raced
+    if (!attr_set) {
+        hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, kPwLds);
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(a.nblocks), dim3(kThreads), lds, st, a);
+}
+template <typename T, bool KR>
+void launch_pw_ns(int ns, const PwArgs& a, size_t lds, hipStream_t st) {
+    if (ns == 8) launch_pw_inst<T, 8, KR>(a, lds, st);
+    else launch_pw_inst<T, 4, KR>(a, lds, st);
+}
+
+// dY ring depth of the persistent pointwise kernel: the deepest that fits
+// beside the resident filter (0: the filter does not fit).
+int pw_stages(int64_t k) {
+    const int64_t wbytes = (k + kBK - 1) / kBK * kBK * kPwBN * 2;
+    for (int ns : {8, 4})
+        if (ns * int64_t(kPwStage) + wbytes <= kPwLds) return ns;
+    return 0;
+}
+
+// Persistent pointwise launch: one block per CU; tile height chosen so the
+// tiles spread most evenly over the blocks.
+int launch_pw_persist(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
+                      hipStream_t st) {
+    PwArgs a{};
+    a.dy = dy; a.w = w; a.dx = dx;
+    a.M = int(p.n * p.h * p.w);
+    a.C = int(p.c); a.K = int(p.k);
+    a.kpad = (a.K + kBK - 1) / kBK * kBK;
+    a.dy_bytes = uint32_t(int64_t(a.M) * a.K * 2);
+    a.w_bytes = uint32_t(int64_t(a.K) * a.C * 2);
+    a.dx_bytes = uint32_t(int64_t(a.M) * a.C * 2);
+    const int64_t slots = kNumCUs;
+    int best_bm = kPwBM;
+    int64_t best_cost = INT64_MAX;
+    for (int bm = kPwBM; bm >= kPwBM / 4; bm -= 2) {
+        const int64_t tiles = (a.M + bm - 1) / bm;
+        const int64_t cost = (tiles + slots - 1) / slots * bm;
+        if (cost < best_cost) { best_cost = cost; best_bm = bm; }
+    }
+    // tune >= 16: tile height override (pixels per tile, at most the capacity)
+    a.bm = pl.tune >= 16 ? std::min(pl.tune, kPwBM) : best_bm;
+    const int64_t ntiles = (a.M + a.bm - 1) / a.bm;
+    if (ntiles <= 0) return CNHWC_OK;
+    a.ntiles = int(ntiles);
+    a.nblocks = int(std::min<int64_t>(ntiles, slots));
+    const int ns = pw_stages(a.K);
+    const size_t lds = size_t(ns) * kPwStage + size_t(a.kpad) * kPwBN * 2;
+    const bool bf = p.dtype == CNHWC_BF16;
+    const bool kr = a.K % kBK != 0;
+    if (bf) kr ? launch_pw_ns<BF16, true>(ns, a, lds, st) : launch_pw_ns<BF16, false>(ns, a, lds, st);
+    else kr ? launch_pw_ns<F16, true>(ns, a, lds, st) : launch_pw_ns<F16, false>(ns, a, lds, st);
+    return CNHWC_OK;
+}
+
 }  // namespace
 
 std::string dgrad_igemm_reason(const Prob& p, bool pointwise) {
@@ -987,6 +1315,10 @@ int launch_dgrad_halo(const Prob& p, const void* dy, const void* w, void* dx, hi
 int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
                        hipStream_t st) {
     const bool pw = pl.variant == CNHWC_VAR_DGRAD_POINTWISE;
+    // pointwise with C <= 64 and a filter that fits LDS: the persistent
+    // kernel (tune 1 asks for the ring kernel)
+    if (pw && pl.tune != 1 && p.c <= kPwBN && pw_stages(p.k) > 0)
+        return launch_pw_persist(p, pl, dy, w, dx, st);
     // Stride 1: classes with two or more taps go to the window kernel, the
     // rest (and the pointwise fast path) to the ring kernel below.  Strided
     // problems split into several classes of few taps each, where the window

@@ -88,6 +88,23 @@ def test_pointwise_bit_identical_to_general(p):
     assert np.array_equal(fast.view(np.uint16), gen.view(np.uint16))
 
 
+@pytest.mark.parametrize("tune", [0, 16, 50], ids=["auto", "bm16", "bm50"])
+@pytest.mark.parametrize("p", [P(8, 56, 56, 64, 256, 1, 1), P(3, 17, 13, 40, 72, 1, 1),
+                               P(4, 20, 20, 56, 128, 1, 1, dtype="bf16"),
+                               P(2, 10, 10, 32, 520, 1, 1)], ids=ident)
+def test_pointwise_persistent_matches_ring(p, tune):
+    """The persistent pointwise kernel (several tiles per block at small tile
+    heights, ragged last tile, K % 64 != 0, C below the tile width, the
+    shallower ring beside a large filter) against the one-tile-per-block ring
+    kernel, bit for bit."""
+    ab, _, wb, _ = operands(p, "dgrad", 109)
+    with api.override(tune=tune):
+        pers = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    with api.override(tune=1):
+        ring = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    assert np.array_equal(pers.view(np.uint16), ring.view(np.uint16))
+
+
 def test_reproducible_bitwise():
     p = P(2, 14, 14, 64, 128, 3, 3, 2, 1, 1)
     ab, _, wb, _ = operands(p, "dgrad", 105)
