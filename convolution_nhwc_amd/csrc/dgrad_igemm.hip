@@ -1,7 +1,10 @@
 // Backward-data convolution as implicit GEMMs on the gfx950 matrix cores:
 // a ring kernel (both operands streamed per reduction step; also the 1x1
-// pointwise fast path, as a compile-time specialisation) and a dY-window
-// kernel for stride-1 problems whose filters have two or more taps.
+// pointwise fast path, as a compile-time specialisation), a dY-window kernel
+// for stride-1 problems whose filters have two or more taps, and two
+// pointwise kernels for narrow dX (C <= 64) that keep the filter on chip: a
+// row-streamed one (K = 64..256 in steps of 64) and an LDS-persistent one.
+// All pointwise paths produce the same bits as the general ring kernel.
 //
 // Strided dgrad splits dX into stride*stride phase classes (h mod s, w mod s)
 // -- the "tilde" decomposition of "perf(rocke/conv): add the pointwise fast
@@ -673,6 +676,216 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_pw_persist_kernel(const PwA
 }
 
 // ---------------------------------------------------------------------------
+// Pointwise (1x1) dgrad for C <= 64 and K in {64, 128, 192, 256}: per-wave
+// row streaming.
+//
+// Same fragments and the same ascending 32-deep MFMA chain per output as the
+// ring kernel (bit-identical results); the schedule is built around HBM
+// access: every dY load instruction reads 1 KiB of contiguous memory (whole
+// pixel rows), which streams markedly faster than the 128-byte row slices a
+// 64-deep step of a wide tile touches.
+//   * The filter (K x 64 channels) is loaded once per block and each wave
+//     keeps all of it in registers as MFMA operand fragments.
+//   * Each wave owns a contiguous run of M / waves pixels and walks it in
+//     blocks of 16 pixels (16 whole dY rows, contiguous in memory) through a
+//     private LDS ring: asynchronous loads write the rows straight into LDS,
+//     several blocks ahead, with the 16-byte chunks of a row XOR-ed by
+//     row & 7 (the permutation is applied to the source addresses, so the
+//     loads stay contiguous) so the fragment reads are conflict-free.  No
+//     other wave touches the ring: no barriers in the loop.
+//   * A finished block is staged (rounded) in the slot it has just consumed
+//     and written back as contiguous 16-byte runs of dX rows.
+struct PwrArgs {
+    const void* dy;
+    const void* w;
+    void* dx;
+    uint32_t dy_bytes, w_bytes, dx_bytes;
+    int M, C, K;       // pixels, channels of dX (<= 64, multiple of 8), channels of dY (64*KC)
+    int nwaves;        // waves in the grid
+};
+
+template <typename T, int KC, int WAVES>
+__global__ __launch_bounds__(WAVES * 64, 1) void dgrad_pw_rows_kernel(const PwrArgs a) {
+    constexpr int WNB = 4;                           // 64 channels: 4 MFMA column blocks
+    constexpr int CPR = KC * 8;                      // 16-byte chunks per dY row
+    constexpr int SLOT = 16 * CPR * 16;              // one 16-pixel block of dY rows
+    constexpr int LPB = SLOT / 1024;                 // async loads per lane per block
+    constexpr int W_BYTES = KC * kBK * kPwBN * 2;
+    constexpr int NBF = (kPwLds - W_BYTES) / (WAVES * SLOT);
+    constexpr int NB = NBF < 16 ? NBF : 16;          // ring slots per wave
+    constexpr int RING = NB * SLOT;
+    static_assert(NB >= 2, "ring depth");
+    static_assert(W_BYTES + WAVES * RING <= kPwLds, "LDS");
+    static_assert((NB - 1) * LPB < 64, "vmcnt range");
+    static_assert(RING < 65536, "slot offsets fit the LDS immediate");
+    static_assert(SLOT >= 16 * 128, "a slot holds the staged output block");
+    __shared__ __attribute__((aligned(16))) unsigned char lds[W_BYTES + WAVES * RING];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int frow = lane & 15, fgrp = lane >> 4;
+    const int gw = blockIdx.x * WAVES + wave;
+    const int r0 = int(int64_t(a.M) * gw / a.nwaves);
+    const int r1 = int(int64_t(a.M) * (gw + 1) / a.nwaves);
+    const int nblk = (r1 - r0 + 15) / 16;
+
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
+    unsigned char* ring = lds + W_BYTES + wave * RING;
+    const uint32_t ring0 = lds_addr(ring);
+
+    // ---- filter -> LDS: 1 KiB regions of 8 k-rows, chunks swizzled as in a
+    // W stage; channels past C read as zeros ----
+#pragma unroll
+    for (int q = wave; q < KC * 8; q += WAVES) {
+        const int row = 8 * q + (lane >> 3);
+        const int chunk = (lane & 7) ^ swz_b<8>(row);
+        const uint32_t v = chunk * 8 < a.C ? uint32_t((row * a.C + chunk * 8) * 2) : kOob;
+        dma16(rw, lds + q * 1024, v, 0);
+    }
+
+    // ---- dY block loads: load D of a block covers 1 KiB; lane l takes
+    // element e = 64*D + l of the block (row e / CPR, stored chunk e % CPR,
+    // holding source chunk (e % CPR) ^ (row & 7)) ----
+    uint32_t a_voff[LPB];
+    int a_row[LPB];
+#pragma unroll
+    for (int d = 0; d < LPB; ++d) {
+        const int e = 64 * d + lane;
+        const int r = e / CPR, p = e % CPR;
+        a_row[d] = r;
+        a_voff[d] = uint32_t((r * a.K + ((p ^ (r & 7)) * 8)) * 2);
+    }
+    auto issue = [&](auto slot, int blk) {
+        constexpr int SL = decltype(slot)::value;
+        (void)a_voff; (void)a_row;
+        const int m0 = r0 + blk * 16;
+        const int lim = r1 - m0;
+        const uint32_t soff = uint32_t(m0) * uint32_t(a.K) * 2u;
+#pragma unroll
+        for (int d = 0; d < LPB; ++d)
+            dma16(rdy, ring + SL * SLOT + d * 1024, a_row[d] < lim ? a_voff[d] : kOob, soff);
+    };
+    sfor<NB - 1>([&](auto sc) { issue(sc, decltype(sc)::value); });
+
+    // ---- filter fragments -> registers: lane (frow, fgrp) of fragment
+    // (kc, ks, j) holds channel j*16 + frow, k-rows kc*64 + ks*32 + fgrp*8 .. +7 ----
+    wait_vm<(NB - 1) * LPB>();
+    __builtin_amdgcn_s_barrier();
+    i32x4 wr[KC][2][WNB];
+    {
+        const uint32_t lds0 = lds_addr(lds);
+        sfor<KC>([&](auto kcc) {
+            constexpr int KCI = decltype(kcc)::value;
+            (void)wr;
+            i32x2 h[2][WNB][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < WNB; ++j)
+#pragma unroll
+                    for (int hh = 0; hh < 2; ++hh) {
+                        const int k = ks * 32 + fgrp * 8 + 4 * hh + (frow >> 2);
+                        const int c = j * 16 + 4 * (frow & 3);
+                        const uint32_t addr = lds0 + (KCI * kBK + k) * (kPwBN * 2) +
+                                              (((c >> 3) ^ swz_b<8>(k)) << 4) + (c & 7) * 2;
+                        asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(h[ks][j][hh]) : "v"(addr));
+                    }
+            asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int j = 0; j < WNB; ++j) {
+                    asm volatile("" : "+v"(h[ks][j][0]), "+v"(h[ks][j][1]));
+                    wr[KCI][ks][j] = i32x4{h[ks][j][0][0], h[ks][j][0][1], h[ks][j][1][0], h[ks][j][1][1]};
+                }
+        });
+    }
+
+    // fragment read addresses: lane (frow, fgrp) of half ks reads row frow,
+    // chunk kc*8 + ks*4 + fgrp (stored at chunk ^ (frow & 7))
+    uint32_t fa_addr[2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks)
+        fa_addr[ks] = ring0 + frow * (CPR * 16) + (((ks * 4 + fgrp) ^ (frow & 7)) << 4);
+    // output staging: lane (frow, fgrp) writes channels j*16 + fgrp*4 .. +3 of
+    // pixel frow into 128-byte rows (16-byte chunks XOR-ed by row & 7) ...
+    uint32_t st_addr[WNB];
+#pragma unroll
+    for (int j = 0; j < WNB; ++j)
+        st_addr[j] = ring0 + frow * 128 + (((2 * j + (fgrp >> 1)) ^ (frow & 7)) << 4) + (fgrp & 1) * 8;
+    // ... and reads back 16-byte chunk e = 64*d + lane of the block's
+    // contiguous dX rows (row e / (C/8), chunk e % (C/8))
+    const int cc = a.C / 8;
+    uint32_t ld_addr[2];
+    int ld_row[2], ld_e[2];
+#pragma unroll
+    for (int d = 0; d < 2; ++d) {
+        const int e = 64 * d + lane;
+        const bool used = e < 16 * cc;
+        const int r = used ? e / cc : 0, ch = used ? e % cc : 0;
+        ld_e[d] = used ? e : -1;
+        ld_row[d] = r;
+        ld_addr[d] = ring0 + r * 128 + ((ch ^ (r & 7)) << 4);
+    }
+
+    auto block_fn = [&](auto slot, int blk) {
+        constexpr int SL = decltype(slot)::value;
+        (void)fa_addr; (void)st_addr; (void)ld_addr; (void)ld_row; (void)ld_e; (void)wr;
+        issue(IC<(SL + NB - 1) % NB>{}, blk + NB - 1);
+        wait_vm<(NB - 1) * LPB>();
+        i32x4 af[KC][2];
+        sfor<KC>([&](auto kcc) {
+            constexpr int KCI = decltype(kcc)::value;
+            (void)af; (void)fa_addr;
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+                asm volatile("ds_read_b128 %0, %1 offset:%2"
+                             : "=v"(af[KCI][ks]) : "v"(fa_addr[ks]), "i"(SL * SLOT + KCI * 128));
+        });
+        f32x4 acc[WNB];
+#pragma unroll
+        for (int j = 0; j < WNB; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        sfor<2 * KC>([&](auto xc) {
+            constexpr int X = decltype(xc)::value, KCI = X / 2, KS = X % 2;
+            (void)af; (void)acc; (void)wr;
+            asm volatile("s_waitcnt lgkmcnt(%1)" : "+v"(af[KCI][KS]) : "i"(2 * KC - 1 - X));
+#pragma unroll
+            for (int j = 0; j < WNB; ++j)
+                acc[j] = mfma16x16x32<T>(wr[KCI][KS][j], af[KCI][KS], acc[j]);
+        });
+        // round, stage in this slot, store contiguous dX rows
+#pragma unroll
+        for (int j = 0; j < WNB; ++j) {
+            const i32x2 v = {int(pack2<T>(acc[j][0], acc[j][1])), int(pack2<T>(acc[j][2], acc[j][3]))};
+            asm volatile("ds_write_b64 %0, %1 offset:%2" :: "v"(st_addr[j]), "v"(v), "i"(SL * SLOT));
+        }
+        const int m0 = r0 + blk * 16;
+        const int lim = r1 - m0;
+        i32x4 o[2];
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+            asm volatile("ds_read_b128 %0, %1 offset:%2" : "=v"(o[d]) : "v"(ld_addr[d]), "i"(SL * SLOT));
+        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(o[0]), "+v"(o[1]));
+#pragma unroll
+        for (int d = 0; d < 2; ++d)
+            if (ld_e[d] >= 0 && ld_row[d] < lim)
+                buf_store16(o[d], rdx, uint32_t((m0 * a.C + ld_e[d] * 8) * 2));
+    };
+
+#pragma unroll 1
+    for (int b0 = 0; b0 < nblk; b0 += NB) {
+        sfor<NB>([&](auto pc) {
+            constexpr int P = decltype(pc)::value;
+            if (b0 + P < nblk) block_fn(IC<P>{}, b0 + P);
+        });
+    }
+    wait_vm<0>();   // loads issued past the last block still target LDS
+}
+
+// ---------------------------------------------------------------------------
 // General dgrad with the dY operand staged as an LDS window (classes with at
 // least two filter taps).
 //
@@ -1117,6 +1330,39 @@ int pw_stages(int64_t k) {
     return 0;
 }
 
+constexpr int kPwrWaves = 8;   // waves per block (two per SIMD)
+template <typename T>
+void launch_pwr_kc(int kc, const PwrArgs& a, int blocks, hipStream_t st) {
+    constexpr int W = kPwrWaves;
+    if (kc == 1) hipLaunchKernelGGL((dgrad_pw_rows_kernel<T, 1, W>), dim3(blocks), dim3(W * 64), 0, st, a);
+    else if (kc == 2) hipLaunchKernelGGL((dgrad_pw_rows_kernel<T, 2, W>), dim3(blocks), dim3(W * 64), 0, st, a);
+    else if (kc == 3) hipLaunchKernelGGL((dgrad_pw_rows_kernel<T, 3, W>), dim3(blocks), dim3(W * 64), 0, st, a);
+    else hipLaunchKernelGGL((dgrad_pw_rows_kernel<T, 4, W>), dim3(blocks), dim3(W * 64), 0, st, a);
+}
+
+bool pw_rows_ok(const Prob& p) {
+    return p.c <= kPwBN && p.c % 8 == 0 && p.k % kBK == 0 && p.k <= 4 * kBK;
+}
+
+// Row-streamed pointwise launch: one block per CU (at most), each wave over
+// an equal run of pixels (at least 16 for small M).
+int launch_pw_rows(const Prob& p, const void* dy, const void* w, void* dx, hipStream_t st) {
+    PwrArgs a{};
+    a.dy = dy; a.w = w; a.dx = dx;
+    a.M = int(p.n * p.h * p.w);
+    a.C = int(p.c); a.K = int(p.k);
+    a.dy_bytes = uint32_t(int64_t(a.M) * a.K * 2);
+    a.w_bytes = uint32_t(int64_t(a.K) * a.C * 2);
+    a.dx_bytes = uint32_t(int64_t(a.M) * a.C * 2);
+    if (a.M <= 0) return CNHWC_OK;
+    const int blocks = int(std::min<int64_t>(kNumCUs, (a.M + 16 * kPwrWaves - 1) / (16 * kPwrWaves)));
+    a.nwaves = blocks * kPwrWaves;
+    const int kc = a.K / kBK;
+    if (p.dtype == CNHWC_BF16) launch_pwr_kc<BF16>(kc, a, blocks, st);
+    else launch_pwr_kc<F16>(kc, a, blocks, st);
+    return CNHWC_OK;
+}
+
 // Persistent pointwise launch: one block per CU; tile height chosen so the
 // tiles spread most evenly over the blocks.
 int launch_pw_persist(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
@@ -1315,10 +1561,14 @@ int launch_dgrad_halo(const Prob& p, const void* dy, const void* w, void* dx, hi
 int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
                        hipStream_t st) {
     const bool pw = pl.variant == CNHWC_VAR_DGRAD_POINTWISE;
-    // pointwise with C <= 64 and a filter that fits LDS: the persistent
-    // kernel (tune 1 asks for the ring kernel)
-    if (pw && pl.tune != 1 && p.c <= kPwBN && pw_stages(p.k) > 0)
-        return launch_pw_persist(p, pl, dy, w, dx, st);
+    // pointwise with C <= 64: the row-streamed kernel for K = 64..256 in
+    // steps of 64, else the LDS-persistent kernel while the filter fits LDS
+    // (tune 1 asks for the ring kernel, tune 3 or >= 16 for the LDS-persistent
+    // one)
+    if (pw && pl.tune != 1 && p.c <= kPwBN) {
+        if (pw_rows_ok(p) && pl.tune != 3 && pl.tune < 16) return launch_pw_rows(p, dy, w, dx, st);
+        if (pw_stages(p.k) > 0) return launch_pw_persist(p, pl, dy, w, dx, st);
+    }
     // Stride 1: classes with two or more taps go to the window kernel, the
     // rest (and the pointwise fast path) to the ring kernel below.  Strided
     // problems split into several classes of few taps each, where the window

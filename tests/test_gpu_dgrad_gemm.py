@@ -26,6 +26,8 @@ POINTWISE = [
     P(3, 17, 13, 136, 72, 1, 1),          # C and K not multiples of the tiles
     P(1, 8, 8, 16, 16, 1, 1, dtype="bf16"),
     P(2, 20, 20, 192, 40, 1, 1, dtype="bf16"),
+    P(2, 13, 11, 40, 128, 1, 1),          # row-streamed kernel, C < 64
+    P(1, 7, 9, 64, 192, 1, 1, dtype="bf16"),
 ]
 
 
@@ -88,15 +90,18 @@ def test_pointwise_bit_identical_to_general(p):
     assert np.array_equal(fast.view(np.uint16), gen.view(np.uint16))
 
 
-@pytest.mark.parametrize("tune", [0, 16, 50], ids=["auto", "bm16", "bm50"])
+@pytest.mark.parametrize("tune", [0, 3, 16, 50], ids=["auto", "lds", "bm16", "bm50"])
 @pytest.mark.parametrize("p", [P(8, 56, 56, 64, 256, 1, 1), P(3, 17, 13, 40, 72, 1, 1),
                                P(4, 20, 20, 56, 128, 1, 1, dtype="bf16"),
-                               P(2, 10, 10, 32, 520, 1, 1)], ids=ident)
+                               P(2, 10, 10, 32, 520, 1, 1), P(1, 5, 7, 8, 64, 1, 1),
+                               P(3, 11, 9, 24, 192, 1, 1), P(1, 1, 3, 64, 256, 1, 1)], ids=ident)
 def test_pointwise_persistent_matches_ring(p, tune):
-    """The persistent pointwise kernel (several tiles per block at small tile
-    heights, ragged last tile, K % 64 != 0, C below the tile width, the
-    shallower ring beside a large filter) against the one-tile-per-block ring
-    kernel, bit for bit."""
+    """The row-streamed pointwise kernel (auto for K = 64..256 in steps of 64:
+    runs of pixels per wave with ragged last blocks, C from 8 to 64, tiny M)
+    and the LDS-persistent one (tune 3 or a tile height; several tiles per
+    block at small heights, ragged last tile, K % 64 != 0, the shallower ring
+    beside a large filter) against the one-tile-per-block ring kernel, bit for
+    bit."""
     ab, _, wb, _ = operands(p, "dgrad", 109)
     with api.override(tune=tune):
         pers = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
