@@ -520,6 +520,177 @@ __global__ __launch_bounds__(kThreads) void fwd_grouped_kernel(const GrpArgs a) 
     }
 }
 
+// ---- grouped merge, whole-pixel-row variant ---------------------------------
+// Same MFMA problem per group set as fwd_grouped_kernel (32 merged input
+// channels x G_m*Kg outputs, block-diagonal weights), organised around HBM
+// access: a block owns TH x TW output pixels of one image for ALL channels,
+// so its input halo arrives as whole pixel rows (C*2 contiguous bytes per
+// pixel, 1 KiB per load instruction) instead of 64-byte slices, and its
+// output leaves as whole rows.  Eight waves; wave w computes group sets w,
+// w+8, ...; each holds its set's block-diagonal weight fragments in registers
+// (loaded straight from the filter as stored: lanes whose 8 merged channels
+// belong to another group read out of range, i.e. zeros) and reads the
+// input fragments from the halo (16-byte chunks XOR-ed by pixel & 15, or & 7
+// for rows of fewer chunks, applied to the source addresses).  Results are rounded into an output tile in LDS
+// and stored as contiguous rows at the end.
+constexpr int kGrThreads = 512;
+
+struct GrowArgs {
+    const void* x;
+    const void* w;
+    void* y;
+    uint32_t x_bytes, w_bytes, y_bytes;
+    int N, H, W, C, K, stride, pad_h, pad_w, Ho, Wo, Cg, Kg;
+    int bn, gsets;                // outputs per group set, group sets
+    int TH, TW, IH, IW;           // output tile, input halo
+    int ptiles_h, ptiles_w;       // tiles per image
+    int halo_bytes;               // LDS of the halo (whole 1 KiB loads)
+    int hmask, omask;             // chunk swizzle masks: 15 when a row has 16k chunks, else 7
+    FastDiv fd_cpr, fd_iw, fd_tw, fd_kc;   // division by C/8, IW, TW, K/8
+};
+
+template <typename T, int BN, int R, int S>
+__global__ __launch_bounds__(kGrThreads, 1) void fwd_grouped_rows_kernel(const GrowArgs a) {
+    constexpr int TAPS = R * S, FM = kBM / 16, FN = BN / 16;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char* hs = lds;                       // halo [pixel][C]
+    unsigned char* os = lds + a.halo_bytes;        // output tile [pixel][K]
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int per_img = a.ptiles_h * a.ptiles_w;
+    const int n = blockIdx.x / per_img;
+    const int pt = blockIdx.x - n * per_img;
+    const int ho0 = (pt / a.ptiles_w) * a.TH, wo0 = (pt % a.ptiles_w) * a.TW;
+    const int s = a.stride;
+    const int cpr = a.C / 8;                       // 16-byte chunks per input pixel
+
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
+
+    // ---- halo: element e = pixel * cpr + stored chunk, holding source chunk
+    // (stored ^ (pixel & 7)); pixels outside the image read zeros ----
+    const int hchunks = a.IH * a.IW * cpr;
+    for (int e0 = wave * 64; e0 < hchunks; e0 += kGrThreads) {
+        const int e = e0 + lane;
+        const int hp = fdiv(e, a.fd_cpr);
+        const int sc = (e - hp * cpr) ^ (hp & a.hmask);
+        const int ih = fdiv(hp, a.fd_iw), iw = hp - ih * a.IW;
+        const int h = ho0 * s - a.pad_h + ih, w = wo0 * s - a.pad_w + iw;
+        uint32_t off = kOob;
+        if (e < hchunks && h >= 0 && h < a.H && w >= 0 && w < a.W)
+            off = uint32_t(((n * a.H + h) * a.W + w) * a.C + sc * 8) * 2u;
+        dma16(rx, hs + e0 * 16, off, 0);
+    }
+
+    const int frow = lane & 15, fgrp = lane >> 4;
+    const int tile_pix = a.TH * a.TW;
+    int hbase[FM];
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+        int m = i * 16 + frow;
+        if (m >= tile_pix) m = 0;
+        const int th = fdiv(m, a.fd_tw), tw = m - th * a.TW;
+        hbase[i] = th * s * a.IW + tw * s;
+    }
+    // weight fragments of a set: lane (frow, fgrp) of fragment (tap, j) holds
+    // output channel j*16 + frow of the set against merged channels
+    // fgrp*8 .. +7, zero unless those belong to that output's group
+    auto load_w = [&](int gs, i32x4 (&wf)[TAPS][FN]) {
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+            const int kk = j * 16 + frow;
+            const bool own = kk < a.bn && (fgrp * 8) / a.Cg == kk / a.Kg;
+            const uint32_t base = uint32_t(((gs * a.bn + kk) * TAPS) * a.Cg + (fgrp * 8) % a.Cg) * 2u;
+#pragma unroll
+            for (int tap = 0; tap < TAPS; ++tap)
+                wf[tap][j] = buf_load16(rw, own ? base + uint32_t(tap * a.Cg * 2) : kOob);
+        }
+    };
+
+    i32x4 wf[TAPS][FN];
+    if (wave < a.gsets) load_w(wave, wf);
+    wait_vm<0>();
+    __syncthreads();
+
+    const int out_cpr = a.K / 8;                   // 16-byte chunks per output pixel
+#pragma unroll 1
+    for (int gs = wave; gs < a.gsets; gs += kGrThreads / 64) {
+        if (gs != wave) load_w(gs, wf);
+        // opaque per set: keeps the per-(tap, row block) read addresses from
+        // being hoisted out of the set loop (they would hold 72+ registers)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) asm volatile("" : "+v"(hbase[i]));
+        f32x4 acc[FM][FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+            for (int j = 0; j < FN; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+        // input fragments of a tap: all FM row blocks (rows past the tile read
+        // pixel 0 and are never stored), double-buffered: the reads of tap t+1
+        // are issued between the products of tap t
+        i32x4 fa[2][FM];
+        const uint32_t hs0 = lds_addr(hs);
+        auto read_tap = [&](auto bufc, auto tapc, auto ic) {
+            constexpr int B = decltype(bufc)::value, TP = decltype(tapc)::value, I = decltype(ic)::value;
+            (void)fa; (void)hbase;
+            const int hp = hbase[I] + (TP / S) * a.IW + TP % S;
+            const uint32_t addr = hs0 + uint32_t(hp * (cpr * 16)) + uint32_t(((gs * 4 + fgrp) ^ (hp & a.hmask)) << 4);
+            asm volatile("ds_read_b128 %0, %1" : "=v"(fa[B][I]) : "v"(addr));
+        };
+        auto wait_fa = [&](auto bufc) {
+            constexpr int B = decltype(bufc)::value;
+            asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[B][0]));
+#pragma unroll
+            for (int i = 1; i < FM; ++i) asm volatile("" : "+v"(fa[B][i]));
+        };
+        sfor<FM>([&](auto ic) { read_tap(IC<0>{}, IC<0>{}, ic); });
+        wait_fa(IC<0>{});
+        sfor<TAPS>([&](auto tapc) {
+            constexpr int TP = decltype(tapc)::value, B = TP & 1;
+            (void)fa; (void)acc; (void)wf;
+            sfor<FM * FN>([&](auto mc) {
+                constexpr int M = decltype(mc)::value, I = M / FN, J = M % FN;
+                acc[I][J] = mfma16x16x32<T>(wf[TP][J], fa[B][I], acc[I][J]);
+                if constexpr (TP + 1 < TAPS && M % FN == 0) read_tap(IC<B ^ 1>{}, IC<TP + 1>{}, IC<I>{});
+                __builtin_amdgcn_sched_barrier(0);
+            });
+            if constexpr (TP + 1 < TAPS) wait_fa(IC<B ^ 1>{});
+        });
+        // round into the output tile: pixel m, channels gs*bn + j*16 + fgrp*4 .. +3
+        // (16-byte chunk index XOR-ed by m & 15, or & 7)
+#pragma unroll
+        for (int i = 0; i < FM; ++i) {
+            const int m = i * 16 + frow;
+            if (m < tile_pix) {
+#pragma unroll
+                for (int j = 0; j < FN; ++j) {
+                    const int col = gs * a.bn + j * 16 + fgrp * 4;
+                    if (j * 16 < a.bn) {
+                        const i32x2 v = {int(pack2<T>(acc[i][j][0], acc[i][j][1])),
+                                         int(pack2<T>(acc[i][j][2], acc[i][j][3]))};
+                        *reinterpret_cast<i32x2*>(os + m * (out_cpr * 16) + (((col >> 3) ^ (m & a.omask)) << 4) +
+                                                  (col & 7) * 2) = v;
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+    // ---- store whole output rows: element e = pixel * out_cpr + chunk ----
+    const int ochunks = tile_pix * out_cpr;
+    for (int e = tid; e < ochunks; e += kGrThreads) {
+        const int m = fdiv(e, a.fd_kc);
+        const int c = e - m * out_cpr;
+        const int th = fdiv(m, a.fd_tw), tw = m - th * a.TW;
+        const int ho = ho0 + th, wo = wo0 + tw;
+        if (ho >= a.Ho || wo >= a.Wo) continue;
+        const i32x4 v = *reinterpret_cast<const i32x4*>(os + m * (out_cpr * 16) + ((c ^ (m & a.omask)) << 4));
+        buf_store16(v, ry, uint32_t(((n * a.Ho + ho) * a.Wo + wo) * a.K + c * 8) * 2u);
+    }
+}
+
 // Tile geometry: up to 128 output pixels as NB whole images or TH x TW rows,
 // with a halo of at most `halo_max` pixels.
 bool pick_geo(const Prob& p, int halo_max, Geo* g) {
@@ -697,8 +868,83 @@ int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* 
     return CNHWC_OK;
 }
 
-int launch_fwd_grouped(const Prob& p, const Plan&, const void* x, const void* w, void* y,
+// Whole-row grouped variant: tile geometry (one image, TH x TW <= 128 output
+// pixels, halo + output tile within LDS) or false when it does not apply.
+static bool grow_geometry(const Prob& p, GrowArgs* a, size_t* lds) {
+    int gm, bn;
+    if (!grouped_shape(p, &gm, &bn)) return false;
+    if (p.cg % 8 != 0 || p.c % 64 != 0 || p.k % 64 != 0) return false;
+    const bool t9 = p.r == 3 && p.s == 3, t1 = p.r == 1 && p.s == 1;
+    if (!(t9 && bn <= 32) && !t1) return false;
+    const int64_t s = p.stride;
+    int64_t TW = std::min<int64_t>(p.wo, kBM), TH = std::max<int64_t>(1, std::min<int64_t>(p.ho, kBM / TW));
+    auto need = [&](int64_t th, int64_t tw) {
+        const int64_t ih = (th - 1) * s + p.r, iw = (tw - 1) * s + p.s;
+        const int64_t halo = (ih * iw * (p.c / 8) + 63) / 64 * 1024;
+        return std::make_pair(halo, halo + th * tw * p.k * 2);
+    };
+    while (TH > 1 && need(TH, TW).second > 160 * 1024) --TH;
+    while (TW > 8 && need(TH, TW).second > 160 * 1024) TW -= 8;
+    if (need(TH, TW).second > 160 * 1024) return false;
+    a->TH = int(TH); a->TW = int(TW);
+    a->IH = int((TH - 1) * s + p.r); a->IW = int((TW - 1) * s + p.s);
+    a->ptiles_h = int((p.ho + TH - 1) / TH);
+    a->ptiles_w = int((p.wo + TW - 1) / TW);
+    a->halo_bytes = int(need(TH, TW).first);
+    a->bn = bn;
+    a->gsets = p.groups / gm;
+    *lds = size_t(need(TH, TW).second);
+    return true;
+}
+
+static int launch_fwd_grouped_rows(const Prob& p, const void* x, const void* w, void* y, hipStream_t st) {
+    GrowArgs a{};
+    size_t lds = 0;
+    if (!grow_geometry(p, &a, &lds)) return CNHWC_UNSUPPORTED;
+    a.x = x; a.w = w; a.y = y;
+    a.x_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
+    a.w_bytes = uint32_t(p.k * p.r * p.s * p.cg * 2);
+    a.y_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
+    a.N = int(p.n); a.H = int(p.h); a.W = int(p.w); a.C = int(p.c); a.K = int(p.k);
+    a.stride = p.stride; a.pad_h = p.pad_h; a.pad_w = p.pad_w;
+    a.Ho = int(p.ho); a.Wo = int(p.wo); a.Cg = int(p.cg); a.Kg = int(p.kg);
+    a.fd_cpr = make_fastdiv(uint32_t(p.c / 8));
+    a.fd_iw = make_fastdiv(uint32_t(a.IW));
+    a.fd_tw = make_fastdiv(uint32_t(a.TW));
+    a.fd_kc = make_fastdiv(uint32_t(p.k / 8));
+    a.hmask = (p.c / 8) % 16 == 0 ? 15 : 7;
+    a.omask = (p.k / 8) % 16 == 0 ? 15 : 7;
+    const int64_t blocks = p.n * a.ptiles_h * a.ptiles_w;
+    const bool bf = p.dtype == CNHWC_BF16;
+    const void* fn;
+    void (*launch)(const GrowArgs&, int64_t, size_t, hipStream_t);
+#define CNHWC_GROW(T, BN, R, S)                                                                  \
+    fn = reinterpret_cast<const void*>(&fwd_grouped_rows_kernel<T, BN, R, S>);                   \
+    launch = [](const GrowArgs& g, int64_t nb, size_t l, hipStream_t q) {                        \
+        hipLaunchKernelGGL((fwd_grouped_rows_kernel<T, BN, R, S>), dim3(nb), dim3(kGrThreads), l, q, g); \
+    };
+    if (p.r == 3) {
+        if (bf) { CNHWC_GROW(BF16, 32, 3, 3) } else { CNHWC_GROW(F16, 32, 3, 3) }
+    } else if (a.bn <= 32) {
+        if (bf) { CNHWC_GROW(BF16, 32, 1, 1) } else { CNHWC_GROW(F16, 32, 1, 1) }
+    } else {
+        if (bf) { CNHWC_GROW(BF16, 64, 1, 1) } else { CNHWC_GROW(F16, 64, 1, 1) }
+    }
+#undef CNHWC_GROW
+    if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+        return CNHWC_HIP_ERROR;
+    launch(a, blocks, lds, st);
+    return CNHWC_OK;
+}
+
+int launch_fwd_grouped(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                        hipStream_t st) {
+    // whole-row variant where it applies (tune 1 asks for the group-set kernel)
+    if (pl.tune != 1) {
+        GrowArgs g{};
+        size_t lds = 0;
+        if (grow_geometry(p, &g, &lds)) return launch_fwd_grouped_rows(p, x, w, y, st);
+    }
     GrpArgs a{};
     if (!pick_geo(p, kGHaloMax, &a.geo)) return CNHWC_UNSUPPORTED;
     if (!grouped_shape(p, &a.gm, &a.bn)) return CNHWC_UNSUPPORTED;

@@ -81,13 +81,22 @@ GROUPED = [
     P(1, 9, 9, 64, 64, 5, 5, 1, 2, 2, groups=4),       # Cg 16: 2 merged
     P(1, 11, 13, 64, 32, 3, 1, 1, 1, 0, groups=2),     # Cg 32: no merge
     P(2, 8, 8, 64, 64, 3, 3, 1, 1, 1, groups=8, dtype="f16"),
+    P(2, 13, 11, 64, 64, 3, 3, 2, 1, 1, groups=8),     # whole-row kernel, stride 2
+    P(1, 10, 10, 128, 128, 1, 1, 1, 0, 0, groups=8),   # whole-row kernel, 1x1, Cg 16
+    P(1, 15, 13, 64, 128, 1, 1, 1, 0, 0, groups=4),    # whole-row kernel, 1x1, 64 wide
+    P(1, 8, 8, 512, 512, 3, 3, 1, 1, 1, groups=64),    # whole-row kernel, 16 sets over 8 waves
+    P(1, 30, 9, 128, 128, 3, 3, 1, 1, 0, groups=16, dtype="f16"),  # whole-row kernel, two row tiles
 ]
 
 
+@pytest.mark.parametrize("tune", [0, 1], ids=["auto", "setkernel"])
 @pytest.mark.parametrize("p", GROUPED, ids=ident)
-def test_grouped_merge_parity(p):
+def test_grouped_merge_parity(p, tune):
+    """Both grouped kernels: the whole-row one (auto, where it applies) and the
+    group-set one (tune 1, every shape)."""
     assert api.cnhwc_plan(p, api.OP_FWD)[1] == api.VAR_FWD_GROUPED
-    parity(p, "fwd", 204)
+    with api.override(tune=tune):
+        parity(p, "fwd", 204)
 
 
 @pytest.mark.parametrize("p,var", [(P(2, 7, 7, 128, 64, 3, 3, 1, 1, 1), api.VAR_FWD_DIRECT),
