@@ -768,6 +768,9 @@ __global__ __launch_bounds__(WAVES * 64, 1) void dgrad_pw_rows_kernel(const PwrA
         for (int d = 0; d < LPB; ++d)
             dma16(rdy, ring + SL * SLOT + d * 1024, a_row[d] < lim ? a_voff[d] : kOob, soff);
     };
+    // every wave's filter loads go out before any dY block load, so the
+    // filter (needed first, by all waves) is not queued behind dY blocks
+    __builtin_amdgcn_s_barrier();
     sfor<NB - 1>([&](auto sc) { issue(sc, decltype(sc)::value); });
 
     // ---- filter fragments -> registers: lane (frow, fgrp) of fragment

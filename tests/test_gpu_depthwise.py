@@ -73,6 +73,8 @@ TILED = [
     DW(2, 23, 17, 32, 5, 5, 1, 2, 2),
     DW(1, 12, 31, 24, 5, 5, 1, 4, 0),          # pad > R-1 on one axis
     DW(1, 20, 22, 64, 7, 7, 1, 3, 3),
+    DW(1, 9, 33, 200, 3, 3, 1, 1, 1),          # several channel blocks, ragged last block
+    DW(1, 13, 29, 136, 7, 7, 1, 3, 3, dtype="bf16"),
     DW(1, 9, 12, 16, 7, 7, 1, 2, 5),           # short image, odd pads
     DW(1, 5, 6, 8, 7, 7, 1, 3, 3),             # image smaller than the filter
     DW(2, 19, 29, 64, 3, 3, 1, 1, 1, dtype="bf16"),
