@@ -457,6 +457,7 @@ constexpr int kRotTHT = 2;     // output rows per lane
 constexpr int kRotTWT = 8;     // output columns per lane
 constexpr int kRotTB = 8;      // filter columns per register slice
 constexpr int kRotMaxF = 64;   // largest filter side
+constexpr int kRotSplit = 2;   // lane groups splitting the filter steps of a tile
 
 struct RotArgs {
     const void* dy;
@@ -474,11 +475,13 @@ struct RotArgs {
 
 // Block: 256 lanes = 4 channel pairs x 4 column groups (8 columns) x 16 row
 // groups (2 rows): a 32 x 32 x 8 output tile.
-template <typename T>
-__global__ __launch_bounds__(256, 1) void dw_rotated_kernel(const RotArgs a) {
+template <typename T, int SPLIT>
+__global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
+    constexpr int NT = 256 * SPLIT;
     const int tid = threadIdx.x;
-    const int cp = tid & 3, cg = (tid >> 2) & 3, rg = tid >> 4;
+    const int lt = tid & 255, grp = tid >> 8;      // lane role within its group; tap group
+    const int cp = lt & 3, cg = (lt >> 2) & 3, rg = lt >> 4;
     int bid = blockIdx.x;
     const int cb = bid % a.cblocks;
     bid /= a.cblocks;
@@ -496,7 +499,7 @@ __global__ __launch_bounds__(256, 1) void dw_rotated_kernel(const RotArgs a) {
     // word layout: [row][col][4 channel pairs], row stride a.row_dw words
     uint32_t* win = smem;
     const int npix = a.IHB * a.IWB;
-    for (int q = tid; q < npix; q += 256) {
+    for (int q = tid; q < npix; q += NT) {
         const int ih = q / a.IWB, iw = q - (q / a.IWB) * a.IWB;
         const int u = h0 - a.ph2 + ih, v = w0 - a.pw2 + iw;
         uint32_t off = kOob;
@@ -509,7 +512,7 @@ __global__ __launch_bounds__(256, 1) void dw_rotated_kernel(const RotArgs a) {
     uint32_t* wpl = smem + a.IHB * a.row_dw;
     const int tpad = a.tslices * kRotTB;
     const int nwp = a.rpairs * tpad * kRotCB;
-    for (int q = tid; q < nwp; q += 256) {
+    for (int q = tid; q < nwp; q += NT) {
         const int ch = q % kRotCB;
         const int t = (q / kRotCB) % tpad;
         const int rp = q / (kRotCB * tpad);
@@ -558,9 +561,13 @@ __global__ __launch_bounds__(256, 1) void dw_rotated_kernel(const RotArgs a) {
         uint32_t x[kRotTHT + 1][NV];
         uint32_t w0[kRotTB], w1[kRotTB];
     };
+    // SPLIT groups of 256 lanes compute the same outputs over disjoint runs
+    // of the flattened (row pair, column slice) steps; their fp32 sums are
+    // added at the end in group order
     const int nts = ts_hi - ts_lo;
     const int total = (rp_hi - rp_lo) * nts;
-    int lrp = rp_lo, lts = ts_lo;     // load cursor
+    const int it_lo = grp * total / SPLIT, it_hi = (grp + 1) * total / SPLIT;
+    int lrp = rp_lo + (nts > 0 ? it_lo / nts : 0), lts = ts_lo + (nts > 0 ? it_lo % nts : 0);   // load cursor
     auto load = [&](Frag& f) {
 #pragma unroll
         for (int t = 0; t < kRotTB; ++t) {
@@ -598,15 +605,42 @@ __global__ __launch_bounds__(256, 1) void dw_rotated_kernel(const RotArgs a) {
         }
     };
     Frag fa, fb;
-    if (total > 0) load(fa);
+    if (it_lo < it_hi) load(fa);
 #pragma unroll 1
-    for (int it = 0; it < total; it += 2) {
-        if (it + 1 < total) load(fb);
+    for (int it = it_lo; it < it_hi; it += 2) {
+        if (it + 1 < it_hi) load(fb);
         compute(fa);
-        if (it + 1 < total) {
-            if (it + 2 < total) load(fa);
+        if (it + 1 < it_hi) {
+            if (it + 2 < it_hi) load(fa);
             compute(fb);
         }
+    }
+    if constexpr (SPLIT > 1) {
+        // groups 1.. park their sums in LDS (the window is no longer read);
+        // group 0 adds them in group order and stores
+        __syncthreads();
+        float* part = reinterpret_cast<float*>(smem);
+        constexpr int NA = kRotTHT * kRotTWT * 2;
+        if (grp > 0) {
+#pragma unroll
+            for (int i = 0; i < kRotTHT; ++i)
+#pragma unroll
+                for (int j = 0; j < kRotTWT; ++j)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        part[((grp - 1) * NA + (i * kRotTWT + j) * 2 + c) * 256 + lt] = acc[i][j][c];
+        }
+        __syncthreads();
+        if (grp > 0) return;
+#pragma unroll 1
+        for (int g2 = 1; g2 < SPLIT; ++g2)
+#pragma unroll
+            for (int i = 0; i < kRotTHT; ++i)
+#pragma unroll
+                for (int j = 0; j < kRotTWT; ++j)
+#pragma unroll
+                    for (int c = 0; c < 2; ++c)
+                        acc[i][j][c] += part[((g2 - 1) * NA + (i * kRotTWT + j) * 2 + c) * 256 + lt];
     }
     // ---- store: 2 channels per lane ----
 #pragma unroll
@@ -634,8 +668,10 @@ bool rot_geometry(const Prob& p, RotArgs* a, size_t* lds) {
     a->row_dw = a->IWB * 4 + 4;
     const size_t win = size_t(a->IHB) * a->row_dw * 4;
     const size_t wts = size_t(a->rpairs) * a->tslices * kRotTB * kRotCB * 4;
-    *lds = win + wts;
-    return *lds <= 160 * 1024;
+    // the tap groups' partial sums reuse the window's LDS at the end
+    const size_t parts = size_t(kRotSplit - 1) * 256 * kRotTHT * kRotTWT * 2 * 4;
+    *lds = std::max(win + wts, parts);
+    return win + wts <= 160 * 1024;
 }
 
 }  // namespace
@@ -744,7 +780,7 @@ int launch_dgrad_dw_tiled(const Prob& p, const Plan&, const void* dy, const void
                                  : launch_tile_t<F16>(p, a, int(blocks), st);
 }
 
-int launch_dgrad_dw_rotated(const Prob& p, const Plan&, const void* dy, const void* w, void* dx,
+int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
                             hipStream_t st) {
     RotArgs a{};
     size_t lds;
@@ -761,20 +797,28 @@ int launch_dgrad_dw_rotated(const Prob& p, const Plan&, const void* dy, const vo
     a.tiles_w = int((p.w + a.OWB - 1) / a.OWB);
     a.cblocks = int(p.c / kRotCB);
     const int64_t blocks = int64_t(a.N) * a.tiles_h * a.tiles_w * a.cblocks;
+    // tap groups: kRotSplit (two waves per SIMD at one block per CU); tune 1
+    // asks for one group
+    const bool split = pl.tune != 1;
+    if (!split) lds = size_t(a.IHB) * a.row_dw * 4 + size_t(a.rpairs) * a.tslices * kRotTB * kRotCB * 4;
     // dynamic LDS above 64 KiB must be opted into per kernel
-    static bool attr_set[2] = {false, false};
-    const int which = p.dtype == CNHWC_BF16 ? 1 : 0;
+    static bool attr_set[4] = {false, false, false, false};
+    const int which = (p.dtype == CNHWC_BF16 ? 1 : 0) + (split ? 2 : 0);
+    const void* fns[4] = {reinterpret_cast<const void*>(&dw_rotated_kernel<F16, 1>),
+                          reinterpret_cast<const void*>(&dw_rotated_kernel<BF16, 1>),
+                          reinterpret_cast<const void*>(&dw_rotated_kernel<F16, kRotSplit>),
+                          reinterpret_cast<const void*>(&dw_rotated_kernel<BF16, kRotSplit>)};
     if (!attr_set[which]) {
-        const void* fn = which ? reinterpret_cast<const void*>(&dw_rotated_kernel<BF16>)
-                               : reinterpret_cast<const void*>(&dw_rotated_kernel<F16>);
-        if (hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
+        if (hipFuncSetAttribute(fns[which], hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
             return CNHWC_HIP_ERROR;
         attr_set[which] = true;
     }
-    if (which)
-        hipLaunchKernelGGL(dw_rotated_kernel<BF16>, dim3(blocks), dim3(256), lds, st, a);
-    else
-        hipLaunchKernelGGL(dw_rotated_kernel<F16>, dim3(blocks), dim3(256), lds, st, a);
+    switch (which) {
+    case 0: hipLaunchKernelGGL((dw_rotated_kernel<F16, 1>), dim3(blocks), dim3(256), lds, st, a); break;
+    case 1: hipLaunchKernelGGL((dw_rotated_kernel<BF16, 1>), dim3(blocks), dim3(256), lds, st, a); break;
+    case 2: hipLaunchKernelGGL((dw_rotated_kernel<F16, kRotSplit>), dim3(blocks), dim3(256 * kRotSplit), lds, st, a); break;
+    default: hipLaunchKernelGGL((dw_rotated_kernel<BF16, kRotSplit>), dim3(blocks), dim3(256 * kRotSplit), lds, st, a); break;
+    }
     return CNHWC_OK;
 }
 

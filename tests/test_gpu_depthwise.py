@@ -60,9 +60,12 @@ ROT = [
 ]
 
 
+@pytest.mark.parametrize("tune", [0, 1], ids=["split", "onegroup"])
 @pytest.mark.parametrize("p", ROT, ids=ident)
-def test_rotated_parity(p):
-    with api.override(variant=api.VAR_DGRAD_DW_ROTATED):
+def test_rotated_parity(p, tune):
+    """The rotated-filter kernel with its filter steps split over two lane
+    groups (default) and with one group (tune 1)."""
+    with api.override(variant=api.VAR_DGRAD_DW_ROTATED, tune=tune):
         parity(p, "dgrad", 302)
 
 
