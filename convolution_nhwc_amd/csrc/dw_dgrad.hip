@@ -281,6 +281,7 @@ struct TileArgs {
     int N, H, W, C, Ho, Wo, pad_h, pad_w;
     int tiles_h, tiles_w, cblocks;
     int nblocks, remap;
+    int flip;          // 1: use the filter rotated by 180 degrees (depthwise forward)
 };
 
 template <int R, int S>
@@ -361,8 +362,13 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
             const int ch = e % kTileCB;
             const int t = (e / kTileCB) % S;
             const int i = e / (kTileCB * S);
-            const uint32_t lo = raw[ch * R * S + (2 * i) * S + t];
-            const uint32_t hi = 2 * i + 1 < R ? uint32_t(raw[ch * R * S + (2 * i + 1) * S + t]) : 0u;
+            // tap (r, t) of the filter as used; the rotated filter reads (R-1-r, S-1-t)
+            auto tap = [&](int r) {
+                return a.flip ? uint32_t(raw[ch * R * S + (R - 1 - r) * S + (S - 1 - t)])
+                              : uint32_t(raw[ch * R * S + r * S + t]);
+            };
+            const uint32_t lo = tap(2 * i);
+            const uint32_t hi = 2 * i + 1 < R ? tap(2 * i + 1) : 0u;
             wts[e] = lo | (hi << 16);
         }
     }
@@ -465,7 +471,8 @@ struct RotArgs {
     void* dx;
     uint32_t dy_bytes, w_bytes, dx_bytes;
     int N, H, W, C, Ho, Wo, R, S;
-    int ph2, pw2;          // rotated padding R-1-pad_h, S-1-pad_w
+    int ph2, pw2;          // padding of the correlation (dgrad: R-1-pad_h, S-1-pad_w)
+    int rot;               // 1: correlate with the filter rotated by 180 degrees (dgrad)
     int OHB, OWB;          // output tile of a block
     int IHB, IWB;          // staged dY window (rows padded to pairs, columns to slices)
     int rpairs, tslices;   // ceil(R/2), ceil(S/8)
@@ -520,8 +527,12 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
         if (t < a.S) {
             const int r0 = 2 * rp, r1 = 2 * rp + 1;   // rotated rows
             const uint32_t base = uint32_t(c0 + ch) * (a.R * a.S);
-            const uint32_t lo = r0 < a.R ? buf_load2(rw, (base + (a.R - 1 - r0) * a.S + (a.S - 1 - t)) * 2u) : 0u;
-            const uint32_t hi = r1 < a.R ? buf_load2(rw, (base + (a.R - 1 - r1) * a.S + (a.S - 1 - t)) * 2u) : 0u;
+            auto tap = [&](int r) {
+                const uint32_t e = a.rot ? (a.R - 1 - r) * a.S + (a.S - 1 - t) : r * a.S + t;
+                return uint32_t(buf_load2(rw, (base + e) * 2u));
+            };
+            const uint32_t lo = r0 < a.R ? tap(r0) : 0u;
+            const uint32_t hi = r1 < a.R ? tap(r1) : 0u;
             v = lo | (hi << 16);
         }
         wpl[q] = v;
@@ -760,9 +771,26 @@ int launch_tile_t(const Prob& p, const TileArgs& a, int blocks, hipStream_t st) 
 }
 }  // namespace
 
-int launch_dgrad_dw_tiled(const Prob& p, const Plan&, const void* dy, const void* w, void* dx,
-                          hipStream_t st) {
+namespace {
+
+// Depthwise forward (stride 1) through the dgrad kernels: y is x correlated
+// with the filter at padding pad, which is the dgrad correlation of x (as dY,
+// extents H x W) at padding R-1-pad with the filter rotated by 180 degrees --
+// the rotation identity of "Depthwise kernels" (Rotated-filter dgrad) read in
+// the other direction.  The swapped problem is what the dgrad launchers take.
+Prob fwd_as_dgrad(const Prob& p) {
+    Prob q = p;
+    q.h = p.ho; q.w = p.wo; q.ho = p.h; q.wo = p.w;
+    q.pad_h = int(p.r) - 1 - p.pad_h;
+    q.pad_w = int(p.s) - 1 - p.pad_w;
+    return q;
+}
+
+// p in dgrad terms (dy: N x Ho x Wo x C in, dx: N x H x W x C out);
+// flip: read the filter rotated by 180 degrees
+int launch_tiled(const Prob& p, int flip, const void* dy, const void* w, void* dx, hipStream_t st) {
     TileArgs a{};
+    a.flip = flip;
     a.dy = dy; a.w = w; a.dx = dx;
     a.dy_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
     a.w_bytes = uint32_t(p.k * p.r * p.s * 2);
@@ -780,11 +808,14 @@ int launch_dgrad_dw_tiled(const Prob& p, const Plan&, const void* dy, const void
                                  : launch_tile_t<F16>(p, a, int(blocks), st);
 }
 
-int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
-                            hipStream_t st) {
+// p in dgrad terms; rot: correlate with the filter rotated by 180 degrees at
+// padding R-1-pad (dgrad), else with the filter as stored at padding R-1-pad
+int launch_rotated(const Prob& p, const Plan& pl, int rot, const void* dy, const void* w, void* dx,
+                   hipStream_t st) {
     RotArgs a{};
     size_t lds;
     if (!rot_geometry(p, &a, &lds)) return CNHWC_UNSUPPORTED;
+    a.rot = rot;
     a.dy = dy; a.w = w; a.dx = dx;
     a.dy_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
     a.w_bytes = uint32_t(p.k * p.r * p.s * 2);
@@ -820,6 +851,38 @@ int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const
     default: hipLaunchKernelGGL((dw_rotated_kernel<BF16, kRotSplit>), dim3(blocks), dim3(256 * kRotSplit), lds, st, a); break;
     }
     return CNHWC_OK;
+}
+
+}  // namespace
+
+int launch_dgrad_dw_tiled(const Prob& p, const Plan&, const void* dy, const void* w, void* dx,
+                          hipStream_t st) {
+    return launch_tiled(p, 0, dy, w, dx, st);
+}
+
+int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
+                            hipStream_t st) {
+    return launch_rotated(p, pl, 1, dy, w, dx, st);
+}
+
+int launch_fwd_dw_tiled(const Prob& p, const Plan&, const void* x, const void* w, void* y,
+                        hipStream_t st) {
+    return launch_tiled(fwd_as_dgrad(p), 1, x, w, y, st);
+}
+
+int launch_fwd_dw_rotated(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
+                          hipStream_t st) {
+    return launch_rotated(fwd_as_dgrad(p), pl, 0, x, w, y, st);
+}
+
+std::string fwd_dw_tiled_reason(const Prob& p) {
+    if (p.stride != 1) return "the LDS-tiled depthwise forward needs stride 1";
+    return dw_tiled_reason(fwd_as_dgrad(p));
+}
+
+std::string fwd_dw_rotated_reason(const Prob& p) {
+    if (p.stride != 1) return "the rotated-filter depthwise forward needs stride 1";
+    return dw_rotated_reason(fwd_as_dgrad(p));
 }
 
 }  // namespace cnhwc

@@ -81,7 +81,8 @@ bool variant_is_dgrad(int v) {
 }
 bool variant_is_fwd(int v) {
     return v == CNHWC_VAR_FWD_DIRECT || v == CNHWC_VAR_FWD_SPLITC ||
-           v == CNHWC_VAR_FWD_GROUPED || v == CNHWC_VAR_FWD_GENERIC;
+           v == CNHWC_VAR_FWD_GROUPED || v == CNHWC_VAR_FWD_GENERIC ||
+           v == CNHWC_VAR_FWD_DW_TILED || v == CNHWC_VAR_FWD_DW_ROTATED;
 }
 
 const char* dt(const Prob& p) { return p.dtype == CNHWC_F16 ? "f16" : "bf16"; }
@@ -101,6 +102,8 @@ std::string variant_reason(const Prob& p, int op, int v, int cpl, int split_c) {
     case CNHWC_VAR_FWD_DIRECT: return fwd_direct_reason(p, 1);
     case CNHWC_VAR_FWD_SPLITC: return fwd_direct_reason(p, split_c);
     case CNHWC_VAR_FWD_GROUPED: return fwd_grouped_reason(p);
+    case CNHWC_VAR_FWD_DW_TILED: return fwd_dw_tiled_reason(p);
+    case CNHWC_VAR_FWD_DW_ROTATED: return fwd_dw_rotated_reason(p);
     case CNHWC_VAR_FWD_GENERIC:
     case CNHWC_VAR_DGRAD_GENERIC: return "";
     default: return "unknown variant " + std::to_string(v);
@@ -133,6 +136,12 @@ std::string plan_name(const Prob& p, const Plan& pl) {
         std::snprintf(buf, sizeof buf, "fwd_grouped_merge_%s", dt(p)); break;
     case CNHWC_VAR_FWD_GENERIC:
         std::snprintf(buf, sizeof buf, "fwd_generic_%s", dt(p)); break;
+    case CNHWC_VAR_FWD_DW_TILED:
+        std::snprintf(buf, sizeof buf, "fwd_dw_tiled_%s_f%lldx%lld", dt(p), (long long)p.r,
+                      (long long)p.s); break;
+    case CNHWC_VAR_FWD_DW_ROTATED:
+        std::snprintf(buf, sizeof buf, "fwd_dw_rot_%s_f%lldx%lld_p%dx%d", dt(p),
+                      (long long)p.r, (long long)p.s, p.pad_h, p.pad_w); break;
     default: std::snprintf(buf, sizeof buf, "none");
     }
     return buf;
@@ -186,7 +195,15 @@ int choose(const Prob& p, int op, Plan* out) {
         if (!ok) ok = take(CNHWC_VAR_DGRAD_IGEMM, 0, 1);
         if (!ok) ok = take(CNHWC_VAR_DGRAD_GENERIC, 0, 1);
     } else {
-        if (p.groups > 1) ok = take(CNHWC_VAR_FWD_GROUPED, 0, 1);
+        if (is_depthwise(p) && p.stride == 1) {
+            // same split as depthwise dgrad: small square filters on the tiled
+            // kernel, large or non-square ones on the rotated-filter kernel
+            const bool big = p.r > 11 || p.s > 11 || p.r != p.s || p.pad_h != p.pad_w;
+            if (big) ok = take(CNHWC_VAR_FWD_DW_ROTATED, 0, 1);
+            if (!ok) ok = take(CNHWC_VAR_FWD_DW_TILED, 0, 1);
+            if (!ok) ok = take(CNHWC_VAR_FWD_DW_ROTATED, 0, 1);
+        }
+        if (!ok && p.groups > 1) ok = take(CNHWC_VAR_FWD_GROUPED, 0, 1);
         if (!ok) {
             int split = ov.split_c > 0 ? ov.split_c : fwd_direct_auto_split(p);
             if (split > 1) ok = take(CNHWC_VAR_FWD_SPLITC, 0, split);
@@ -307,6 +324,8 @@ int run(const cnhwc_problem* prob, int op, const void* in, const void* w, void* 
         case CNHWC_VAR_FWD_SPLITC: rc = launch_fwd_direct(pc, pl, ip, w, op_, ws, s); break;
         case CNHWC_VAR_FWD_GROUPED: rc = launch_fwd_grouped(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_FWD_GENERIC: rc = launch_fwd_generic(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_FWD_DW_TILED: rc = launch_fwd_dw_tiled(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_FWD_DW_ROTATED: rc = launch_fwd_dw_rotated(pc, pl, ip, w, op_, s); break;
         default: rc = CNHWC_UNSUPPORTED;
         }
         if (rc) return fail(rc, "launcher for " + pl.name + " refused the chunk");

@@ -116,4 +116,9 @@ WORKLOADS = {
                       prob=problem(8, 32, 32, 256, 256, 51, 5, 1, 25, 2, groups=256)),
     "c5_dw5x51": dict(op="dgrad", seed=55, fan_in=255,
                       prob=problem(8, 32, 32, 256, 256, 5, 51, 1, 2, 25, groups=256)),
+    # depthwise forward (the next row after the hot path): the C5 shapes, forward
+    "f1_dwfwd3x3": dict(op="fwd", seed=61, fan_in=9,
+                        prob=problem(16, 56, 56, 384, 384, 3, 3, 1, 1, 1, groups=384)),
+    "f1_dwfwd31x31": dict(op="fwd", seed=63, fan_in=961,
+                          prob=problem(8, 32, 32, 256, 256, 31, 31, 1, 15, 15, groups=256)),
 }

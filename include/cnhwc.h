@@ -90,6 +90,10 @@ typedef struct cnhwc_problem {
 #define CNHWC_VAR_FWD_GENERIC 8      /* plain one-output-per-lane forward (any valid problem) */
 #define CNHWC_VAR_DGRAD_GENERIC 9    /* plain one-output-per-lane dgrad (any valid problem) */
 #define CNHWC_VAR_DGRAD_DW_TILED 10  /* depthwise dgrad, stride 1, 3x3/5x5/7x7, dY window tiled in LDS */
+#define CNHWC_VAR_FWD_DW_TILED 11    /* depthwise forward, stride 1, 3x3/5x5/7x7: the tiled dgrad kernel
+                                        on x with the filter rotated by 180 degrees, padding R-1-pad */
+#define CNHWC_VAR_FWD_DW_ROTATED 12  /* depthwise forward, stride 1, filters up to 64 a side, any
+                                        padding: the rotated-filter kernel with the filter as stored */
 
 /* Output dims by the floor formula above.  INVALID_ARG for a bad descriptor. */
 int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo);

@@ -94,6 +94,8 @@ EXPECT = {
     "c5_dw31x31": api.VAR_DGRAD_DW_ROTATED,
     "c5_dw51x5": api.VAR_DGRAD_DW_ROTATED,
     "c5_dw5x51": api.VAR_DGRAD_DW_ROTATED,
+    "f1_dwfwd3x3": api.VAR_FWD_DW_TILED,
+    "f1_dwfwd31x31": api.VAR_FWD_DW_ROTATED,
 }
 
 
@@ -103,6 +105,21 @@ def test_dispatcher_choice_per_workload(name):
     op = api.OP_FWD if w["op"] == "fwd" else api.OP_DGRAD
     kname, var = api.cnhwc_plan(w["prob"], op)
     assert var == EXPECT[name], (name, kname)
+
+
+def test_depthwise_forward_dispatch():
+    """Stride-1 depthwise forward runs on the depthwise kernels (small square
+    filters tiled, large / non-square / uneven padding rotated); strided
+    depthwise forward stays on the grouped merge."""
+    dw = dict(n=1, h=20, w=20, c=32, k=32, groups=32, dtype="f16")
+    assert api.cnhwc_plan(dict(dw, r=5, s=5, stride=1, pad_h=2, pad_w=2), api.OP_FWD)[1] == api.VAR_FWD_DW_TILED
+    assert api.cnhwc_plan(dict(dw, r=13, s=13, stride=1, pad_h=6, pad_w=6), api.OP_FWD)[1] == api.VAR_FWD_DW_ROTATED
+    assert api.cnhwc_plan(dict(dw, r=7, s=5, stride=1, pad_h=3, pad_w=2), api.OP_FWD)[1] == api.VAR_FWD_DW_ROTATED
+    assert api.cnhwc_plan(dict(dw, r=3, s=3, stride=2, pad_h=1, pad_w=1), api.OP_FWD)[1] == api.VAR_FWD_GROUPED
+    # a depthwise dgrad variant is not a forward kernel
+    with api.override(variant=api.VAR_DGRAD_DW_TILED):
+        with pytest.raises(Exception):
+            api.cnhwc_plan(dict(dw, r=3, s=3, stride=1, pad_h=1, pad_w=1), api.OP_FWD)
 
 
 def test_dispatcher_falls_back_to_generic():
