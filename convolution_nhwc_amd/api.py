@@ -22,7 +22,7 @@ F16, BF16 = 0, 1
 OP_FWD, OP_DGRAD = 1, 2
 (VAR_AUTO, VAR_DGRAD_POINTWISE, VAR_DGRAD_IGEMM, VAR_DGRAD_DW_STREAM, VAR_DGRAD_DW_ROTATED,
  VAR_FWD_DIRECT, VAR_FWD_SPLITC, VAR_FWD_GROUPED, VAR_FWD_GENERIC, VAR_DGRAD_GENERIC,
- VAR_DGRAD_DW_TILED, VAR_FWD_DW_TILED, VAR_FWD_DW_ROTATED) = range(13)
+ VAR_DGRAD_DW_TILED, VAR_FWD_DW_TILED, VAR_FWD_DW_ROTATED, VAR_DGRAD_GROUPED) = range(14)
 
 SYMBOLS = ("cnhwc_out_dims", "cnhwc_workspace_size", "cnhwc_plan", "cnhwc_chunk_plan",
            "cnhwc_fwd", "cnhwc_dgrad", "cnhwc_last_error", "cnhwc_set_override")

@@ -549,7 +549,11 @@ struct GrowArgs {
     FastDiv fd_cpr, fd_iw, fd_tw, fd_kc;   // division by C/8, IW, TW, K/8
 };
 
-template <typename T, int BN, int R, int S>
+// DG: the same correlation run for grouped dgrad at stride 1 (x = dY, y = dX,
+// padding R-1-pad): element (o, tap, i) of the correlation's filter is then
+// W[g*Cg + i][R-1-r][S-1-t][o - g*Kg] of the stored filter (Cg, Kg here are the
+// correlation's input and output channels per group).
+template <typename T, int BN, int R, int S, bool DG>
 __global__ __launch_bounds__(kGrThreads, 1) void fwd_grouped_rows_kernel(const GrowArgs a) {
     constexpr int TAPS = R * S, FM = kBM / 16, FN = BN / 16;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -602,10 +606,27 @@ __global__ __launch_bounds__(kGrThreads, 1) void fwd_grouped_rows_kernel(const G
         for (int j = 0; j < FN; ++j) {
             const int kk = j * 16 + frow;
             const bool own = kk < a.bn && (fgrp * 8) / a.Cg == kk / a.Kg;
-            const uint32_t base = uint32_t(((gs * a.bn + kk) * TAPS) * a.Cg + (fgrp * 8) % a.Cg) * 2u;
+            if constexpr (!DG) {
+                const uint32_t base = uint32_t(((gs * a.bn + kk) * TAPS) * a.Cg + (fgrp * 8) % a.Cg) * 2u;
 #pragma unroll
-            for (int tap = 0; tap < TAPS; ++tap)
-                wf[tap][j] = buf_load16(rw, own ? base + uint32_t(tap * a.Cg * 2) : kOob);
+                for (int tap = 0; tap < TAPS; ++tap)
+                    wf[tap][j] = buf_load16(rw, own ? base + uint32_t(tap * a.Cg * 2) : kOob);
+            } else {
+                // the 8 merged channels are 8 filter rows k, TAPS * Kg elements apart
+                const int o = gs * a.bn + kk;
+                const int g = o / a.Kg;
+                const uint32_t base = uint32_t((g * a.Cg + (fgrp * 8) % a.Cg) * TAPS * a.Kg + (o - g * a.Kg));
+#pragma unroll
+                for (int tap = 0; tap < TAPS; ++tap) {
+                    uint32_t h[8];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e)
+                        h[e] = own ? uint32_t(buf_load2(rw, (base + uint32_t((e * TAPS + TAPS - 1 - tap) * a.Kg)) * 2u))
+                                   : 0u;
+                    wf[tap][j] = i32x4{int(h[0] | (h[1] << 16)), int(h[2] | (h[3] << 16)),
+                                       int(h[4] | (h[5] << 16)), int(h[6] | (h[7] << 16))};
+                }
+            }
         }
     };
 
@@ -897,7 +918,8 @@ static bool grow_geometry(const Prob& p, GrowArgs* a, size_t* lds) {
     return true;
 }
 
-static int launch_fwd_grouped_rows(const Prob& p, const void* x, const void* w, void* y, hipStream_t st) {
+// p: the forward problem, or for dgrad (dg) the swapped correlation problem
+static int launch_grouped_rows(const Prob& p, bool dg, const void* x, const void* w, void* y, hipStream_t st) {
     GrowArgs a{};
     size_t lds = 0;
     if (!grow_geometry(p, &a, &lds)) return CNHWC_UNSUPPORTED;
@@ -918,18 +940,20 @@ static int launch_fwd_grouped_rows(const Prob& p, const void* x, const void* w, 
     const bool bf = p.dtype == CNHWC_BF16;
     const void* fn;
     void (*launch)(const GrowArgs&, int64_t, size_t, hipStream_t);
-#define CNHWC_GROW(T, BN, R, S)                                                                  \
-    fn = reinterpret_cast<const void*>(&fwd_grouped_rows_kernel<T, BN, R, S>);                   \
+#define CNHWC_GROW(T, BN, R, S, DG)                                                              \
+    fn = reinterpret_cast<const void*>(&fwd_grouped_rows_kernel<T, BN, R, S, DG>);               \
     launch = [](const GrowArgs& g, int64_t nb, size_t l, hipStream_t q) {                        \
-        hipLaunchKernelGGL((fwd_grouped_rows_kernel<T, BN, R, S>), dim3(nb), dim3(kGrThreads), l, q, g); \
+        hipLaunchKernelGGL((fwd_grouped_rows_kernel<T, BN, R, S, DG>), dim3(nb), dim3(kGrThreads), l, q, g); \
     };
+#define CNHWC_GROW_DG(T, BN, R, S) if (dg) { CNHWC_GROW(T, BN, R, S, true) } else { CNHWC_GROW(T, BN, R, S, false) }
     if (p.r == 3) {
-        if (bf) { CNHWC_GROW(BF16, 32, 3, 3) } else { CNHWC_GROW(F16, 32, 3, 3) }
+        if (bf) { CNHWC_GROW_DG(BF16, 32, 3, 3) } else { CNHWC_GROW_DG(F16, 32, 3, 3) }
     } else if (a.bn <= 32) {
-        if (bf) { CNHWC_GROW(BF16, 32, 1, 1) } else { CNHWC_GROW(F16, 32, 1, 1) }
+        if (bf) { CNHWC_GROW_DG(BF16, 32, 1, 1) } else { CNHWC_GROW_DG(F16, 32, 1, 1) }
     } else {
-        if (bf) { CNHWC_GROW(BF16, 64, 1, 1) } else { CNHWC_GROW(F16, 64, 1, 1) }
+        if (bf) { CNHWC_GROW_DG(BF16, 64, 1, 1) } else { CNHWC_GROW_DG(F16, 64, 1, 1) }
     }
+#undef CNHWC_GROW_DG
 #undef CNHWC_GROW
     if (lds > 64 * 1024 && hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
         return CNHWC_HIP_ERROR;
@@ -943,7 +967,7 @@ int launch_fwd_grouped(const Prob& p, const Plan& pl, const void* x, const void*
     if (pl.tune != 1) {
         GrowArgs g{};
         size_t lds = 0;
-        if (grow_geometry(p, &g, &lds)) return launch_fwd_grouped_rows(p, x, w, y, st);
+        if (grow_geometry(p, &g, &lds)) return launch_grouped_rows(p, false, x, w, y, st);
     }
     GrpArgs a{};
     if (!pick_geo(p, kGHaloMax, &a.geo)) return CNHWC_UNSUPPORTED;
@@ -983,6 +1007,40 @@ int launch_fwd_grouped(const Prob& p, const Plan& pl, const void* x, const void*
     CNHWC_GRP(64)
 #undef CNHWC_GRP
     return CNHWC_UNSUPPORTED;
+}
+
+// ---- grouped dgrad, stride 1, on the whole-row grouped kernel -------------
+// dX is dY correlated with the filter rotated by 180 degrees and transposed
+// per group (dX channel c of group g gathers dY channels g*Kg .. +Kg), at
+// padding R-1-pad: a grouped forward correlation with input dY (K channels,
+// Kg per group, extents Ho x Wo) and output dX (C channels, Cg per group,
+// extents H x W) -- the same block-diagonal merge of small groups.
+static Prob dgrad_as_fwd(const Prob& p) {
+    Prob q = p;
+    q.h = p.ho; q.w = p.wo; q.ho = p.h; q.wo = p.w;
+    q.c = p.k; q.k = p.c; q.cg = p.kg; q.kg = p.cg;
+    q.pad_h = int(p.r) - 1 - p.pad_h;
+    q.pad_w = int(p.s) - 1 - p.pad_w;
+    return q;
+}
+
+std::string dgrad_grouped_reason(const Prob& p) {
+    if (p.groups < 2) return "grouped merge needs groups > 1";
+    if (p.stride != 1) return "grouped dgrad merge needs stride 1";
+    if (p.h * p.w * p.c > (int64_t(1) << 30) || p.ho * p.wo * p.k > (int64_t(1) << 30))
+        return "one image exceeds the 32-bit element range";
+    GrowArgs g{};
+    size_t lds = 0;
+    if (!grow_geometry(dgrad_as_fwd(p), &g, &lds))
+        return "grouped dgrad merge needs K/groups dividing 32 (a multiple of 8), C and K multiples of "
+               "64, a 3x3 filter with (32/(K/groups))*(C/groups) <= 32 or a 1x1 filter with it <= 64, "
+               "and a tile within LDS";
+    return "";
+}
+
+int launch_dgrad_grouped(const Prob& p, const Plan&, const void* dy, const void* w, void* dx,
+                         hipStream_t st) {
+    return launch_grouped_rows(dgrad_as_fwd(p), true, dy, w, dx, st);
 }
 
 }  // namespace cnhwc

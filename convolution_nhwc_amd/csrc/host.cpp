@@ -77,7 +77,7 @@ bool is_depthwise(const Prob& p) { return p.groups == p.c && p.groups == p.k; }
 bool variant_is_dgrad(int v) {
     return v == CNHWC_VAR_DGRAD_POINTWISE || v == CNHWC_VAR_DGRAD_IGEMM ||
            v == CNHWC_VAR_DGRAD_DW_STREAM || v == CNHWC_VAR_DGRAD_DW_ROTATED ||
-           v == CNHWC_VAR_DGRAD_DW_TILED || v == CNHWC_VAR_DGRAD_GENERIC;
+           v == CNHWC_VAR_DGRAD_DW_TILED || v == CNHWC_VAR_DGRAD_GENERIC || v == CNHWC_VAR_DGRAD_GROUPED;
 }
 bool variant_is_fwd(int v) {
     return v == CNHWC_VAR_FWD_DIRECT || v == CNHWC_VAR_FWD_SPLITC ||
@@ -99,6 +99,7 @@ std::string variant_reason(const Prob& p, int op, int v, int cpl, int split_c) {
     case CNHWC_VAR_DGRAD_DW_STREAM: return dw_stream_reason(p, cpl);
     case CNHWC_VAR_DGRAD_DW_ROTATED: return dw_rotated_reason(p);
     case CNHWC_VAR_DGRAD_DW_TILED: return dw_tiled_reason(p);
+    case CNHWC_VAR_DGRAD_GROUPED: return dgrad_grouped_reason(p);
     case CNHWC_VAR_FWD_DIRECT: return fwd_direct_reason(p, 1);
     case CNHWC_VAR_FWD_SPLITC: return fwd_direct_reason(p, split_c);
     case CNHWC_VAR_FWD_GROUPED: return fwd_grouped_reason(p);
@@ -128,6 +129,8 @@ std::string plan_name(const Prob& p, const Plan& pl) {
                       (long long)p.s); break;
     case CNHWC_VAR_DGRAD_GENERIC:
         std::snprintf(buf, sizeof buf, "dgrad_generic_%s", dt(p)); break;
+    case CNHWC_VAR_DGRAD_GROUPED:
+        std::snprintf(buf, sizeof buf, "dgrad_grouped_merge_%s", dt(p)); break;
     case CNHWC_VAR_FWD_DIRECT:
         std::snprintf(buf, sizeof buf, "fwd_direct_%s", dt(p)); break;
     case CNHWC_VAR_FWD_SPLITC:
@@ -190,6 +193,7 @@ int choose(const Prob& p, int op, Plan* out) {
             }
             if (!ok && p.stride == 1) ok = take(CNHWC_VAR_DGRAD_DW_ROTATED, 0, 1);
         }
+        if (!ok && p.groups > 1 && !is_depthwise(p) && p.stride == 1) ok = take(CNHWC_VAR_DGRAD_GROUPED, 0, 1);
         if (!ok && p.groups == 1 && p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0)
             ok = take(CNHWC_VAR_DGRAD_POINTWISE, 0, 1);
         if (!ok) ok = take(CNHWC_VAR_DGRAD_IGEMM, 0, 1);
@@ -320,6 +324,7 @@ int run(const cnhwc_problem* prob, int op, const void* in, const void* w, void* 
         case CNHWC_VAR_DGRAD_DW_ROTATED: rc = launch_dgrad_dw_rotated(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_DGRAD_DW_TILED: rc = launch_dgrad_dw_tiled(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_DGRAD_GENERIC: rc = launch_dgrad_generic(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_DGRAD_GROUPED: rc = launch_dgrad_grouped(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_FWD_DIRECT:
         case CNHWC_VAR_FWD_SPLITC: rc = launch_fwd_direct(pc, pl, ip, w, op_, ws, s); break;
         case CNHWC_VAR_FWD_GROUPED: rc = launch_fwd_grouped(pc, pl, ip, w, op_, s); break;

@@ -59,6 +59,9 @@ int launch_fwd_grouped(const Prob& p, const Plan& pl, const void* x, const void*
                        hipStream_t st);
 int launch_fwd_generic(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                        hipStream_t st);
+// Grouped dgrad, stride 1, small groups merged: the whole-row grouped kernel.
+int launch_dgrad_grouped(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
+                         hipStream_t st);
 // Depthwise forward, stride 1, on the depthwise dgrad kernels (rotation identity).
 int launch_fwd_dw_tiled(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                         hipStream_t st);
@@ -71,6 +74,7 @@ std::string dw_stream_reason(const Prob& p, int cpl);
 std::string dw_rotated_reason(const Prob& p);
 std::string dw_tiled_reason(const Prob& p);
 std::string fwd_dw_tiled_reason(const Prob& p);
+std::string dgrad_grouped_reason(const Prob& p);
 std::string fwd_dw_rotated_reason(const Prob& p);
 std::string fwd_direct_reason(const Prob& p, int split_c);
 std::string fwd_grouped_reason(const Prob& p);

@@ -121,4 +121,8 @@ WORKLOADS = {
                         prob=problem(16, 56, 56, 384, 384, 3, 3, 1, 1, 1, groups=384)),
     "f1_dwfwd31x31": dict(op="fwd", seed=63, fan_in=961,
                           prob=problem(8, 32, 32, 256, 256, 31, 31, 1, 15, 15, groups=256)),
+    # grouped dgrad (the second next row): the grouped forward shape, backward
+    "f2_grouped_dgrad": dict(op="dgrad", seed=71, fan_in=8 * 9,
+                             prob=problem(32, 28, 28, 256, 256, 3, 3, 1, 1, 1, groups=32,
+                                          dtype=BF16)),
 }

@@ -94,6 +94,9 @@ typedef struct cnhwc_problem {
                                         on x with the filter rotated by 180 degrees, padding R-1-pad */
 #define CNHWC_VAR_FWD_DW_ROTATED 12  /* depthwise forward, stride 1, filters up to 64 a side, any
                                         padding: the rotated-filter kernel with the filter as stored */
+#define CNHWC_VAR_DGRAD_GROUPED 13   /* grouped dgrad, stride 1, small groups merged block-diagonally:
+                                        the whole-row grouped kernel on dY with the filter rotated and
+                                        transposed per group, padding R-1-pad */
 
 /* Output dims by the floor formula above.  INVALID_ARG for a bad descriptor. */
 int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo);

@@ -58,8 +58,11 @@ IGEMM = [
 
 @pytest.mark.parametrize("p", IGEMM, ids=ident)
 def test_igemm_parity(p):
-    assert api.cnhwc_plan(p, api.OP_DGRAD)[1] == api.VAR_DGRAD_IGEMM
-    parity(p, "dgrad", 102)
+    # stride-1 grouped shapes may be dispatched to the grouped merge instead;
+    # this test runs the implicit-GEMM kernel on every shape
+    assert api.cnhwc_plan(p, api.OP_DGRAD)[1] in (api.VAR_DGRAD_IGEMM, api.VAR_DGRAD_GROUPED)
+    with api.override(variant=api.VAR_DGRAD_IGEMM):
+        parity(p, "dgrad", 102)
 
 
 @pytest.mark.parametrize("tune", [1, 2], ids=["ring", "window"])
@@ -110,6 +113,35 @@ def test_pointwise_persistent_matches_ring(p, tune):
     assert np.array_equal(pers.view(np.uint16), ring.view(np.uint16))
 
 
+GROUPED = [
+    P(2, 12, 12, 64, 64, 3, 3, 1, 1, 1, groups=8),          # Cg = Kg = 8: 4 groups merged
+    P(1, 10, 10, 128, 256, 3, 3, 1, 1, 1, groups=16),       # Cg 8, Kg 16: 2 groups merged
+    P(1, 13, 11, 64, 64, 3, 3, 1, 0, 2, groups=8),          # per-axis padding
+    P(1, 9, 11, 256, 128, 1, 1, 1, 0, 0, groups=16),        # 1x1, 64 merged outputs
+    P(2, 28, 28, 256, 256, 3, 3, 1, 1, 1, groups=32, dtype="bf16"),
+    P(1, 30, 9, 128, 128, 3, 3, 1, 1, 0, groups=16, dtype="bf16"),  # two row tiles
+]
+
+
+@pytest.mark.parametrize("p", GROUPED, ids=ident)
+def test_grouped_dgrad_parity(p):
+    """Grouped dgrad (stride 1) on the block-diagonal merge."""
+    assert api.cnhwc_plan(p, api.OP_DGRAD)[1] == api.VAR_DGRAD_GROUPED
+    parity(p, "dgrad", 110)
+
+
+@pytest.mark.parametrize("p", [GROUPED[0], GROUPED[1], GROUPED[3]], ids=ident)
+def test_grouped_dgrad_matches_igemm_on_exact_inputs(p):
+    """Inputs in {-1, 0, 1}: exact partial sums, so the merged kernel and the
+    implicit-GEMM kernel (one group per tile) agree bit for bit."""
+    ab, _, wb, _ = operands(p, "dgrad", 111, exact=True)
+    merged = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    with api.override(variant=api.VAR_DGRAD_IGEMM):
+        ig = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    assert np.array_equal(merged, ig)
+    parity(p, "dgrad", 111, exact=True)
+
+
 def test_reproducible_bitwise():
     p = P(2, 14, 14, 64, 128, 3, 3, 2, 1, 1)
     ab, _, wb, _ = operands(p, "dgrad", 105)
@@ -142,7 +174,7 @@ def test_planted_stride_mistake_is_caught():
         check_close(got, oracle.conv_dgrad(wrong, wf, p))
 
 
-FULL = ["c2_pointwise", "c3a_3x3_s1", "c3b_3x3_s2"]
+FULL = ["c2_pointwise", "c3a_3x3_s1", "c3b_3x3_s2", "f2_grouped_dgrad"]
 
 
 @pytest.mark.parametrize("name", FULL)

@@ -94,8 +94,11 @@ GROUPED = [
 def test_grouped_merge_parity(p, tune):
     """Both grouped kernels: the whole-row one (auto, where it applies) and the
     group-set one (tune 1, every shape)."""
-    assert api.cnhwc_plan(p, api.OP_FWD)[1] == api.VAR_FWD_GROUPED
-    with api.override(tune=tune):
+    depthwise = p["groups"] == p["c"] == p["k"] and p["stride"] == 1
+    # stride-1 depthwise forward is dispatched to the depthwise kernels; the
+    # merge is run on it by override here
+    assert api.cnhwc_plan(p, api.OP_FWD)[1] == (api.VAR_FWD_DW_TILED if depthwise else api.VAR_FWD_GROUPED)
+    with api.override(tune=tune, variant=api.VAR_FWD_GROUPED):
         parity(p, "fwd", 204)
 
 

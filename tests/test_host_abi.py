@@ -96,6 +96,7 @@ EXPECT = {
     "c5_dw5x51": api.VAR_DGRAD_DW_ROTATED,
     "f1_dwfwd3x3": api.VAR_FWD_DW_TILED,
     "f1_dwfwd31x31": api.VAR_FWD_DW_ROTATED,
+    "f2_grouped_dgrad": api.VAR_DGRAD_GROUPED,
 }
 
 
