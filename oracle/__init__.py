@@ -8,6 +8,7 @@ from .oracle import (  # noqa: F401
     build,
     conv_dgrad,
     conv_fwd,
+    conv_wgrad,
     num_threads,
     out_dims,
     set_num_threads,

@@ -1,5 +1,6 @@
 /*
- * Plain fp64 CPU convolution oracle (forward and backward-data, NHWC / KRSC).
+ * Plain fp64 CPU convolution oracle (forward, backward-data and weight
+ * gradient, NHWC / KRSC).
  *
  * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may link, load or
  * call this file; only the test suite, the smoke check and the benchmark's
@@ -18,6 +19,9 @@
  *    unflipped weight of the covering tap ("feat(rocke): channel-packed and
  *    large-filter depthwise dgrad", Rotated-filter dgrad: the same quantity
  *    written as a correlation with the 180-degree-rotated filter);
+ *  - the weight gradient (wgrad) is the derivative of the forward map with
+ *    respect to the weight, the third pass the first page lists beside
+ *    forward and dgrad (Motivation);
  *  - per-axis padding: pad_h pads top and bottom, pad_w left and right, and
  *    the output width follows pad_w (same page, Per-axis padding section and
  *    the review that counts 22 against 24 output columns);
@@ -176,6 +180,54 @@ int oracle_conv_dgrad_f64(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K,
                         }
                     }
                     dx[((n * H + h) * W + ww) * C + c] = acc;
+                }
+            }
+        }
+    }
+    return 0;
+}
+
+/* dw[k,r,t,j] = sum_{n,ho,wo} dy[n,ho,wo,k] * x[n, ho*s - pad_h + r, wo*s - pad_w + t, g*Cg + j],
+ * g = k / Kg, with x taken as 0 outside the image: the gradient of the
+ * forward map with respect to the weight (its value at each weight entry is
+ * the sum, over the output pixels, of dY times the input the forward
+ * multiplies that entry with). */
+int oracle_conv_wgrad_f64(int64_t N, int64_t H, int64_t W, int64_t C, int64_t K,
+                          int64_t R, int64_t S, int64_t stride, int64_t pad_h,
+                          int64_t pad_w, int64_t groups, const double* x,
+                          const double* dy, double* dw)
+{
+    int64_t Ho, Wo;
+    if (oracle_dims(N, H, W, C, K, R, S, stride, pad_h, pad_w, groups, &Ho, &Wo))
+        return 1;
+    const int64_t Cg = C / groups, Kg = K / groups;
+
+#pragma omp parallel for collapse(2) schedule(static)
+    for (int64_t k = 0; k < K; ++k) {
+        for (int64_t r = 0; r < R; ++r) {
+            const int64_t g = k / Kg;
+            for (int64_t t = 0; t < S; ++t) {
+                for (int64_t j = 0; j < Cg; ++j) {
+                    double acc = 0.0;
+                    for (int64_t n = 0; n < N; ++n) {
+                        for (int64_t ho = 0; ho < Ho; ++ho) {
+                            const int64_t h = ho * stride - pad_h + r;
+                            if (h < 0 || h >= H)
+                                continue;
+                            for (int64_t wo = 0; wo < Wo; ++wo) {
+#if ORACLE_MUTATION == 7 /* planted: filter columns mirrored in the weight gradient */
+                                const int64_t ww = wo * stride - pad_w + (S - 1 - t);
+#else
+                                const int64_t ww = wo * stride - pad_w + t;
+#endif
+                                if (ww < 0 || ww >= W)
+                                    continue;
+                                acc += dy[((n * Ho + ho) * Wo + wo) * K + k] *
+                                       x[((n * H + h) * W + ww) * C + g * Cg + j];
+                            }
+                        }
+                    }
+                    dw[((k * R + r) * S + t) * Cg + j] = acc;
                 }
             }
         }

@@ -1,6 +1,6 @@
 """ctypes front end of the fp64 C oracle in ``oracle.c`` (test infrastructure only).
 
-``conv_fwd`` and ``conv_dgrad`` take and return float64 numpy arrays in NHWC
+``conv_fwd``, ``conv_dgrad`` and ``conv_wgrad`` take and return float64 numpy arrays in NHWC
 (activations) and KRSC (weights) layout and compute the plain definitions given
 in ``oracle.c``.  ``build`` compiles the C file with gcc (OpenMP) into
 ``oracle/_build``; a deliberate-mistake variant can be built with ``mutation``
@@ -45,7 +45,7 @@ def _lib(mutation=0):
             lib = ctypes.CDLL(build(mutation))
             i64 = ctypes.c_int64
             dp = ctypes.POINTER(ctypes.c_double)
-            for fn in ("oracle_conv_fwd_f64", "oracle_conv_dgrad_f64"):
+            for fn in ("oracle_conv_fwd_f64", "oracle_conv_dgrad_f64", "oracle_conv_wgrad_f64"):
                 f = getattr(lib, fn)
                 f.argtypes = [i64] * 11 + [dp, dp, dp]
                 f.restype = ctypes.c_int
@@ -100,6 +100,19 @@ def conv_dgrad(dy, w, p, mutation=0):
     if _lib(mutation).oracle_conv_dgrad_f64(*_dims(p), _ptr(dy), _ptr(w), _ptr(dx)):
         raise ValueError("oracle refused %r" % (p,))
     return dx
+
+
+def conv_wgrad(x, dy, p, mutation=0):
+    """dw[K,R,S,C/G] = gradient of the forward map with respect to the weight,
+    for input x[N,H,W,C] and output gradient dy[N,Ho,Wo,K]."""
+    ho, wo = out_dims(p)
+    x, dy = _f64(x), _f64(dy)
+    assert x.shape == (p["n"], p["h"], p["w"], p["c"]), x.shape
+    assert dy.shape == (p["n"], ho, wo, p["k"]), dy.shape
+    dw = np.empty((p["k"], p["r"], p["s"], p["c"] // p["groups"]), dtype=np.float64)
+    if _lib(mutation).oracle_conv_wgrad_f64(*_dims(p), _ptr(x), _ptr(dy), _ptr(dw)):
+        raise ValueError("oracle refused %r" % (p,))
+    return dw
 
 
 def num_threads():

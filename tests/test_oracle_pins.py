@@ -7,7 +7,8 @@ Each pin is independent of oracle.c's loops:
   * the GEMM identity of the 1x1 stride-1 dgrad ("perf(rocke/conv): add the
     pointwise fast path dgrad was missing": the tilde decomposition is the
     identity there and the offsets are m*K + k and k*C + c);
-  * the adjoint inner-product identity;
+  * the adjoint inner-product identity (and, for the weight gradient, the
+    same identity with the weight as the variable);
   * the rotated-filter identity of stride-1 depthwise dgrad ("feat(rocke):
     channel-packed and large-filter depthwise dgrad", Rotated-filter dgrad);
   * the textbook zero-insertion form of strided dgrad;
@@ -293,6 +294,71 @@ def test_per_axis_width_from_the_pages():
         assert oracle.out_dims(q)[1] == case["wo_if_pad_used"]
 
 
+def weight_operator(p, x):
+    """Matrix B with fwd(x, w) = B @ w.ravel() for the fixed input x, filled
+    from the same forward index relation as dense_operator, with the roles of
+    x and w exchanged: the weight gradient is then B^T dy."""
+    n_, h_, w_, c_, k_ = p["n"], p["h"], p["w"], p["c"], p["k"]
+    R, S, s, ph, pw, G = p["r"], p["s"], p["stride"], p["pad_h"], p["pad_w"], p["groups"]
+    Cg, Kg = c_ // G, k_ // G
+    Ho, Wo = oracle.out_dims(p)
+    B = np.zeros((n_ * Ho * Wo * k_, k_ * R * S * Cg))
+    for n, ho, wo, k in itertools.product(range(n_), range(Ho), range(Wo), range(k_)):
+        row = ((n * Ho + ho) * Wo + wo) * k_ + k
+        g = k // Kg
+        for r, t, j in itertools.product(range(R), range(S), range(Cg)):
+            hh, ww = ho * s - ph + r, wo * s - pw + t
+            if 0 <= hh < h_ and 0 <= ww < w_:
+                B[row, ((k * R + r) * S + t) * Cg + j] += x[n, hh, ww, g * Cg + j]
+    return B
+
+
+@pytest.mark.parametrize("p", TINY, ids=lambda p: "h{h}w{w}c{c}k{k}r{r}s{s}st{stride}p{pad_h}x{pad_w}g{groups}".format(**p))
+def test_wgrad_matches_weight_operator_transpose(p):
+    """Brute force: wgrad(x, dy) = B(x)^T dy, with B built here element by element."""
+    x, dy, _ = rand_operands(p, 15)
+    B = weight_operator(p, x)
+    ref = (B.T @ dy.ravel()).reshape(p["k"], p["r"], p["s"], p["c"] // p["groups"])
+    np.testing.assert_allclose(oracle.conv_wgrad(x, dy, p), ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("p", ADJ + [TINY[3], TINY[7]], ids=lambda p: "r{r}s{s}st{stride}p{pad_h}x{pad_w}g{groups}".format(**p))
+def test_wgrad_adjoint_identity(p):
+    """wgrad is the weight gradient of the forward map: for every weight w,
+    <fwd(x, w), dy> = <w, wgrad(x, dy)> (the forward map is linear in w).
+    Three random weights pin three independent functionals."""
+    x, dy, _ = rand_operands(p, 16)
+    dw = oracle.conv_wgrad(x, dy, p)
+    rng = np.random.default_rng(17)
+    for _ in range(3):
+        w = rng.standard_normal(dw.shape)
+        lhs = np.vdot(oracle.conv_fwd(x, w, p), dy)
+        rhs = np.vdot(w, dw)
+        assert abs(lhs - rhs) <= 1e-12 * max(1.0, abs(lhs))
+
+
+def test_pointwise_wgrad_is_a_gemm():
+    """1x1 stride 1: dW[k, c] = sum over pixels of dY[m, k] x[m, c] = (dY^T X)[k, c]."""
+    p = P(2, 6, 7, 24, 40, 1, 1)
+    x, dy, _ = rand_operands(p, 18)
+    m = p["n"] * p["h"] * p["w"]
+    ref = (dy.reshape(m, p["k"]).T @ x.reshape(m, p["c"])).reshape(p["k"], 1, 1, p["c"])
+    np.testing.assert_allclose(oracle.conv_wgrad(x, dy, p), ref, rtol=1e-12, atol=1e-12)
+
+
+@pytest.mark.parametrize("p", MEDIUM, ids=lambda p: "h{h}w{w}c{c}k{k}r{r}s{s}st{stride}g{groups}".format(**p))
+def test_wgrad_torch_cpu_cross_check(p):
+    torch = pytest.importorskip("torch")
+    x, dy, w = rand_operands(p, 19)
+    xt = torch.from_numpy(x).permute(0, 3, 1, 2)
+    dyt = torch.from_numpy(dy).permute(0, 3, 1, 2)
+    wshape = (p["k"], p["c"] // p["groups"], p["r"], p["s"])
+    dw_t = torch.nn.grad.conv2d_weight(xt, wshape, dyt, stride=p["stride"],
+                                       padding=(p["pad_h"], p["pad_w"]), groups=p["groups"])
+    np.testing.assert_allclose(oracle.conv_wgrad(x, dy, p), dw_t.permute(0, 2, 3, 1).numpy(),
+                               rtol=1e-10, atol=1e-10)
+
+
 def test_refuses_invalid_descriptors():
     bad = [P(1, 4, 4, 4, 4, 3, 3, groups=0), P(1, 4, 4, 4, 4, 3, 3, groups=-4),
            P(1, 4, 4, 6, 4, 3, 3, groups=4), P(1, 4, 4, 4, 4, 3, 3, stride=0),
@@ -315,10 +381,14 @@ def _pins_hold(mutation):
             return False
         if not np.allclose(dx, (A.T @ dy.ravel()).reshape(dx.shape), rtol=1e-12, atol=1e-12):
             return False
+        # weight gradient: <A(w) x, dy> is linear in w with coefficients wgrad(x, dy)
+        dw = oracle.conv_wgrad(x, dy, p, mutation=mutation)
+        if not np.isclose(np.vdot(y, dy), np.vdot(w, dw), rtol=1e-12, atol=1e-12):
+            return False
     return True
 
 
 def test_pins_catch_planted_mistakes():
     assert _pins_hold(0)
-    for m in range(1, 7):
+    for m in range(1, 8):
         assert not _pins_hold(m), "planted mistake %d went unnoticed" % m
