@@ -7,8 +7,8 @@ resident in HBM.  Steps rotate over enough copies of the operands that the
 256 MB Infinity Cache cannot serve a step from the previous one.  HIP events
 on the launch stream bracket exactly K steps after W warm-up steps.
 
-The JSON line also carries, per seeded workload of the method (forward and
-dgrad shapes), the measured time and its fraction of the binding MI355X roof
+The JSON line also carries, per seeded workload of the method (forward, dgrad
+and weight-gradient shapes), the measured time and its fraction of the binding MI355X roof
 (HBM 8 TB/s, dense fp16/bf16 MFMA 2.5 PFLOP/s, fp32 vector 157.3 TFLOP/s), and
 the fp64 CPU oracle timed on a bounded sample of the headline workload.
 
@@ -50,7 +50,10 @@ def parse():
 
 
 def metrics(name):
-    """Algorithmic bytes, nominal and valid flops, and the binding roof of a workload."""
+    """Algorithmic bytes, nominal and valid flops, and the binding roof of a workload.
+
+    Every pass reads two of x, dY, W and writes the third once, and performs
+    the same multiply-adds: the formulas hold for forward, dgrad and wgrad."""
     import oracle
     from convolution_nhwc_amd import synth
     wl = synth.WORKLOADS[name]
@@ -115,21 +118,31 @@ class Workload:
         self.op = wl["op"]
         ho, wo = api.cnhwc_out_dims(p)
         cg = p["c"] // p["groups"]
-        act_shape = (p["n"], p["h"], p["w"], p["c"]) if self.op == "fwd" else (p["n"], ho, wo, p["k"])
-        out_shape = (p["n"], ho, wo, p["k"]) if self.op == "fwd" else (p["n"], p["h"], p["w"], p["c"])
-        (ab, _), (wb, _) = synth.operands(wl["seed"], act_shape, (p["k"], p["r"], p["s"], cg),
-                                          p["dtype"], act_dist=("uniform", -1.0, 1.0),
-                                          w_dist=wl.get("w_dist"), w_fan_in=wl["fan_in"])
+        x_shape, y_shape = (p["n"], p["h"], p["w"], p["c"]), (p["n"], ho, wo, p["k"])
+        w_shape = (p["k"], p["r"], p["s"], cg)
         dev = "cuda"
+        if self.op == "wgrad":
+            # both operands are activations (x, dY) and rotate; the output is dW
+            (ab, _), (bb, _) = synth.wgrad_operands(wl["seed"], x_shape, y_shape, p["dtype"])
+            out_shape = w_shape
+        else:
+            act_shape = x_shape if self.op == "fwd" else y_shape
+            out_shape = y_shape if self.op == "fwd" else x_shape
+            (ab, _), (bb, _) = synth.operands(wl["seed"], act_shape, w_shape,
+                                              p["dtype"], act_dist=("uniform", -1.0, 1.0),
+                                              w_dist=wl.get("w_dist"), w_fan_in=wl["fan_in"])
         a0 = torch.from_numpy(ab.view(np.int16)).to(dev)
-        self.w = torch.from_numpy(wb.view(np.int16)).to(dev)
-        opc = api.OP_FWD if self.op == "fwd" else api.OP_DGRAD
+        b0 = torch.from_numpy(bb.view(np.int16)).to(dev)
+        opc = {"fwd": api.OP_FWD, "dgrad": api.OP_DGRAD, "wgrad": api.OP_WGRAD}[self.op]
         self.opc = opc
         self.kernel, self.variant = api.cnhwc_plan(p, opc)
         self.ws_bytes = api.cnhwc_workspace_size(p, opc)
-        per_set = a0.numel() * 2 + int(np.prod(out_shape)) * 2 + self.ws_bytes
+        rot_b = self.op == "wgrad"
+        per_set = a0.numel() * 2 + (b0.numel() * 2 if rot_b else 0) + \
+            int(np.prod(out_shape)) * 2 + self.ws_bytes
         nsets = int(max(1, min(64, -(-ROTATE_BYTES // per_set))))
         self.acts = [a0] + [a0.clone() for _ in range(nsets - 1)]
+        self.bs = [b0] + [b0.clone() if rot_b else b0 for _ in range(nsets - 1)]
         self.outs = [torch.empty(out_shape, dtype=torch.int16, device=dev) for _ in range(nsets)]
         self.wss = [torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
                     for _ in range(nsets)]
@@ -141,8 +154,9 @@ class Workload:
     def step(self):
         j = self.i % self.nsets
         self.i += 1
-        f = self.api.cnhwc_fwd if self.op == "fwd" else self.api.cnhwc_dgrad
-        f(self.p, self.acts[j].data_ptr(), self.w.data_ptr(), self.outs[j].data_ptr(),
+        f = {"fwd": self.api.cnhwc_fwd, "dgrad": self.api.cnhwc_dgrad,
+             "wgrad": self.api.cnhwc_wgrad}[self.op]
+        f(self.p, self.acts[j].data_ptr(), self.bs[j].data_ptr(), self.outs[j].data_ptr(),
           self.wss[j].data_ptr(), self.ws_bytes, self.stream)
 
 

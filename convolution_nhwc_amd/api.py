@@ -2,7 +2,7 @@
 
 The cnhwc_* functions mirror the C entry points one to one (argument
 marshalling only: every step of the computation runs in the HIP library).
-``fwd`` / ``dgrad`` are conveniences over PyTorch device tensors: torch only
+``fwd`` / ``dgrad`` / ``wgrad`` are conveniences over PyTorch device tensors: torch only
 allocates the outputs and workspace and supplies the current stream.
 
 A problem is a dict with keys n, h, w, c, k, r, s, stride, pad_h, pad_w,
@@ -19,13 +19,14 @@ LIB_PATH = os.path.join(_HERE, "libcnhwc.so")
 
 OK, INVALID_ARG, UNSUPPORTED, WORKSPACE_TOO_SMALL, MISALIGNED, HIP_ERROR = range(6)
 F16, BF16 = 0, 1
-OP_FWD, OP_DGRAD = 1, 2
+OP_FWD, OP_DGRAD, OP_WGRAD = 1, 2, 4
 (VAR_AUTO, VAR_DGRAD_POINTWISE, VAR_DGRAD_IGEMM, VAR_DGRAD_DW_STREAM, VAR_DGRAD_DW_ROTATED,
  VAR_FWD_DIRECT, VAR_FWD_SPLITC, VAR_FWD_GROUPED, VAR_FWD_GENERIC, VAR_DGRAD_GENERIC,
- VAR_DGRAD_DW_TILED, VAR_FWD_DW_TILED, VAR_FWD_DW_ROTATED, VAR_DGRAD_GROUPED) = range(14)
+ VAR_DGRAD_DW_TILED, VAR_FWD_DW_TILED, VAR_FWD_DW_ROTATED, VAR_DGRAD_GROUPED,
+ VAR_WGRAD_GENERIC, VAR_WGRAD_POINTWISE, VAR_WGRAD_SPLITK) = range(17)
 
 SYMBOLS = ("cnhwc_out_dims", "cnhwc_workspace_size", "cnhwc_plan", "cnhwc_chunk_plan",
-           "cnhwc_fwd", "cnhwc_dgrad", "cnhwc_last_error", "cnhwc_set_override")
+           "cnhwc_fwd", "cnhwc_dgrad", "cnhwc_wgrad", "cnhwc_last_error", "cnhwc_set_override")
 
 
 class CnhwcError(RuntimeError):
@@ -75,6 +76,7 @@ def lib():
         L.cnhwc_chunk_plan.argtypes = [P, ctypes.c_int, i64p, ctypes.c_int64, i64p]
         L.cnhwc_fwd.argtypes = [P, vp, vp, vp, vp, sz, vp]
         L.cnhwc_dgrad.argtypes = [P, vp, vp, vp, vp, sz, vp]
+        L.cnhwc_wgrad.argtypes = [P, vp, vp, vp, vp, sz, vp]
         L.cnhwc_last_error.argtypes = []
         L.cnhwc_last_error.restype = ctypes.c_char_p
         L.cnhwc_set_override.argtypes = [ctypes.POINTER(Override)]
@@ -139,6 +141,10 @@ def cnhwc_dgrad(p, dy, w, dx, ws, ws_bytes, stream):
     _check(lib().cnhwc_dgrad(ctypes.byref(_problem(p)), dy, w, dx, ws, ws_bytes, stream))
 
 
+def cnhwc_wgrad(p, x, dy, dw, ws, ws_bytes, stream):
+    _check(lib().cnhwc_wgrad(ctypes.byref(_problem(p)), x, dy, dw, ws, ws_bytes, stream))
+
+
 def cnhwc_set_override(variant=0, cpl=0, split_c=0, chunk_limit_bytes=0, tune=0):
     _check(lib().cnhwc_set_override(ctypes.byref(Override(variant, cpl, split_c, tune,
                                                           chunk_limit_bytes))))
@@ -196,3 +202,19 @@ def dgrad(dy, w, p, dx=None, ws=None):
                 ws.numel() * ws.element_size() if ws is not None else 0,
                 _stream_handle(torch, dy.device))
     return dx
+
+
+def wgrad(x, dy, p, dw=None, ws=None):
+    """dw = weight gradient of device tensors x [N,H,W,C] and dy [N,Ho,Wo,K]."""
+    import torch
+    if dw is None:
+        dw = torch.empty((p["k"], p["r"], p["s"], p["c"] // p.get("groups", 1)),
+                         dtype=_storage_dtype(torch, p), device=x.device)
+    need = cnhwc_workspace_size(p, OP_WGRAD)
+    if ws is None and need:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    cnhwc_wgrad(p, x.data_ptr(), dy.data_ptr(), dw.data_ptr(),
+                ws.data_ptr() if ws is not None else None,
+                ws.numel() * ws.element_size() if ws is not None else 0,
+                _stream_handle(torch, x.device))
+    return dw

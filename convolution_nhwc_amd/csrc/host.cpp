@@ -79,6 +79,10 @@ bool variant_is_dgrad(int v) {
            v == CNHWC_VAR_DGRAD_DW_STREAM || v == CNHWC_VAR_DGRAD_DW_ROTATED ||
            v == CNHWC_VAR_DGRAD_DW_TILED || v == CNHWC_VAR_DGRAD_GENERIC || v == CNHWC_VAR_DGRAD_GROUPED;
 }
+bool variant_is_wgrad(int v) {
+    return v == CNHWC_VAR_WGRAD_GENERIC || v == CNHWC_VAR_WGRAD_POINTWISE || v == CNHWC_VAR_WGRAD_SPLITK;
+}
+bool wgrad_uses_ws(int v) { return v == CNHWC_VAR_WGRAD_POINTWISE || v == CNHWC_VAR_WGRAD_SPLITK; }
 bool variant_is_fwd(int v) {
     return v == CNHWC_VAR_FWD_DIRECT || v == CNHWC_VAR_FWD_SPLITC ||
            v == CNHWC_VAR_FWD_GROUPED || v == CNHWC_VAR_FWD_GENERIC ||
@@ -93,6 +97,8 @@ std::string variant_reason(const Prob& p, int op, int v, int cpl, int split_c) {
         return "variant " + std::to_string(v) + " is not a dgrad kernel";
     if (op == CNHWC_OP_FWD && !variant_is_fwd(v))
         return "variant " + std::to_string(v) + " is not a forward kernel";
+    if (op == CNHWC_OP_WGRAD && !variant_is_wgrad(v))
+        return "variant " + std::to_string(v) + " is not a wgrad kernel";
     switch (v) {
     case CNHWC_VAR_DGRAD_POINTWISE: return dgrad_igemm_reason(p, true);
     case CNHWC_VAR_DGRAD_IGEMM: return dgrad_igemm_reason(p, false);
@@ -105,8 +111,11 @@ std::string variant_reason(const Prob& p, int op, int v, int cpl, int split_c) {
     case CNHWC_VAR_FWD_GROUPED: return fwd_grouped_reason(p);
     case CNHWC_VAR_FWD_DW_TILED: return fwd_dw_tiled_reason(p);
     case CNHWC_VAR_FWD_DW_ROTATED: return fwd_dw_rotated_reason(p);
+    case CNHWC_VAR_WGRAD_POINTWISE: return wgrad_splitk_reason(p, true);
+    case CNHWC_VAR_WGRAD_SPLITK: return wgrad_splitk_reason(p, false);
     case CNHWC_VAR_FWD_GENERIC:
-    case CNHWC_VAR_DGRAD_GENERIC: return "";
+    case CNHWC_VAR_DGRAD_GENERIC:
+    case CNHWC_VAR_WGRAD_GENERIC: return "";
     default: return "unknown variant " + std::to_string(v);
     }
 }
@@ -145,6 +154,13 @@ std::string plan_name(const Prob& p, const Plan& pl) {
     case CNHWC_VAR_FWD_DW_ROTATED:
         std::snprintf(buf, sizeof buf, "fwd_dw_rot_%s_f%lldx%lld_p%dx%d", dt(p),
                       (long long)p.r, (long long)p.s, p.pad_h, p.pad_w); break;
+    case CNHWC_VAR_WGRAD_GENERIC:
+        std::snprintf(buf, sizeof buf, "wgrad_generic_%s", dt(p)); break;
+    case CNHWC_VAR_WGRAD_POINTWISE:
+        std::snprintf(buf, sizeof buf, "wgrad_pointwise_%s+reduce", dt(p)); break;
+    case CNHWC_VAR_WGRAD_SPLITK:
+        std::snprintf(buf, sizeof buf, "wgrad_splitk_%s_f%lldx%lld_s%d+reduce", dt(p), (long long)p.r,
+                      (long long)p.s, p.stride); break;
     default: std::snprintf(buf, sizeof buf, "none");
     }
     return buf;
@@ -154,8 +170,9 @@ std::string plan_name(const Prob& p, const Plan& pl) {
 int choose(const Prob& p, int op, Plan* out) {
     Plan pl;
     const cnhwc_override& ov = g_ov;
-    if (op != CNHWC_OP_FWD && op != CNHWC_OP_DGRAD)
-        return fail(CNHWC_INVALID_ARG, "op must be CNHWC_OP_FWD (1) or CNHWC_OP_DGRAD (2)");
+    if (op != CNHWC_OP_FWD && op != CNHWC_OP_DGRAD && op != CNHWC_OP_WGRAD)
+        return fail(CNHWC_INVALID_ARG,
+                    "op must be CNHWC_OP_FWD (1), CNHWC_OP_DGRAD (2) or CNHWC_OP_WGRAD (4)");
     if (ov.variant != CNHWC_VAR_AUTO) {
         pl.variant = ov.variant;
         pl.cpl = ov.cpl > 0 ? ov.cpl : (ov.variant == CNHWC_VAR_DGRAD_DW_STREAM ? dw_stream_best_cpl(p) : 0);
@@ -182,7 +199,12 @@ int choose(const Prob& p, int op, Plan* out) {
         return true;
     };
     bool ok = false;
-    if (op == CNHWC_OP_DGRAD) {
+    if (op == CNHWC_OP_WGRAD) {
+        if (p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0)
+            ok = take(CNHWC_VAR_WGRAD_POINTWISE, 0, 1);
+        if (!ok) ok = take(CNHWC_VAR_WGRAD_SPLITK, 0, 1);
+        if (!ok) ok = take(CNHWC_VAR_WGRAD_GENERIC, 0, 1);
+    } else if (op == CNHWC_OP_DGRAD) {
         if (is_depthwise(p)) {
             const bool big = p.r > 11 || p.s > 11 || p.r != p.s || p.pad_h != p.pad_w;
             if (p.stride == 1 && big) ok = take(CNHWC_VAR_DGRAD_DW_ROTATED, 0, 1);
@@ -246,6 +268,11 @@ int64_t limit_bytes() { return g_ov.chunk_limit_bytes > 0 ? g_ov.chunk_limit_byt
 // Balanced batch split: the fewest chunks that keep each per-chunk view within
 // the limit, sizes floor(N/chunks) or ceil(N/chunks), larger ones first.
 int plan_chunks(const Prob& p, int op, const Plan& pl, std::vector<int64_t>* counts) {
+    if (op == CNHWC_OP_WGRAD && pl.variant == CNHWC_VAR_WGRAD_GENERIC) {
+        // the plain kernel addresses with 64-bit pointers: one launch
+        counts->assign(1, p.n);
+        return CNHWC_OK;
+    }
     const ChunkBytes b = chunk_bytes(p, op, pl);
     const int64_t lim = limit_bytes();
     if (b.fixed > kBufferLimit)
@@ -344,6 +371,94 @@ int run(const cnhwc_problem* prob, int op, const void* in, const void* w, void* 
     return CNHWC_OK;
 }
 
+// Split-K wgrad: pixel splits of each chunk and their total.
+int64_t wgrad_total_splits(const Prob& p, const Plan& pl, const std::vector<int64_t>& counts,
+                           std::vector<int>* per_chunk) {
+    int64_t total = 0;
+    if (per_chunk) per_chunk->clear();
+    for (int64_t cnt : counts) {
+        Prob pc = p;
+        pc.n = cnt;
+        const int s = wgrad_splits(pc, pl.tune);
+        if (per_chunk) per_chunk->push_back(s);
+        total += s;
+    }
+    return total;
+}
+
+int64_t workspace_bytes(const Prob& p, int op, const Plan& pl, const std::vector<int64_t>& counts) {
+    if (op == CNHWC_OP_WGRAD)
+        return wgrad_uses_ws(pl.variant) ? wgrad_total_splits(p, pl, counts, nullptr) * wgrad_split_elems(p) * 4
+                                         : 0;
+    const int64_t mx = *std::max_element(counts.begin(), counts.end());
+    return chunk_bytes(p, op, pl).ws_per_image * mx;
+}
+
+int run_wgrad(const cnhwc_problem* prob, const void* x, const void* dy, void* dw, void* ws,
+              size_t ws_bytes, void* stream) {
+    Prob p;
+    int st = validate(prob, &p);
+    if (st) return st;
+    Plan pl;
+    if ((st = choose(p, CNHWC_OP_WGRAD, &pl))) return st;
+    if ((st = check_ptr(x, "x"))) return st;
+    if ((st = check_ptr(dy, "dy"))) return st;
+    if ((st = check_ptr(dw, "dw"))) return st;
+    const int64_t x_bytes = p.n * p.h * p.w * p.c * 2;
+    const int64_t dy_bytes = p.n * p.ho * p.wo * p.k * 2;
+    const int64_t w_bytes = p.k * p.r * p.s * p.cg * 2;
+    if (overlap(dw, w_bytes, x, x_bytes) || overlap(dw, w_bytes, dy, dy_bytes))
+        return fail(CNHWC_INVALID_ARG, "dw overlaps an input");
+    std::vector<int64_t> counts;
+    if ((st = plan_chunks(p, CNHWC_OP_WGRAD, pl, &counts))) return st;
+    const int64_t need_ws = workspace_bytes(p, CNHWC_OP_WGRAD, pl, counts);
+    if (need_ws > 0) {
+        if ((st = check_ptr(ws, "ws"))) return st;
+        if (int64_t(ws_bytes) < need_ws)
+            return fail(CNHWC_WORKSPACE_TOO_SMALL, "workspace needs " + std::to_string(need_ws) +
+                                                       " bytes, got " + std::to_string(ws_bytes));
+        if (overlap(ws, need_ws, x, x_bytes) || overlap(ws, need_ws, dy, dy_bytes) ||
+            overlap(ws, need_ws, dw, w_bytes))
+            return fail(CNHWC_INVALID_ARG, "workspace overlaps a tensor");
+    }
+    hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    auto launched = [&](const char* what) -> int {
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess)
+            return fail(CNHWC_HIP_ERROR, std::string("launch of ") + what + " failed: " + hipGetErrorString(e));
+        return CNHWC_OK;
+    };
+    if (pl.variant == CNHWC_VAR_WGRAD_GENERIC) {
+        int rc = launch_wgrad_generic(p, x, dy, dw, s);
+        if (rc) return fail(rc, "launcher for " + pl.name + " refused the problem");
+        if ((rc = launched(pl.name.c_str()))) return rc;
+        g_err.clear();
+        return CNHWC_OK;
+    }
+    std::vector<int> splits;
+    const int64_t total = wgrad_total_splits(p, pl, counts, &splits);
+    float* wsf = static_cast<float*>(ws);
+    const int64_t x_img = x_bytes / p.n, dy_img = dy_bytes / p.n;
+    int64_t first = 0, split_base = 0;
+    for (size_t i = 0; i < counts.size(); ++i) {
+        Prob pc = p;
+        pc.n = counts[i];
+        const char* xp = static_cast<const char*>(x) + first * x_img;
+        const char* yp = static_cast<const char*>(dy) + first * dy_img;
+        int rc = launch_wgrad_splitk(pc, pl, xp, yp, wsf + split_base * wgrad_split_elems(p), splits[i], s);
+        if (rc) return fail(rc, "launcher for " + pl.name + " refused the chunk");
+        if ((rc = launched(pl.name.c_str()))) return rc;
+        first += counts[i];
+        split_base += splits[i];
+    }
+    int rc = launch_wgrad_reduce(p, int(total), wsf, dw, s);
+    if (rc) return fail(rc, "wgrad reduce refused the problem");
+    if ((rc = launched("wgrad_reduce"))) return rc;
+    g_err.clear();
+    return CNHWC_OK;
+}
+
 }  // namespace
 }  // namespace cnhwc
 
@@ -369,8 +484,7 @@ int cnhwc_workspace_size(const cnhwc_problem* prob, int op, size_t* bytes) {
     if ((st = choose(p, op, &pl))) return st;
     std::vector<int64_t> counts;
     if ((st = plan_chunks(p, op, pl, &counts))) return st;
-    const int64_t mx = *std::max_element(counts.begin(), counts.end());
-    if (bytes) *bytes = size_t(chunk_bytes(p, op, pl).ws_per_image * mx);
+    if (bytes) *bytes = size_t(workspace_bytes(p, op, pl, counts));
     g_err.clear();
     return CNHWC_OK;
 }
@@ -413,6 +527,11 @@ int cnhwc_fwd(const cnhwc_problem* prob, const void* x, const void* w, void* y, 
 int cnhwc_dgrad(const cnhwc_problem* prob, const void* dy, const void* w, void* dx, void* ws,
                 size_t ws_bytes, void* hip_stream) {
     return run(prob, CNHWC_OP_DGRAD, dy, w, dx, ws, ws_bytes, hip_stream);
+}
+
+int cnhwc_wgrad(const cnhwc_problem* prob, const void* x, const void* dy, void* dw, void* ws,
+                size_t ws_bytes, void* hip_stream) {
+    return run_wgrad(prob, x, dy, dw, ws, ws_bytes, hip_stream);
 }
 
 const char* cnhwc_last_error(void) { return g_err.c_str(); }

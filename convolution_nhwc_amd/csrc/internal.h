@@ -68,6 +68,18 @@ int launch_fwd_dw_tiled(const Prob& p, const Plan& pl, const void* x, const void
 int launch_fwd_dw_rotated(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                           hipStream_t st);
 
+// Weight gradient.  Split-K MFMA kernel (one chunk: fp32 partials of `splits`
+// pixel splits into ws[split][K][R][S][Cg]), the reduce pass over all splits
+// of all chunks, and the plain kernel (whole batch, 64-bit addressing).
+int launch_wgrad_splitk(const Prob& p, const Plan& pl, const void* x, const void* dy, float* ws,
+                        int splits, hipStream_t st);
+int launch_wgrad_reduce(const Prob& p, int splits, const float* ws, void* dw, hipStream_t st);
+int launch_wgrad_generic(const Prob& p, const void* x, const void* dy, void* dw, hipStream_t st);
+// Pixel splits of one chunk (tune > 0 forces that many) and the elements of
+// one split's partial tile (K*R*S*Cg).
+int wgrad_splits(const Prob& p, int tune);
+int64_t wgrad_split_elems(const Prob& p);
+
 // ---- per-variant acceptance (empty string = accepted, else the reason) ------
 std::string dgrad_igemm_reason(const Prob& p, bool pointwise);
 std::string dw_stream_reason(const Prob& p, int cpl);
@@ -77,6 +89,7 @@ std::string fwd_dw_tiled_reason(const Prob& p);
 std::string dgrad_grouped_reason(const Prob& p);
 std::string fwd_dw_rotated_reason(const Prob& p);
 std::string fwd_direct_reason(const Prob& p, int split_c);
+std::string wgrad_splitk_reason(const Prob& p, bool pointwise);
 std::string fwd_grouped_reason(const Prob& p);
 std::string fwd_window_reason(const Prob& p, int split_c);
 int fwd_window_auto_split(const Prob& p);

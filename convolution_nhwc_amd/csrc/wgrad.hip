@@ -1,0 +1,420 @@
+// Weight gradient (wgrad): the derivative of the forward map with respect to
+// the weight, the third convolution pass beside forward and dgrad ("perf(rocke/
+// conv): add the pointwise fast path dgrad was missing", Motivation: forward
+// and wgrad both special-case 1x1 convolutions).
+//
+//   dW[k][r][t][j] = sum over output pixels m = (n, ho, wo) of
+//                    dY[m][k] * x[n, ho*s - pad_h + r, wo*s - pad_w + t, g*Cg + j],  g = k / Kg
+//
+// (x read as zero outside the image).  Per filter tap (r, t) this is a GEMM
+// dW_tap[k][j] = sum_m dY[m][k] * X_tap[m][j] whose reduction runs over all
+// N*Ho*Wo output pixels: deep and narrow, so the pixels are split across
+// blocks (split-K) and each block writes an fp32 partial tile to a workspace
+// [split][K][R][S][Cg]; a second pass sums the splits in ascending order and
+// rounds once (round to nearest even) to fp16 / bf16.
+//
+// Split-K kernel data path (gfx950): one block per (group, 128-channel k
+// block, tap, j block of 64 or 128 input channels) and pixel split.  It
+// streams its split 32 output pixels at a time: the dY rows (k slice) and the
+// tap's input rows (j slice, gathered pixel by pixel, zero outside the image
+// through the buffer range check) go global -> LDS by LDS-direct DMA into a
+// four-stage ring, so three stages are in flight while one is multiplied.
+// Both tiles keep pixels as rows, exactly as they lie in memory; the MFMA
+// operands (eight consecutive pixels of one channel per lane) come from the
+// LDS transpose read (ds_read_b64_tr_b16).  The 16-byte chunks of each row are
+// XOR-swizzled by row at the source (the DMA writes LDS linearly) so that the
+// 16 rows one transpose read touches fall on distinct bank groups.  The MFMA
+// computes the transposed product (j x k), so each lane ends with four
+// consecutive j of one k: one 16-byte fp32 store per tile fragment.
+//
+// The 1x1 stride-1 unpadded case is the same kernel with the gather dropped:
+// the input row of output pixel m is row m itself (offset m*C + g*Cg + j, as
+// the fast-path commit on the first page states for the pointwise offsets),
+// so no division by Ho*Wo and Wo is made per row.  Same reduction order, same
+// rounding: bit-identical to the general kernel on the same problem.
+//
+// A plain one-weight-per-lane kernel covers every other valid problem.
+#include "device.h"
+#include "internal.h"
+
+#include <algorithm>
+#include <string>
+
+namespace cnhwc {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kWBK = 128;        // output channels (k) per block
+constexpr int kWBM = 32;         // output pixels per stage (one MFMA depth)
+constexpr int kWStages = 4;
+
+struct WgArgs {
+    const void* x;
+    const void* dy;
+    float* ws;                   // this chunk's first split
+    uint32_t x_bytes, dy_bytes;
+    int N, H, W, C, K, R, S, stride, pad_h, pad_w, Ho, Wo, Cg, Kg;
+    int P;                       // output pixels of the chunk
+    int kblocks, jblocks, tiles; // per group: ceil(Kg/128), ceil(Cg/BJ); all tiles
+    int splits;                  // pixel splits of the chunk
+    int remap;                   // 1: deal logical blocks to XCDs in contiguous runs
+    FastDiv div_hw, div_w;       // by Ho*Wo, by Wo
+    int64_t split_elems;         // K*R*S*Cg (workspace stride of one split)
+};
+
+// Source-side chunk swizzle of a stage row.  A transpose read touches rows
+// 8f + 4h + i (f, i = 0..3) of one 32-byte chunk pair; the value XOR-ed into
+// the chunk index spreads those 16 rows over 8 distinct pair positions (256 B
+// rows) or, with 128 B rows, over 4 positions x the two row parities.
+template <int CHUNKS>
+__device__ inline int wswz(int row) {
+    if constexpr (CHUNKS == 16) return 2 * ((row & 3) | ((row >> 1) & 4));
+    else return 2 * (((row >> 1) & 1) | ((row >> 2) & 2));
+}
+
+template <typename T, int BJ, bool PW>
+__global__ __launch_bounds__(kThreads, 2) void wgrad_splitk_kernel(const WgArgs a) {
+    constexpr int WAVES_J = BJ / 64;                 // 1 or 2
+    constexpr int WAVES_K = 4 / WAVES_J;             // 4 or 2
+    constexpr int WJT = 4;                           // 16-wide j tiles per wave
+    constexpr int WKT = kWBK / (WAVES_K * 16);       // 16-wide k tiles per wave: 2 or 4
+    constexpr int XROW = BJ * 2;                     // bytes of one input row in a stage
+    constexpr int XCH = BJ / 8;                      // 16-byte chunks per input row
+    constexpr int YROW = kWBK * 2;                   // bytes of one dY row in a stage
+    constexpr int YCH = kWBK / 8;
+    constexpr int XBYTES = kWBM * XROW;
+    constexpr int STAGE = XBYTES + kWBM * YROW;
+    constexpr int XD = XBYTES / 1024;                // 1 KB DMAs of the input tile
+    constexpr int ND = STAGE / 1024;
+    constexpr int LPS = ND / 4;                      // DMAs per wave per stage
+    static_assert(ND % 4 == 0, "stage must split evenly over the four waves");
+    __shared__ __attribute__((aligned(1024))) unsigned char lds[kWStages * STAGE];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    // wave index as a scalar: the DMA roles below branch on it, and each wave
+    // must issue exactly LPS loads per stage for the vmcnt waits to hold
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int frow = lane & 15, fgrp = lane >> 4;
+
+    // ---- block -> (split, group, k block, tap, j block) ----
+    int bid = blockIdx.x;
+    if (a.remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+    const int split = bid / a.tiles;
+    int tile = bid - split * a.tiles;
+    const int jb = tile % a.jblocks;
+    tile /= a.jblocks;
+    const int RS = a.R * a.S;
+    const int tap = tile % RS;
+    tile /= RS;
+    const int kb = tile % a.kblocks;
+    const int g = tile / a.kblocks;
+    const int r = tap / a.S, t = tap - r * a.S;
+    const int m_begin = int(int64_t(split) * a.P / a.splits);
+    const int m_end = int(int64_t(split + 1) * a.P / a.splits);
+    const int nsteps = (m_end - m_begin + kWBM - 1) / kWBM;
+
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
+
+    // ---- per-lane DMA roles: DMA q = wave*LPS + d covers bytes [1024q, 1024q+1024) of a stage ----
+    int d_row[LPS];              // stage row (pixel 0..31)
+    uint32_t d_chan[LPS];        // channel byte offset within the pixel, or kOob
+    bool d_isx[LPS];
+#pragma unroll
+    for (int d = 0; d < LPS; ++d) {
+        const int q = wave * LPS + d;
+        if (q < XD) {
+            const int row = q * (1024 / XROW) + lane / XCH;
+            const int chunk = (lane % XCH) ^ wswz<XCH>(row);
+            const int j = jb * BJ + chunk * 8;
+            d_row[d] = row;
+            d_isx[d] = true;
+            d_chan[d] = j < a.Cg ? uint32_t((g * a.Cg + j) * 2) : kOob;
+        } else {
+            const int row = (q - XD) * (1024 / YROW) + lane / YCH;
+            const int chunk = (lane % YCH) ^ wswz<YCH>(row);
+            const int k = kb * kWBK + chunk * 8;
+            d_row[d] = row;
+            d_isx[d] = false;
+            d_chan[d] = k < a.Kg ? uint32_t((g * a.Kg + k) * 2) : kOob;
+        }
+    }
+    // issue the loads of stage slot SL for pixels m0 .. m0+31
+    auto issue = [&](auto slot, int m0) {
+        constexpr int SL = decltype(slot)::value;
+#pragma unroll
+        for (int d = 0; d < LPS; ++d) {
+            const int m = m0 + d_row[d];
+            unsigned char* dst = lds + SL * STAGE + (wave * LPS + d) * 1024;
+            if (d_isx[d]) {
+                uint32_t off = kOob;
+                if constexpr (PW) {
+                    if (m < m_end && d_chan[d] != kOob) off = uint32_t(m) * uint32_t(a.C * 2) + d_chan[d];
+                } else {
+                    const int n = fdiv(m, a.div_hw);
+                    const int rem = m - n * (a.Ho * a.Wo);
+                    const int ho = fdiv(rem, a.div_w);
+                    const int wo = rem - ho * a.Wo;
+                    const int h = ho * a.stride - a.pad_h + r;
+                    const int w = wo * a.stride - a.pad_w + t;
+                    const bool ok = m < m_end && d_chan[d] != kOob && h >= 0 && h < a.H && w >= 0 &&
+                                    w < a.W;
+                    if (ok) off = uint32_t(((n * a.H + h) * a.W + w) * a.C) * 2u + d_chan[d];
+                }
+                dma16(rx, dst, off, 0);
+            } else {
+                const uint32_t off = (m < m_end && d_chan[d] != kOob)
+                                         ? uint32_t(m) * uint32_t(a.K * 2) + d_chan[d]
+                                         : kOob;
+                dma16(rdy, dst, off, 0);
+            }
+        }
+    };
+
+    // ---- fragment read addresses (within a stage): lane (frow, fgrp), half h
+    // of the 8 pixels fgrp*8.., reads pixel row fgrp*8 + 4h + frow/4, channels
+    // tile*16 + 4*(frow%4) .. +3; the transpose hands it 4 pixels of channel
+    // tile*16 + frow ----
+    const int wj = wave % WAVES_J, wk = wave / WAVES_J;
+    const uint32_t lds0 = lds_addr(lds);
+    uint32_t xa[WJT][2], ya[WKT][2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+        const int row = fgrp * 8 + 4 * h + (frow >> 2);
+#pragma unroll
+        for (int jt = 0; jt < WJT; ++jt) {
+            const int j = wj * 64 + jt * 16 + 4 * (frow & 3);
+            xa[jt][h] = lds0 + row * XROW + (((j >> 3) ^ wswz<XCH>(row)) << 4) + (j & 7) * 2;
+        }
+#pragma unroll
+        for (int kt = 0; kt < WKT; ++kt) {
+            const int k = wk * (WKT * 16) + kt * 16 + 4 * (frow & 3);
+            ya[kt][h] = lds0 + XBYTES + row * YROW + (((k >> 3) ^ wswz<YCH>(row)) << 4) + (k & 7) * 2;
+        }
+    }
+
+    f32x4 acc[WJT][WKT];
+#pragma unroll
+    for (int i = 0; i < WJT; ++i)
+#pragma unroll
+        for (int j = 0; j < WKT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    // multiply the stage in slot SL
+    auto compute = [&](auto slot) {
+        constexpr int SL = decltype(slot)::value;
+        i32x2 fx[WJT][2], fy[WKT][2];
+#pragma unroll
+        for (int jt = 0; jt < WJT; ++jt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                             : "=v"(fx[jt][h]) : "v"(xa[jt][h]), "i"(SL * STAGE));
+#pragma unroll
+        for (int kt = 0; kt < WKT; ++kt)
+#pragma unroll
+            for (int h = 0; h < 2; ++h)
+                asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2"
+                             : "=v"(fy[kt][h]) : "v"(ya[kt][h]), "i"(SL * STAGE));
+        asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+        for (int jt = 0; jt < WJT; ++jt) {
+            asm volatile("" : "+v"(fx[jt][0]), "+v"(fx[jt][1]));
+            const i32x4 av = {fx[jt][0][0], fx[jt][0][1], fx[jt][1][0], fx[jt][1][1]};
+#pragma unroll
+            for (int kt = 0; kt < WKT; ++kt) {
+                if (jt == 0) asm volatile("" : "+v"(fy[kt][0]), "+v"(fy[kt][1]));
+                const i32x4 bv = {fy[kt][0][0], fy[kt][0][1], fy[kt][1][0], fy[kt][1][1]};
+                acc[jt][kt] = mfma16x16x32<T>(av, bv, acc[jt][kt]);
+            }
+        }
+    };
+
+    // ---- ring: stages 0..2 in flight before the first multiply ----
+    sfor<kWStages - 1>([&](auto sc) { issue(sc, m_begin + decltype(sc)::value * kWBM); });
+    for (int s0 = 0; s0 < nsteps; s0 += kWStages) {
+        sfor<kWStages>([&](auto sc) {
+            constexpr int SL = decltype(sc)::value;
+            const int s = s0 + SL;
+            if (s < nsteps) {
+                wait_vm<(kWStages - 2) * LPS>();
+                __builtin_amdgcn_s_barrier();
+                // the slot freed by the previous stage takes stage s + 3
+                issue(IC<(SL + kWStages - 1) % kWStages>{}, m_begin + (s + kWStages - 1) * kWBM);
+                compute(IC<SL>{});
+            }
+        });
+    }
+    wait_vm<0>();   // no DMA may still be writing LDS when the block retires
+
+    // ---- fp32 partials: lane holds j rows 4*fgrp..+3 of k column frow ----
+    float* wsp = a.ws + int64_t(split) * a.split_elems;
+#pragma unroll
+    for (int kt = 0; kt < WKT; ++kt) {
+        const int k = kb * kWBK + wk * (WKT * 16) + kt * 16 + frow;
+        if (k >= a.Kg) continue;
+        float* rowp = wsp + (int64_t(g * a.Kg + k) * RS + tap) * a.Cg;
+#pragma unroll
+        for (int jt = 0; jt < WJT; ++jt) {
+            const int j = jb * BJ + wj * 64 + jt * 16 + 4 * fgrp;
+            if (j < a.Cg) *reinterpret_cast<f32x4*>(rowp + j) = acc[jt][kt];
+        }
+    }
+}
+
+// dw[i] = round(sum over splits s = 0, 1, ... of ws[s][i]), four elements per lane.
+template <typename T>
+__global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ ws,
+                                                           unsigned short* __restrict__ dw,
+                                                           int64_t total4, int64_t stride4,
+                                                           int splits) {
+    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total4;
+         i += int64_t(gridDim.x) * blockDim.x) {
+        const f32x4* src = reinterpret_cast<const f32x4*>(ws) + i;
+        f32x4 s = src[0];
+        for (int sp0 = 1; sp0 < splits; sp0 += 8) {
+            f32x4 v[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (sp0 + j < splits) v[j] = src[(sp0 + j) * stride4];
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+                if (sp0 + j < splits) {
+                    s[0] += v[j][0]; s[1] += v[j][1]; s[2] += v[j][2]; s[3] += v[j][3];
+                }
+        }
+        i32x2 o = {int(pack2<T>(s[0], s[1])), int(pack2<T>(s[2], s[3]))};
+        *(reinterpret_cast<i32x2*>(dw) + i) = o;
+    }
+}
+
+// One weight element per lane, pixels in (n, ho, wo) order, fp32 accumulation.
+template <typename T>
+__global__ __launch_bounds__(256) void wgrad_generic_kernel(
+    const unsigned short* __restrict__ x, const unsigned short* __restrict__ dy,
+    unsigned short* __restrict__ dw, int64_t total, int N, int H, int W, int C, int K, int R, int S,
+    int stride, int pad_h, int pad_w, int Ho, int Wo, int Cg, int Kg) {
+    const int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    if (i >= total) return;
+    const int j = int(i % Cg);
+    int64_t q = i / Cg;
+    const int t = int(q % S);
+    q /= S;
+    const int r = int(q % R);
+    const int k = int(q / R);
+    const int g = k / Kg;
+    float acc = 0.f;
+    for (int n = 0; n < N; ++n)
+        for (int ho = 0; ho < Ho; ++ho) {
+            const int h = ho * stride - pad_h + r;
+            if (h < 0 || h >= H) continue;
+            for (int wo = 0; wo < Wo; ++wo) {
+                const int w = wo * stride - pad_w + t;
+                if (w < 0 || w >= W) continue;
+                acc += to_f32<T>(dy[((int64_t(n) * Ho + ho) * Wo + wo) * K + k]) *
+                       to_f32<T>(x[((int64_t(n) * H + h) * W + w) * C + g * Cg + j]);
+            }
+        }
+    dw[i] = pack1<T>(acc);
+}
+
+int wg_bj(const Prob& p) { return p.cg >= 128 ? 128 : 64; }
+
+int64_t wg_tiles(const Prob& p) {
+    const int bj = wg_bj(p);
+    return int64_t(p.groups) * ((p.kg + kWBK - 1) / kWBK) * p.r * p.s * ((p.cg + bj - 1) / bj);
+}
+
+}  // namespace
+
+std::string wgrad_splitk_reason(const Prob& p, bool pointwise) {
+    if (pointwise && !(p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0))
+        return "pointwise wgrad needs a 1x1 filter, stride 1 and no padding";
+    if (p.cg % 8 != 0 || p.kg % 8 != 0)
+        return "needs C/groups and K/groups multiples of 8 (16-byte rows)";
+    if (p.cg < 16 || p.kg < 16)
+        return "needs at least 16 channels per group on each side (MFMA tile)";
+    if (p.ho * p.wo > (int64_t(1) << 30) || p.h * p.w > (int64_t(1) << 30))
+        return "feature map too large for the kernel's 32-bit pixel indices";
+    return "";
+}
+
+int wgrad_splits(const Prob& p, int tune) {
+    if (tune > 0) return int(std::min<int64_t>(tune, p.n * p.ho * p.wo));
+    const int64_t tiles = wg_tiles(p);
+    const int64_t P = p.n * p.ho * p.wo;
+    // two blocks per compute unit, every split at least 8 stages deep
+    int64_t s = std::max<int64_t>(1, (2 * kNumCUs + tiles - 1) / tiles);
+    s = std::min<int64_t>(s, std::max<int64_t>(1, P / (8 * kWBM)));
+    // a multiple of 8 blocks lets the XCD remap deal contiguous runs
+    while ((s * tiles) % 8 != 0 && (s + 1) <= P / kWBM && s < 4 * (2 * kNumCUs)) ++s;
+    return int(s);
+}
+
+int64_t wgrad_split_elems(const Prob& p) { return p.k * p.r * p.s * p.cg; }
+
+int launch_wgrad_splitk(const Prob& p, const Plan& pl, const void* x, const void* dy, float* ws,
+                        int splits, hipStream_t st) {
+    WgArgs a;
+    a.x = x; a.dy = dy; a.ws = ws;
+    a.x_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
+    a.dy_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
+    a.N = int(p.n); a.H = int(p.h); a.W = int(p.w); a.C = int(p.c); a.K = int(p.k);
+    a.R = int(p.r); a.S = int(p.s); a.stride = p.stride; a.pad_h = p.pad_h; a.pad_w = p.pad_w;
+    a.Ho = int(p.ho); a.Wo = int(p.wo); a.Cg = int(p.cg); a.Kg = int(p.kg);
+    a.P = int(p.n * p.ho * p.wo);
+    const int bj = wg_bj(p);
+    a.kblocks = int((p.kg + kWBK - 1) / kWBK);
+    a.jblocks = int((p.cg + bj - 1) / bj);
+    a.tiles = int(wg_tiles(p));
+    a.splits = splits;
+    a.div_hw = make_fastdiv(uint32_t(p.ho * p.wo));
+    a.div_w = make_fastdiv(uint32_t(p.wo));
+    a.split_elems = wgrad_split_elems(p);
+    const int64_t blocks = int64_t(a.tiles) * splits;
+    if (blocks > (int64_t(1) << 31) - 1) return CNHWC_UNSUPPORTED;
+    a.remap = blocks % 8 == 0 ? 1 : 0;
+    const bool pw = pl.variant == CNHWC_VAR_WGRAD_POINTWISE;
+    const bool bf = p.dtype == CNHWC_BF16;
+#define CNHWC_WG(T, BJ, PW) hipLaunchKernelGGL((wgrad_splitk_kernel<T, BJ, PW>), dim3(unsigned(blocks)), \
+                                               dim3(kThreads), 0, st, a)
+    if (bj == 128) {
+        if (pw) { if (bf) CNHWC_WG(BF16, 128, true); else CNHWC_WG(F16, 128, true); }
+        else { if (bf) CNHWC_WG(BF16, 128, false); else CNHWC_WG(F16, 128, false); }
+    } else {
+        if (pw) { if (bf) CNHWC_WG(BF16, 64, true); else CNHWC_WG(F16, 64, true); }
+        else { if (bf) CNHWC_WG(BF16, 64, false); else CNHWC_WG(F16, 64, false); }
+    }
+#undef CNHWC_WG
+    return CNHWC_OK;
+}
+
+int launch_wgrad_reduce(const Prob& p, int splits, const float* ws, void* dw, hipStream_t st) {
+    const int64_t total4 = wgrad_split_elems(p) / 4;
+    const int64_t blocks = std::min<int64_t>((total4 + 255) / 256, 8 * kNumCUs);
+    auto* out = static_cast<unsigned short*>(dw);
+    if (p.dtype == CNHWC_BF16)
+        hipLaunchKernelGGL(wgrad_reduce_kernel<BF16>, dim3(unsigned(blocks)), dim3(256), 0, st, ws,
+                           out, total4, total4, splits);
+    else
+        hipLaunchKernelGGL(wgrad_reduce_kernel<F16>, dim3(unsigned(blocks)), dim3(256), 0, st, ws,
+                           out, total4, total4, splits);
+    return CNHWC_OK;
+}
+
+int launch_wgrad_generic(const Prob& p, const void* x, const void* dy, void* dw, hipStream_t st) {
+    const int64_t total = wgrad_split_elems(p);
+    const unsigned blocks = unsigned((total + 255) / 256);
+    auto* xs = static_cast<const unsigned short*>(x);
+    auto* ys = static_cast<const unsigned short*>(dy);
+    auto* out = static_cast<unsigned short*>(dw);
+#define CNHWC_WGG(T) hipLaunchKernelGGL(wgrad_generic_kernel<T>, dim3(blocks), dim3(256), 0, st, xs, ys, \
+                                        out, total, int(p.n), int(p.h), int(p.w), int(p.c), int(p.k),     \
+                                        int(p.r), int(p.s), p.stride, p.pad_h, p.pad_w, int(p.ho),        \
+                                        int(p.wo), int(p.cg), int(p.kg))
+    if (p.dtype == CNHWC_BF16) CNHWC_WGG(BF16);
+    else CNHWC_WGG(F16);
+#undef CNHWC_WGG
+    return CNHWC_OK;
+}
+
+}  // namespace cnhwc

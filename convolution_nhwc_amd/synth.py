@@ -5,8 +5,9 @@ types; it holds none of the convolution's arithmetic (no output sizes, no
 index maps).  Callers pass every shape explicitly.
 
 Draw order, distributions and seeds for the named workloads are in
-``WORKLOADS``: activations first (x for forward, dY for dgrad), then weights,
-from one ``numpy.random.Generator(PCG64(seed))``; activations are
+``WORKLOADS``: activations first (x for forward, dY for dgrad), then weights
+(for the weight gradient: x, then dY), from one
+``numpy.random.Generator(PCG64(seed))``; activations are
 uniform[-1, 1], weights normal with standard deviation 1/sqrt(fan_in).  Values
 are drawn in float64 and rounded to fp16 (numpy's round-to-nearest-even) or to
 bf16 (to float32 first, then to bf16, both round-to-nearest-even).  The same
@@ -84,13 +85,22 @@ def operands(seed, act_shape, w_shape, dtype, act_dist=("uniform", -1.0, 1.0),
     return round_to(a, dtype), round_to(w, dtype)
 
 
+def wgrad_operands(seed, x_shape, dy_shape, dtype, dist=("uniform", -1.0, 1.0)):
+    """The two activation operands of the weight gradient, x then dY, each as
+    (bits, exact f64 values), both drawn from ``dist``."""
+    rng = generator(seed)
+    x = draw(rng, x_shape, dist)
+    dy = draw(rng, dy_shape, dist)
+    return round_to(x, dtype), round_to(dy, dtype)
+
+
 def problem(n, h, w, c, k, r, s, stride=1, pad_h=0, pad_w=0, groups=1, dtype=F16):
     return dict(n=n, h=h, w=w, c=c, k=k, r=r, s=s, stride=stride, pad_h=pad_h,
                 pad_w=pad_w, groups=groups, dtype=dtype)
 
 
 # The seeded workloads: the five families of shapes the method is measured on.
-# op is "dgrad" or "fwd"; fan_in sets the weight standard deviation.
+# op is "dgrad", "fwd" or "wgrad"; fan_in sets the weight standard deviation.
 WORKLOADS = {
     "c1_pointwise_tiny": dict(op="dgrad", seed=1, fan_in=None,
                               w_dist=("uniform", -1.0, 1.0),
@@ -125,4 +135,10 @@ WORKLOADS = {
     "f2_grouped_dgrad": dict(op="dgrad", seed=71, fan_in=8 * 9,
                              prob=problem(32, 28, 28, 256, 256, 3, 3, 1, 1, 1, groups=32,
                                           dtype=BF16)),
+    # weight gradient (the third next row): the pointwise and 3x3 dgrad shapes,
+    # backward weights; x and dY both uniform[-1, 1] (wgrad_operands)
+    "f3_wgrad_pointwise": dict(op="wgrad", seed=81, fan_in=None,
+                               prob=problem(32, 56, 56, 64, 256, 1, 1)),
+    "f3_wgrad_3x3": dict(op="wgrad", seed=82, fan_in=None,
+                         prob=problem(32, 28, 28, 256, 256, 3, 3, 1, 1, 1)),
 }

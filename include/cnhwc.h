@@ -1,11 +1,14 @@
 /*
  * cnhwc.h -- C ABI of the gfx950 (MI355X) NHWC convolution library libcnhwc.so.
  *
- * Two passes of 2D convolution over fp16 or bf16 tensors with fp32
+ * Three passes of 2D convolution over fp16 or bf16 tensors with fp32
  * accumulation and one round-to-nearest-even rounding of each output element:
  *
  *   forward   y[n,ho,wo,k] = sum_{r,t,j} x[n, ho*s-pad_h+r, wo*s-pad_w+t, g*Cg+j] * w[k,r,t,j]
- *   dgrad     dx = the adjoint of that map applied to dy
+ *   dgrad     dx = the adjoint of that map (in x) applied to dy
+ *   wgrad     dw[k,r,t,j] = sum_{n,ho,wo} dy[n,ho,wo,k] * x[n, ho*s-pad_h+r, wo*s-pad_w+t, g*Cg+j]
+ *             (the adjoint of the map in w; the first page names it beside
+ *             forward and dgrad as the pass that already had a 1x1 fast path)
  *
  * (cross-correlation, no filter flip; g = k / Kg, Cg = C/groups, Kg = K/groups;
  * x is zero outside the image).  The operations are those of three rocKE pull
@@ -17,11 +20,11 @@
  * dgrad" (row-streaming and rotated-filter depthwise dgrad, per-axis padding).
  *
  * Layouts (all dense, row-major, 16-byte-aligned base pointers):
- *   x, dx  [N][H][W][C]          y, dy  [N][Ho][Wo][K]          w  [K][R][S][C/groups]
+ *   x, dx  [N][H][W][C]          y, dy  [N][Ho][Wo][K]          w, dw  [K][R][S][C/groups]
  *   Ho = floor((H + 2*pad_h - R) / stride) + 1,  Wo = floor((W + 2*pad_w - S) / stride) + 1.
  *
  * Conventions shared by every entry point:
- *   - Pointers passed to cnhwc_fwd / cnhwc_dgrad are DEVICE pointers on the
+ *   - Pointers passed to cnhwc_fwd / cnhwc_dgrad / cnhwc_wgrad are DEVICE pointers on the
  *     current HIP device.  The caller allocates and owns every buffer,
  *     including the workspace; the library never allocates, frees or
  *     synchronises.  Inputs are read only; outputs are fully overwritten
@@ -59,9 +62,10 @@ extern "C" {
 #define CNHWC_BF16 1
 
 /* Pass numbers follow MIOpen's -F direction codes the first page's driver
- * parses: 1 = forward, 2 = backward data. */
+ * parses: 1 = forward, 2 = backward data, 4 = backward weights. */
 #define CNHWC_OP_FWD 1
 #define CNHWC_OP_DGRAD 2
+#define CNHWC_OP_WGRAD 4
 
 /* Problem descriptor: the fields rocKE's DirectConvProblem carries (N, H, W,
  * C, K, filter rows R = KH, filter columns S = KW, stride, padding, groups),
@@ -97,13 +101,21 @@ typedef struct cnhwc_problem {
 #define CNHWC_VAR_DGRAD_GROUPED 13   /* grouped dgrad, stride 1, small groups merged block-diagonally:
                                         the whole-row grouped kernel on dY with the filter rotated and
                                         transposed per group, padding R-1-pad */
+#define CNHWC_VAR_WGRAD_GENERIC 14   /* plain one-weight-per-lane wgrad (any valid problem) */
+#define CNHWC_VAR_WGRAD_POINTWISE 15 /* 1x1, stride 1, unpadded: split-K dW = dY^T X on MFMA, fp32
+                                      * partials + reduce pass; the general kernel without the
+                                      * per-row pixel gather, bit-identical to it */
+#define CNHWC_VAR_WGRAD_SPLITK 16    /* general R x S strided wgrad: per tap, split-K implicit GEMM
+                                      * on MFMA over the output pixels, fp32 partials + reduce pass */
 
 /* Output dims by the floor formula above.  INVALID_ARG for a bad descriptor. */
 int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo);
 
-/* Workspace bytes the chosen kernel of pass `op` needs (0 for all but the
- * split-C forward, which needs split_c * N * Ho * Wo * K * 4 bytes of fp32
- * partial sums).  Pass at least this many bytes to cnhwc_fwd/cnhwc_dgrad. */
+/* Workspace bytes the chosen kernel of pass `op` needs: split_c * N * Ho * Wo
+ * * K * 4 bytes of fp32 partial sums for the split-C forward, splits * K * R
+ * * S * C/groups * 4 bytes for the split-K wgrad kernels (splits: the pixel
+ * splits of all batch chunks together), 0 for every other kernel.  Pass at
+ * least this many bytes to cnhwc_fwd / cnhwc_dgrad / cnhwc_wgrad. */
 int cnhwc_workspace_size(const cnhwc_problem* prob, int op, size_t* bytes);
 
 /* The dispatcher's choice for pass `op`: writes the kernel name (variant,
@@ -135,6 +147,14 @@ int cnhwc_fwd(const cnhwc_problem* prob, const void* x, const void* w, void* y,
 int cnhwc_dgrad(const cnhwc_problem* prob, const void* dy, const void* w, void* dx,
                 void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Weight-gradient pass.  x: device [N,H,W,C]; dy: device [N,Ho,Wo,K];
+ * dw: device [K,R,S,C/groups] (written, every element).  ws as for cnhwc_fwd
+ * (the split-K kernels keep one fp32 partial dw per pixel split there; a
+ * second launch sums the splits in ascending order and rounds once; each
+ * batch chunk contributes splits of its own). */
+int cnhwc_wgrad(const cnhwc_problem* prob, const void* x, const void* dy, void* dw,
+                void* ws, size_t ws_bytes, void* hip_stream);
+
 /* Reason for the last non-zero status on this thread ("" after success). */
 const char* cnhwc_last_error(void);
 
@@ -146,7 +166,8 @@ const char* cnhwc_last_error(void);
  * kernel (implicit-GEMM dgrad: 1 runs every phase class on the ring kernel,
  * 2 runs classes with two or more taps on the dY-window kernel, a value of 16
  * or more sets the ring kernel's pixels per tile; direct forward: 1 forces the
- * register-staged kernel, 2 the input-window kernel; other kernels ignore it);
+ * register-staged kernel, 2 the input-window kernel; split-K wgrad: the number
+ * of pixel splits per batch chunk; other kernels ignore it);
  * chunk_limit_bytes: the per-view byte limit of the chunk planner.  Pass NULL
  * to clear. */
 typedef struct cnhwc_override {

@@ -97,14 +97,17 @@ EXPECT = {
     "f1_dwfwd3x3": api.VAR_FWD_DW_TILED,
     "f1_dwfwd31x31": api.VAR_FWD_DW_ROTATED,
     "f2_grouped_dgrad": api.VAR_DGRAD_GROUPED,
+    "f3_wgrad_pointwise": api.VAR_WGRAD_POINTWISE,
+    "f3_wgrad_3x3": api.VAR_WGRAD_SPLITK,
 }
+
+OPC = {"fwd": api.OP_FWD, "dgrad": api.OP_DGRAD, "wgrad": api.OP_WGRAD}
 
 
 @pytest.mark.parametrize("name", sorted(EXPECT))
 def test_dispatcher_choice_per_workload(name):
     w = wl(name)
-    op = api.OP_FWD if w["op"] == "fwd" else api.OP_DGRAD
-    kname, var = api.cnhwc_plan(w["prob"], op)
+    kname, var = api.cnhwc_plan(w["prob"], OPC[w["op"]])
     assert var == EXPECT[name], (name, kname)
 
 
@@ -186,8 +189,7 @@ def test_chunk_planner_is_balanced(n, limit_images):
 
 def test_chunk_planner_default_is_one_chunk_for_every_workload():
     for name, w in synth.WORKLOADS.items():
-        op = api.OP_FWD if w["op"] == "fwd" else api.OP_DGRAD
-        assert api.cnhwc_chunk_plan(w["prob"], op) == [w["prob"]["n"]], name
+        assert api.cnhwc_chunk_plan(w["prob"], OPC[w["op"]]) == [w["prob"]["n"]], name
 
 
 def test_chunk_planner_refuses_an_oversized_image():
@@ -249,3 +251,75 @@ def test_last_error_clears_after_success():
     assert api.last_error() != ""
     api.cnhwc_out_dims(P(1, 8, 8, 8, 8, 1, 1))
     assert api.last_error() == ""
+
+
+def test_wgrad_dispatch():
+    """1x1 stride-1 unpadded wgrad takes the pointwise kernel (grouped too),
+    other shapes with 8-aligned channel groups of at least 16 the split-K
+    kernel, everything else the plain kernel."""
+    W = api.OP_WGRAD
+    assert api.cnhwc_plan(P(2, 8, 8, 64, 32, 1, 1), W)[1] == api.VAR_WGRAD_POINTWISE
+    assert api.cnhwc_plan(P(2, 8, 8, 64, 32, 1, 1, groups=2), W)[1] == api.VAR_WGRAD_POINTWISE
+    for p in [P(1, 8, 8, 16, 16, 1, 1, 2), P(1, 8, 8, 16, 16, 1, 1, 1, 1, 1),
+              P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1), P(2, 9, 7, 32, 64, 5, 3, 2, 2, 1, groups=2)]:
+        assert api.cnhwc_plan(p, W)[1] == api.VAR_WGRAD_SPLITK, p
+    for p in [P(1, 8, 8, 3, 5, 3, 3, 1, 1, 1), P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1, groups=16),
+              P(1, 8, 8, 12, 16, 1, 1), P(1, 8, 8, 16, 8, 3, 3, 1, 1, 1)]:
+        assert api.cnhwc_plan(p, W)[1] == api.VAR_WGRAD_GENERIC, p
+    with api.override(variant=api.VAR_DGRAD_IGEMM):
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_plan(P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1), W)
+    assert "not a wgrad kernel" in e.value.reason
+    with api.override(variant=api.VAR_WGRAD_POINTWISE):
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_plan(P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1), W)
+    assert "1x1" in e.value.reason
+    with api.override(variant=api.VAR_WGRAD_GENERIC):
+        with pytest.raises(api.CnhwcError):
+            api.cnhwc_plan(P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1), api.OP_DGRAD)
+
+
+def test_wgrad_workspace_counts_every_chunks_splits():
+    """Workspace = (pixel splits of all chunks) * K*R*S*Cg fp32 partials; the
+    plain kernel needs none and runs as one launch."""
+    p = P(6, 16, 16, 32, 64, 3, 3, 1, 1, 1)
+    elems = 64 * 9 * 32
+    with api.override(tune=5):
+        assert api.cnhwc_workspace_size(p, api.OP_WGRAD) == 5 * elems * 4
+    img = 16 * 16 * 64 * 2  # dy per image is the largest view
+    with api.override(tune=5, chunk_limit_bytes=img * 2):
+        assert api.cnhwc_chunk_plan(p, api.OP_WGRAD) == [2, 2, 2]
+        assert api.cnhwc_workspace_size(p, api.OP_WGRAD) == 3 * 5 * elems * 4
+    auto = api.cnhwc_workspace_size(p, api.OP_WGRAD)
+    assert auto > 0 and auto % (elems * 4) == 0
+    g = P(6, 16, 16, 3, 5, 3, 3, 1, 1, 1)
+    assert api.cnhwc_workspace_size(g, api.OP_WGRAD) == 0
+    with api.override(chunk_limit_bytes=16 * 16 * 5 * 2):
+        assert api.cnhwc_chunk_plan(g, api.OP_WGRAD) == [6]
+
+
+def test_wgrad_checks_precede_any_launch():
+    p = P(2, 8, 8, 16, 16, 3, 3, 1, 1, 1)
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_wgrad(p, None, 0x200000, 0x300000, None, 0, None)
+    assert e.value.status == api.INVALID_ARG and "x is NULL" in e.value.reason
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_wgrad(p, 0x100000, 0x200008, 0x300000, None, 0, None)
+    assert e.value.status == api.MISALIGNED and "dy" in e.value.reason
+    with pytest.raises(api.CnhwcError) as e:  # dw overlaps x
+        api.cnhwc_wgrad(p, 0x100000, 0x200000, 0x100000 + 64, None, 0, None)
+    assert e.value.status == api.INVALID_ARG and "overlaps" in e.value.reason
+    need = api.cnhwc_workspace_size(p, api.OP_WGRAD)
+    assert need > 0
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_wgrad(p, 0x100000, 0x200000, 0x300000, 0x1000000, need - 16, None)
+    assert e.value.status == api.WORKSPACE_TOO_SMALL
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_wgrad(p, 0x100000, 0x200000, 0x300000, None, need, None)
+    assert e.value.status == api.INVALID_ARG and "ws" in e.value.reason
+    with pytest.raises(api.CnhwcError) as e:  # workspace overlaps dy
+        api.cnhwc_wgrad(p, 0x100000, 0x200000, 0x300000, 0x200000 + 256, need, None)
+    assert e.value.status == api.INVALID_ARG and "workspace overlaps" in e.value.reason
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_plan(p, 3)
+    assert e.value.status == api.INVALID_ARG
