@@ -78,6 +78,8 @@ struct IgemmArgs {
     int ctiles;        // ceil(Cg / BN)
     int nclasses;
     int remap;         // 1: remap block ids so each XCD works on contiguous tiles
+    int splits;        // split-K: reduction splits (grid y); 1 otherwise
+    float* ws;         // split-K: fp32 partials [split][N*H*W][C]
     ClassInfo cls[kMaxClasses];
 };
 
@@ -96,7 +98,7 @@ __device__ inline int swz_b(int k) {
 }
 
 
-template <typename T, int WMB, int WNB, bool PW, bool KR>
+template <typename T, int WMB, int WNB, bool PW, bool KR, bool SK>
 __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArgs a) {
     constexpr int WAVES_M = 2, WAVES_N = 2;
     constexpr int BMC = WAVES_M * WMB * 16;             // tile capacity in pixels
@@ -208,13 +210,24 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
     }
 
     const int kchunks = (a.Kg + kBK - 1) / kBK;
-    const int steps = cl.nr * cl.nt * kchunks;
+    int steps = cl.nr * cl.nt * kchunks;
+    int step0 = 0;
+    if constexpr (SK) {
+        // split-K: this block takes reduction steps [step0, step0 + steps) of
+        // the tile (contiguous, balanced; empty when splits exceed the steps)
+        const int split = blockIdx.y;
+        step0 = int(int64_t(steps) * split / a.splits);
+        steps = int(int64_t(steps) * (split + 1) / a.splits) - step0;
+    }
 
     // Issue cursor (uniform): reduction step = (tap (ti, tj), 64-deep chunk kk).
     // It runs two steps ahead of the multiply and is advanced without
     // branches; past the last step it keeps producing offsets whose loads are
     // either range-checked zeros or in-range data of stages never multiplied.
-    int cur_kk = 0, cur_ti = 0, cur_tj = 0, cur_tap = 0;
+    int cur_tap = step0 / kchunks;
+    int cur_kk = (step0 - cur_tap * kchunks) * kBK;
+    int cur_ti = cl.nt > 0 ? cur_tap / cl.nt : 0;
+    int cur_tj = cur_tap - cur_ti * cl.nt;
     auto advance = [&]() {
         cur_kk += kBK;
         const bool wrap = cur_kk >= a.Kg;
@@ -374,6 +387,31 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
         __builtin_amdgcn_s_barrier();
     }
 
+    if constexpr (SK) {
+        // ---- split-K epilogue: the fp32 partial tile straight to the
+        // workspace, each lane's 4 consecutive channels as one 16-byte store;
+        // every position of the tile is written (zeros for an empty split) ----
+        float* wsp = a.ws + int64_t(blockIdx.y) * (int64_t(a.N) * a.H * a.W * a.C);
+#pragma unroll
+        for (int i = 0; i < WMB; ++i) {
+            const int row = wm * (WMB * 16) + i * 16 + frow;
+            const int m = m_lo + row;
+            if (row >= a.bm || m >= m_hi) continue;
+            const int hw = cl.hc * cl.wc;
+            const int n = m / hw;
+            const int rem = m - n * hw;
+            const int hc = rem / cl.wc;
+            const int wc = rem - hc * cl.wc;
+            const int64_t pix = (int64_t(n) * a.H + cl.a + s * hc) * a.W + cl.b + s * wc;
+#pragma unroll
+            for (int j = 0; j < WNB; ++j) {
+                const int c = c0 + wn * (WNB * 16) + j * 16 + fgrp * 4;
+                if (c < a.Cg)
+                    *reinterpret_cast<f32x4*>(wsp + pix * a.C + g * a.Cg + c) = acc[i][j];
+            }
+        }
+        return;
+    }
     // ---- epilogue: round, stage the tile in LDS, 16-byte row stores ----
 #pragma unroll
     for (int i = 0; i < WMB; ++i)
@@ -1289,17 +1327,23 @@ __global__ __launch_bounds__(kHaloThreads, 1) void dgrad_halo_kernel(const HaloA
 // Tile shapes (M blocks per wave, N blocks per wave) on 2 x 2 waves:
 //   0: 224-pixel capacity x 128 channels (deep channel counts)
 //   1: 128 x 64 (narrow channel counts)
-template <typename T, bool PW, bool KR>
+template <typename T, bool PW, bool KR, bool SK>
 void launch_cfg(int cfg, const IgemmArgs& args, int blocks, hipStream_t st) {
+    const dim3 grid(blocks, SK ? args.splits : 1);
     if (cfg == 0)
-        hipLaunchKernelGGL((dgrad_igemm_kernel<T, 7, 4, PW, KR>), dim3(blocks), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((dgrad_igemm_kernel<T, 7, 4, PW, KR, SK>), grid, dim3(kThreads), 0, st, args);
     else
-        hipLaunchKernelGGL((dgrad_igemm_kernel<T, 4, 2, PW, KR>), dim3(blocks), dim3(kThreads), 0, st, args);
+        hipLaunchKernelGGL((dgrad_igemm_kernel<T, 4, 2, PW, KR, SK>), grid, dim3(kThreads), 0, st, args);
 }
 template <typename T, bool PW>
 void launch_kr(int cfg, bool kr, const IgemmArgs& args, int blocks, hipStream_t st) {
-    if (kr) launch_cfg<T, PW, true>(cfg, args, blocks, st);
-    else launch_cfg<T, PW, false>(cfg, args, blocks, st);
+    if (args.splits > 1) {
+        if (kr) launch_cfg<T, PW, true, true>(cfg, args, blocks, st);
+        else launch_cfg<T, PW, false, true>(cfg, args, blocks, st);
+        return;
+    }
+    if (kr) launch_cfg<T, PW, true, false>(cfg, args, blocks, st);
+    else launch_cfg<T, PW, false, false>(cfg, args, blocks, st);
 }
 
 struct Cfg {
@@ -1561,14 +1605,43 @@ int launch_dgrad_halo(const Prob& p, const void* dy, const void* w, void* dx, hi
 
 }  // namespace
 
+// Split-K dgrad: reduction splits for a problem whose ring-kernel tiles
+// cannot fill the GPU (1: do not split).  Deep reductions over few output
+// tiles (small maps, many dY channels) split their steps so that tiles x
+// splits blocks cover every compute unit once, each split at least 4 steps.
+int dgrad_splitk_auto(const Prob& p) {
+    const int cfg = p.cg > 64 ? 0 : 1;
+    const int s = p.stride;
+    int64_t tiles = 0, max_taps = 0;
+    for (int ca = 0; ca < s; ++ca)
+        for (int cb = 0; cb < s; ++cb) {
+            const int64_t hc = (p.h - ca + s - 1) / s, wc = (p.w - cb + s - 1) / s;
+            if (hc <= 0 || wc <= 0) continue;
+            const int64_t r0 = (ca + p.pad_h) % s, t0 = (cb + p.pad_w) % s;
+            const int64_t nr = r0 < p.r ? (p.r - r0 + s - 1) / s : 0;
+            const int64_t nt = t0 < p.s ? (p.s - t0 + s - 1) / s : 0;
+            tiles += (p.n * hc * wc + kCfgs[cfg].bmc - 1) / kCfgs[cfg].bmc *
+                     ((p.cg + kCfgs[cfg].bn - 1) / kCfgs[cfg].bn) * p.groups;
+            max_taps = std::max(max_taps, nr * nt);
+        }
+    const int64_t steps = max_taps * ((p.kg + kBK - 1) / kBK);
+    if (tiles <= 0 || tiles >= kNumCUs / 2 || steps < 16) return 1;
+    const int64_t sp = std::min<int64_t>({(kNumCUs + tiles - 1) / tiles, steps / 4, 64});
+    return int(std::max<int64_t>(sp, 1));
+}
+
 int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
-                       hipStream_t st) {
-    const bool pw = pl.variant == CNHWC_VAR_DGRAD_POINTWISE;
+                       void* ws, hipStream_t st) {
+    const bool sk = pl.variant == CNHWC_VAR_DGRAD_SPLITK;
+    if (sk && (pl.split_c < 2 || ws == nullptr)) return CNHWC_UNSUPPORTED;
+    const bool pw = pl.variant == CNHWC_VAR_DGRAD_POINTWISE ||
+                    (sk && p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0 &&
+                     p.groups == 1);
     // pointwise with C <= 64: the row-streamed kernel for K = 64..256 in
     // steps of 64, else the LDS-persistent kernel while the filter fits LDS
     // (tune 1 asks for the ring kernel, tune 3 or >= 16 for the LDS-persistent
     // one)
-    if (pw && pl.tune != 1 && p.c <= kPwBN) {
+    if (pw && !sk && pl.tune != 1 && p.c <= kPwBN) {
         if (pw_rows_ok(p) && pl.tune != 3 && pl.tune < 16) return launch_pw_rows(p, dy, w, dx, st);
         if (pw_stages(p.k) > 0) return launch_pw_persist(p, pl, dy, w, dx, st);
     }
@@ -1577,7 +1650,7 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
     // problems split into several classes of few taps each, where the window
     // kernel's fixed cost per block outweighs its dY reuse: ring kernel only.
     // (tune: 1 forces the ring kernel, 2 the window kernel.)
-    const bool window = !pw && (pl.tune == 2 || (pl.tune != 1 && p.stride == 1));
+    const bool window = !pw && !sk && (pl.tune == 2 || (pl.tune != 1 && p.stride == 1));
     if (window) {
         const int rc = launch_dgrad_halo(p, dy, w, dx, st);
         if (rc != CNHWC_OK) return rc;
@@ -1593,6 +1666,8 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
     a.R = int(p.r); a.S = int(p.s); a.stride = p.stride; a.pad_h = p.pad_h; a.pad_w = p.pad_w;
     a.Ho = int(p.ho); a.Wo = int(p.wo); a.Cg = int(p.cg); a.Kg = int(p.kg); a.G = p.groups;
     a.ctiles = int((p.cg + BN - 1) / BN);
+    a.splits = sk ? pl.split_c : 1;
+    a.ws = sk ? static_cast<float*>(ws) : nullptr;
     const int s = p.stride;
     // phase classes, heaviest reduction first so long tiles start early
     struct C { ClassInfo ci; int64_t work; int64_t mc; };
@@ -1650,6 +1725,13 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
     const bool kr = p.kg % kBK != 0;
     if (pw) bf ? launch_kr<BF16, true>(cfg, kr, a, total, st) : launch_kr<F16, true>(cfg, kr, a, total, st);
     else bf ? launch_kr<BF16, false>(cfg, kr, a, total, st) : launch_kr<F16, false>(cfg, kr, a, total, st);
+    if (sk) {
+        // second pass: dX = round(sum of the splits in ascending order), the
+        // split-C forward's reduce over [split][N*H*W][C]
+        Prob q = p;
+        q.ho = p.h; q.wo = p.w; q.k = p.c;
+        return launch_split_reduce(q, a.splits, ws, dx, st);
+    }
     return CNHWC_OK;
 }
 

@@ -77,7 +77,8 @@ bool is_depthwise(const Prob& p) { return p.groups == p.c && p.groups == p.k; }
 bool variant_is_dgrad(int v) {
     return v == CNHWC_VAR_DGRAD_POINTWISE || v == CNHWC_VAR_DGRAD_IGEMM ||
            v == CNHWC_VAR_DGRAD_DW_STREAM || v == CNHWC_VAR_DGRAD_DW_ROTATED ||
-           v == CNHWC_VAR_DGRAD_DW_TILED || v == CNHWC_VAR_DGRAD_GENERIC || v == CNHWC_VAR_DGRAD_GROUPED;
+           v == CNHWC_VAR_DGRAD_DW_TILED || v == CNHWC_VAR_DGRAD_GENERIC || v == CNHWC_VAR_DGRAD_GROUPED ||
+           v == CNHWC_VAR_DGRAD_SPLITK;
 }
 bool variant_is_wgrad(int v) {
     return v == CNHWC_VAR_WGRAD_GENERIC || v == CNHWC_VAR_WGRAD_POINTWISE || v == CNHWC_VAR_WGRAD_SPLITK;
@@ -102,6 +103,9 @@ std::string variant_reason(const Prob& p, int op, int v, int cpl, int split_c) {
     switch (v) {
     case CNHWC_VAR_DGRAD_POINTWISE: return dgrad_igemm_reason(p, true);
     case CNHWC_VAR_DGRAD_IGEMM: return dgrad_igemm_reason(p, false);
+    case CNHWC_VAR_DGRAD_SPLITK:
+        if (split_c < 2) return "split-K dgrad needs at least 2 reduction splits";
+        return dgrad_igemm_reason(p, false);
     case CNHWC_VAR_DGRAD_DW_STREAM: return dw_stream_reason(p, cpl);
     case CNHWC_VAR_DGRAD_DW_ROTATED: return dw_rotated_reason(p);
     case CNHWC_VAR_DGRAD_DW_TILED: return dw_tiled_reason(p);
@@ -127,6 +131,8 @@ std::string plan_name(const Prob& p, const Plan& pl) {
         std::snprintf(buf, sizeof buf, "dgrad_pointwise_%s", dt(p)); break;
     case CNHWC_VAR_DGRAD_IGEMM:
         std::snprintf(buf, sizeof buf, "dgrad_igemm_%s_s%d", dt(p), p.stride); break;
+    case CNHWC_VAR_DGRAD_SPLITK:
+        std::snprintf(buf, sizeof buf, "dgrad_splitk%d_%s_s%d+split_reduce", pl.split_c, dt(p), p.stride); break;
     case CNHWC_VAR_DGRAD_DW_STREAM:
         std::snprintf(buf, sizeof buf, "dgrad_dw_stream_%s_f%lldx%lld_s%d_cpl%d", dt(p),
                       (long long)p.r, (long long)p.s, p.stride, pl.cpl); break;
@@ -177,12 +183,13 @@ int choose(const Prob& p, int op, Plan* out) {
         pl.variant = ov.variant;
         pl.cpl = ov.cpl > 0 ? ov.cpl : (ov.variant == CNHWC_VAR_DGRAD_DW_STREAM ? dw_stream_best_cpl(p) : 0);
         pl.split_c = ov.split_c > 0 ? ov.split_c
-                                    : (ov.variant == CNHWC_VAR_FWD_SPLITC ? fwd_direct_auto_split(p) : 1);
+                                    : (ov.variant == CNHWC_VAR_FWD_SPLITC ? fwd_direct_auto_split(p)
+                                       : ov.variant == CNHWC_VAR_DGRAD_SPLITK ? dgrad_splitk_auto(p) : 1);
         if (ov.variant == CNHWC_VAR_FWD_SPLITC && pl.split_c < 2)
             return fail(CNHWC_UNSUPPORTED, "split-C needs at least 2 channel splits");
         std::string why = variant_reason(p, op, pl.variant, pl.cpl, pl.split_c);
         if (!why.empty()) return fail(CNHWC_UNSUPPORTED, why);
-        if (pl.variant != CNHWC_VAR_FWD_SPLITC) pl.split_c = 1;
+        if (pl.variant != CNHWC_VAR_FWD_SPLITC && pl.variant != CNHWC_VAR_DGRAD_SPLITK) pl.split_c = 1;
         pl.name = plan_name(p, pl);
         pl.tune = ov.tune;
         *out = pl;
@@ -216,6 +223,11 @@ int choose(const Prob& p, int op, Plan* out) {
             if (!ok && p.stride == 1) ok = take(CNHWC_VAR_DGRAD_DW_ROTATED, 0, 1);
         }
         if (!ok && p.groups > 1 && !is_depthwise(p) && p.stride == 1) ok = take(CNHWC_VAR_DGRAD_GROUPED, 0, 1);
+        if (!ok && !is_depthwise(p)) {
+            // few output tiles over a deep reduction: split the reduction
+            const int split = ov.split_c > 0 ? ov.split_c : dgrad_splitk_auto(p);
+            if (split > 1) ok = take(CNHWC_VAR_DGRAD_SPLITK, 0, split);
+        }
         if (!ok && p.groups == 1 && p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0)
             ok = take(CNHWC_VAR_DGRAD_POINTWISE, 0, 1);
         if (!ok) ok = take(CNHWC_VAR_DGRAD_IGEMM, 0, 1);
@@ -258,6 +270,8 @@ ChunkBytes chunk_bytes(const Prob& p, int op, const Plan& pl) {
     b.ws_per_image = 0;
     if (op == CNHWC_OP_FWD && pl.variant == CNHWC_VAR_FWD_SPLITC)
         b.ws_per_image = int64_t(pl.split_c) * p.ho * p.wo * p.k * 4;
+    if (op == CNHWC_OP_DGRAD && pl.variant == CNHWC_VAR_DGRAD_SPLITK)
+        b.ws_per_image = int64_t(pl.split_c) * p.h * p.w * p.c * 4;
     b.per_image_max = std::max(std::max(act, out), b.ws_per_image);
     b.fixed = p.k * p.r * p.s * p.cg * esz;
     return b;
@@ -346,7 +360,8 @@ int run(const cnhwc_problem* prob, int op, const void* in, const void* w, void* 
         int rc = CNHWC_OK;
         switch (pl.variant) {
         case CNHWC_VAR_DGRAD_POINTWISE:
-        case CNHWC_VAR_DGRAD_IGEMM: rc = launch_dgrad_igemm(pc, pl, ip, w, op_, s); break;
+        case CNHWC_VAR_DGRAD_IGEMM: rc = launch_dgrad_igemm(pc, pl, ip, w, op_, nullptr, s); break;
+        case CNHWC_VAR_DGRAD_SPLITK: rc = launch_dgrad_igemm(pc, pl, ip, w, op_, ws, s); break;
         case CNHWC_VAR_DGRAD_DW_STREAM: rc = launch_dgrad_dw_stream(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_DGRAD_DW_ROTATED: rc = launch_dgrad_dw_rotated(pc, pl, ip, w, op_, s); break;
         case CNHWC_VAR_DGRAD_DW_TILED: rc = launch_dgrad_dw_tiled(pc, pl, ip, w, op_, s); break;

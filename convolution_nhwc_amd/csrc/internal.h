@@ -39,8 +39,13 @@ constexpr int64_t kBufferLimit = (int64_t(1) << 31) - 1;
 // ---- launchers (one batch chunk each; p.n is the chunk's batch) -------------
 // Each returns 0 on success or a CNHWC_* status; launch errors are reported by
 // the caller through hipGetLastError.
+// Implicit-GEMM dgrad (pointwise fast path, general strided, and split-K:
+// fp32 partials of pl.split_c reduction splits into ws[split][N*H*W][C], then
+// the split reduce pass into dx).
 int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
-                       hipStream_t st);
+                       void* ws, hipStream_t st);
+// Split-K dgrad: automatic number of reduction splits (1 = do not split).
+int dgrad_splitk_auto(const Prob& p);
 int launch_dgrad_dw_stream(const Prob& p, const Plan& pl, const void* dy, const void* w,
                            void* dx, hipStream_t st);
 int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const void* w,

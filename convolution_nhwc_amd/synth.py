@@ -141,4 +141,9 @@ WORKLOADS = {
                                prob=problem(32, 56, 56, 64, 256, 1, 1)),
     "f3_wgrad_3x3": dict(op="wgrad", seed=82, fan_in=None,
                          prob=problem(32, 28, 28, 256, 256, 3, 3, 1, 1, 1)),
+    # split-K dgrad (the fourth next row): the split-C forward's layer run
+    # backward -- few output pixels (8 x 7 x 7) over a 512 x 9 deep reduction;
+    # the weights keep that layer's distribution
+    "f4_splitk_dgrad": dict(op="dgrad", seed=91, fan_in=2048 * 9,
+                            prob=problem(8, 7, 7, 2048, 512, 3, 3, 1, 1, 1, dtype=BF16)),
 }

@@ -107,12 +107,17 @@ typedef struct cnhwc_problem {
                                       * per-row pixel gather, bit-identical to it */
 #define CNHWC_VAR_WGRAD_SPLITK 16    /* general R x S strided wgrad: per tap, split-K implicit GEMM
                                       * on MFMA over the output pixels, fp32 partials + reduce pass */
+#define CNHWC_VAR_DGRAD_SPLITK 17    /* split-K implicit-GEMM dgrad for few output tiles over a deep
+                                      * reduction (small maps, many dY channels): the reduction steps
+                                      * (filter taps x 64-deep dY channel chunks) of each tile split
+                                      * over blocks, fp32 partials + the split reduce pass */
 
 /* Output dims by the floor formula above.  INVALID_ARG for a bad descriptor. */
 int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo);
 
 /* Workspace bytes the chosen kernel of pass `op` needs: split_c * N * Ho * Wo
- * * K * 4 bytes of fp32 partial sums for the split-C forward, splits * K * R
+ * * K * 4 bytes of fp32 partial sums for the split-C forward, splits * N * H *
+ * W * C * 4 bytes for the split-K dgrad (N: the largest batch chunk), splits * K * R
  * * S * C/groups * 4 bytes for the split-K wgrad kernels (splits: the pixel
  * splits of all batch chunks together), 0 for every other kernel.  Pass at
  * least this many bytes to cnhwc_fwd / cnhwc_dgrad / cnhwc_wgrad. */
@@ -162,12 +167,14 @@ const char* cnhwc_last_error(void);
  * keeps the automatic choice.  variant: a CNHWC_VAR_* to force (the call fails
  * with UNSUPPORTED and the variant's reason if it cannot run the problem);
  * cpl: depthwise channels per lane (1, 2, 4 or 8); split_c: number of channel
- * splits for CNHWC_VAR_FWD_SPLITC; tune: a launch-shape knob of the chosen
- * kernel (implicit-GEMM dgrad: 1 runs every phase class on the ring kernel,
- * 2 runs classes with two or more taps on the dY-window kernel, a value of 16
- * or more sets the ring kernel's pixels per tile; direct forward: 1 forces the
- * register-staged kernel, 2 the input-window kernel; split-K wgrad: the number
- * of pixel splits per batch chunk; other kernels ignore it);
+ * splits for CNHWC_VAR_FWD_SPLITC or of reduction splits for
+ * CNHWC_VAR_DGRAD_SPLITK (with the automatic variant it forces that split);
+ * tune: a launch-shape knob of the chosen kernel (implicit-GEMM dgrad: 1 runs
+ * every phase class on the ring kernel, 2 runs classes with two or more taps on
+ * the dY-window kernel, a value of 16 or more sets the ring kernel's pixels per
+ * tile; direct forward: 1 forces the register-staged kernel, 2 the input-window
+ * kernel; split-K wgrad: the number of pixel splits per batch chunk; other
+ * kernels ignore it);
  * chunk_limit_bytes: the per-view byte limit of the chunk planner.  Pass NULL
  * to clear. */
 typedef struct cnhwc_override {

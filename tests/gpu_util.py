@@ -64,8 +64,10 @@ def run_gpu(p, op, act_bits, w_bits):
                       t.cuda.current_stream().cuda_stream)
     else:
         out = poisoned((p["n"], p["h"], p["w"], p["c"]), p["dtype"])
-        api.cnhwc_dgrad(p, a.data_ptr(), w.data_ptr(), out.data_ptr(), None, 0,
-                        t.cuda.current_stream().cuda_stream)
+        need = api.cnhwc_workspace_size(p, api.OP_DGRAD)
+        ws = t.full((max(need, 16) // 4,), float("nan"), dtype=t.float32, device="cuda")
+        api.cnhwc_dgrad(p, a.data_ptr(), w.data_ptr(), out.data_ptr(), ws.data_ptr() if need else None,
+                        need, t.cuda.current_stream().cuda_stream)
     t.cuda.synchronize()
     return out
 

@@ -58,9 +58,11 @@ IGEMM = [
 
 @pytest.mark.parametrize("p", IGEMM, ids=ident)
 def test_igemm_parity(p):
-    # stride-1 grouped shapes may be dispatched to the grouped merge instead;
-    # this test runs the implicit-GEMM kernel on every shape
-    assert api.cnhwc_plan(p, api.OP_DGRAD)[1] in (api.VAR_DGRAD_IGEMM, api.VAR_DGRAD_GROUPED)
+    # stride-1 grouped shapes may be dispatched to the grouped merge instead,
+    # few tiles over a deep reduction to split-K; this test runs the
+    # implicit-GEMM kernel on every shape
+    assert api.cnhwc_plan(p, api.OP_DGRAD)[1] in (api.VAR_DGRAD_IGEMM, api.VAR_DGRAD_GROUPED,
+                                                  api.VAR_DGRAD_SPLITK)
     with api.override(variant=api.VAR_DGRAD_IGEMM):
         parity(p, "dgrad", 102)
 
@@ -70,7 +72,7 @@ def test_igemm_parity(p):
 def test_igemm_parity_both_kernels(p, tune):
     """Both implicit-GEMM dgrad kernels (every class on the ring kernel; or
     classes with two or more taps on the dY-window kernel) on every shape."""
-    with api.override(tune=tune):
+    with api.override(variant=api.VAR_DGRAD_IGEMM, tune=tune):
         parity(p, "dgrad", 108)
 
 

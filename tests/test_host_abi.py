@@ -99,6 +99,7 @@ EXPECT = {
     "f2_grouped_dgrad": api.VAR_DGRAD_GROUPED,
     "f3_wgrad_pointwise": api.VAR_WGRAD_POINTWISE,
     "f3_wgrad_3x3": api.VAR_WGRAD_SPLITK,
+    "f4_splitk_dgrad": api.VAR_DGRAD_SPLITK,
 }
 
 OPC = {"fwd": api.OP_FWD, "dgrad": api.OP_DGRAD, "wgrad": api.OP_WGRAD}
@@ -323,3 +324,60 @@ def test_wgrad_checks_precede_any_launch():
     with pytest.raises(api.CnhwcError) as e:
         api.cnhwc_plan(p, 3)
     assert e.value.status == api.INVALID_ARG
+
+
+def test_splitk_dgrad_dispatch_and_workspace():
+    """Few output tiles over a deep reduction split the reduction; the
+    workspace holds one fp32 partial of dX per split; the large-map dgrad
+    workloads stay unsplit with no workspace."""
+    w = wl("f4_splitk_dgrad")
+    p = w["prob"]
+    name, var = api.cnhwc_plan(p, api.OP_DGRAD)
+    assert var == api.VAR_DGRAD_SPLITK
+    split = int(re.search(r"splitk(\d+)", name).group(1))
+    assert 2 <= split <= 64
+    assert api.cnhwc_workspace_size(p, api.OP_DGRAD) == split * 8 * 7 * 7 * 2048 * 4
+    for other in ("c2_pointwise", "c3a_3x3_s1", "c3b_3x3_s2"):
+        assert api.cnhwc_workspace_size(wl(other)["prob"], api.OP_DGRAD) == 0
+    # deep 1x1 with a small map splits too (the pointwise addressing inside)
+    small_1x1 = P(1, 7, 7, 512, 2048, 1, 1)
+    assert api.cnhwc_plan(small_1x1, api.OP_DGRAD)[1] == api.VAR_DGRAD_SPLITK
+    # a short reduction does not split
+    assert api.cnhwc_plan(P(1, 7, 7, 64, 64, 3, 3, 1, 1, 1), api.OP_DGRAD)[1] == api.VAR_DGRAD_IGEMM
+    # depthwise never takes it
+    dw = dict(n=1, h=7, w=7, c=512, k=512, r=3, s=3, stride=1, pad_h=1, pad_w=1, groups=512, dtype="f16")
+    assert api.cnhwc_plan(dw, api.OP_DGRAD)[1] != api.VAR_DGRAD_SPLITK
+
+
+def test_splitk_dgrad_forced_split_counts_and_refusals():
+    p = P(2, 9, 9, 64, 256, 3, 3, 2, 1, 1)
+    with api.override(variant=api.VAR_DGRAD_SPLITK, split_c=5):
+        name, var = api.cnhwc_plan(p, api.OP_DGRAD)
+        assert var == api.VAR_DGRAD_SPLITK and "splitk5_" in name
+        assert api.cnhwc_workspace_size(p, api.OP_DGRAD) == 5 * 2 * 9 * 9 * 64 * 4
+    with api.override(variant=api.VAR_DGRAD_SPLITK, split_c=1):
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_plan(p, api.OP_DGRAD)
+        assert e.value.status == api.UNSUPPORTED and "2 reduction splits" in e.value.reason
+    with api.override(variant=api.VAR_DGRAD_SPLITK, split_c=4):
+        with pytest.raises(api.CnhwcError) as e:   # channels not a multiple of 8
+            api.cnhwc_plan(P(1, 8, 8, 12, 16, 3, 3, 1, 1, 1), api.OP_DGRAD)
+        assert e.value.status == api.UNSUPPORTED and "multiple of 8" in e.value.reason
+
+
+def test_splitk_dgrad_workspace_follows_the_largest_chunk_and_is_checked():
+    p = P(5, 7, 7, 256, 1024, 3, 3, 1, 1, 1)
+    with api.override(variant=api.VAR_DGRAD_SPLITK, split_c=4):
+        ws_img = 4 * 7 * 7 * 256 * 4
+        full = api.cnhwc_workspace_size(p, api.OP_DGRAD)
+        assert full == 5 * ws_img
+    with api.override(variant=api.VAR_DGRAD_SPLITK, split_c=4, chunk_limit_bytes=2 * ws_img):
+        assert api.cnhwc_chunk_plan(p, api.OP_DGRAD) == [2, 2, 1]
+        need = api.cnhwc_workspace_size(p, api.OP_DGRAD)
+        assert need == 2 * ws_img
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_dgrad(p, 0x1000000, 0x4000000, 0x8000000, 0x10000000, need - 16, None)
+        assert e.value.status == api.WORKSPACE_TOO_SMALL
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_dgrad(p, 0x1000000, 0x4000000, 0x8000000, None, need, None)
+        assert e.value.status == api.INVALID_ARG
