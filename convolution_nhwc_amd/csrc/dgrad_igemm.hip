@@ -66,6 +66,8 @@ struct ClassInfo {
     int nr, nt;        // number of such rows / columns
     int tile_begin;    // first block of the class
     int mtiles;        // M tiles of the class
+    int u_off, v_off;  // dY row / column of class pixel (0, 0) at tap (r0, t0)
+    FastDiv fd_hw, fd_wc;  // division by hc * wc and by wc (pixel -> n, row, column)
 };
 
 struct IgemmArgs {
@@ -176,12 +178,12 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
                 a_inv[i] = 0;
             } else {
                 const int hw = cl.hc * cl.wc;
-                const int n = m / hw;
+                const int n = fdiv(m, cl.fd_hw);
                 const int rem = m - n * hw;
-                const int hc = rem / cl.wc;
+                const int hc = fdiv(rem, cl.fd_wc);
                 const int wc = rem - hc * cl.wc;
-                const int u0 = (cl.a + s * hc + a.pad_h - cl.r0) / s;
-                const int v0 = (cl.b + s * wc + a.pad_w - cl.t0) / s;
+                const int u0 = hc + cl.u_off;
+                const int v0 = wc + cl.v_off;
                 uint64_t vmask = 0, valid = 0;
 #pragma unroll 1
                 for (int t = 0; t < cl.nt; ++t)
@@ -398,9 +400,9 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
             const int m = m_lo + row;
             if (row >= a.bm || m >= m_hi) continue;
             const int hw = cl.hc * cl.wc;
-            const int n = m / hw;
+            const int n = fdiv(m, cl.fd_hw);
             const int rem = m - n * hw;
-            const int hc = rem / cl.wc;
+            const int hc = fdiv(rem, cl.fd_wc);
             const int wc = rem - hc * cl.wc;
             const int64_t pix = (int64_t(n) * a.H + cl.a + s * hc) * a.W + cl.b + s * wc;
 #pragma unroll
@@ -435,9 +437,9 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
             pix = m;
         } else {
             const int hw = cl.hc * cl.wc;
-            const int n = m / hw;
+            const int n = fdiv(m, cl.fd_hw);
             const int rem = m - n * hw;
-            const int hc = rem / cl.wc;
+            const int hc = fdiv(rem, cl.fd_wc);
             const int wc = rem - hc * cl.wc;
             pix = (n * a.H + cl.a + s * hc) * a.W + cl.b + s * wc;
         }
@@ -1684,6 +1686,10 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
             ci.t0 = (cb + p.pad_w) % s;
             ci.nr = ci.r0 < p.r ? int((p.r - ci.r0 + s - 1) / s) : 0;
             ci.nt = ci.t0 < p.s ? int((p.s - ci.t0 + s - 1) / s) : 0;
+            ci.u_off = (ca + p.pad_h - ci.r0) / s;
+            ci.v_off = (cb + p.pad_w - ci.t0) / s;
+            ci.fd_hw = make_fastdiv(uint32_t(ci.hc * ci.wc));
+            ci.fd_wc = make_fastdiv(uint32_t(ci.wc));
             if (!window || ci.nr * ci.nt <= 1)
                 tmp[nc++] = C{ci, int64_t(ci.nr) * ci.nt, p.n * ci.hc * ci.wc};
         }
