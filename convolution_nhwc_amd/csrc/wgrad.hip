@@ -10,7 +10,7 @@
 // dW_tap[k][j] = sum_m dY[m][k] * X_tap[m][j] whose reduction runs over all
 // N*Ho*Wo output pixels: deep and narrow, so the pixels are split across
 // blocks (split-K) and each block writes an fp32 partial tile to a workspace
-// [split][K][R][S][Cg]; a second pass sums the splits in ascending order and
+// [split][K][R][S][Cg]; a second pass sums the splits in a fixed order and
 // rounds once (round to nearest even) to fp16 / bf16.
 //
 // Split-K kernel data path (gfx950): one block per (group, 128-channel k
@@ -306,28 +306,50 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_splitk_kernel(const WgArgs 
     }
 }
 
-// dw[i] = round(sum over splits s = 0, 1, ... of ws[s][i]), four elements per lane.
+// dw[i] = round(sum over splits of ws[s][i]), four elements per lane group.
+// L lanes (a power of two <= 16, consecutive in one wave) share an element:
+// lane q adds the contiguous split range [q*S/L, (q+1)*S/L) in ascending
+// order, eight loads in flight, and the first lane of the group then adds the
+// L range sums in ascending q.  A fixed order, so the result is reproducible;
+// with L = 1 it is the plain ascending sum.
 template <typename T>
 __global__ __launch_bounds__(256) void wgrad_reduce_kernel(const float* __restrict__ ws,
                                                            unsigned short* __restrict__ dw,
                                                            int64_t total4, int64_t stride4,
-                                                           int splits) {
-    for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total4;
-         i += int64_t(gridDim.x) * blockDim.x) {
+                                                           int splits, int lshift) {
+    const int L = 1 << lshift;
+    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    const int64_t i = gid >> lshift;
+    const int q = int(gid & (L - 1));
+    const bool valid = i < total4;
+    const int s0 = int(int64_t(q) * splits >> lshift), s1 = int(int64_t(q + 1) * splits >> lshift);
+    f32x4 s = f32x4{0.f, 0.f, 0.f, 0.f};
+    if (valid && s0 < s1) {
         const f32x4* src = reinterpret_cast<const f32x4*>(ws) + i;
-        f32x4 s = src[0];
-        for (int sp0 = 1; sp0 < splits; sp0 += 8) {
+        s = src[int64_t(s0) * stride4];
+        for (int sp0 = s0 + 1; sp0 < s1; sp0 += 8) {
             f32x4 v[8];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (sp0 + j < splits) v[j] = src[(sp0 + j) * stride4];
+                if (sp0 + j < s1) v[j] = src[int64_t(sp0 + j) * stride4];
 #pragma unroll
             for (int j = 0; j < 8; ++j)
-                if (sp0 + j < splits) {
+                if (sp0 + j < s1) {
                     s[0] += v[j][0]; s[1] += v[j][1]; s[2] += v[j][2]; s[3] += v[j][3];
                 }
         }
-        i32x2 o = {int(pack2<T>(s[0], s[1])), int(pack2<T>(s[2], s[3]))};
+    }
+    // every lane of the wave takes part in the shuffles (no early exit above)
+    const int lane = int(threadIdx.x & 63), base = lane & ~(L - 1);
+    f32x4 t = s;
+    for (int k = 1; k < L; ++k) {
+        f32x4 v;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v[c] = __shfl(s[c], base + k, 64);
+        t[0] += v[0]; t[1] += v[1]; t[2] += v[2]; t[3] += v[3];
+    }
+    if (valid && q == 0) {
+        i32x2 o = {int(pack2<T>(t[0], t[1])), int(pack2<T>(t[2], t[3]))};
         *(reinterpret_cast<i32x2*>(dw) + i) = o;
     }
 }
@@ -440,14 +462,18 @@ int launch_wgrad_splitk(const Prob& p, const Plan& pl, const void* x, const void
 
 int launch_wgrad_reduce(const Prob& p, int splits, const float* ws, void* dw, hipStream_t st) {
     const int64_t total4 = wgrad_split_elems(p) / 4;
-    const int64_t blocks = std::min<int64_t>((total4 + 255) / 256, 8 * kNumCUs);
+    // lanes per element: enough that each adds at most 8 splits, at most 16
+    int lshift = 0;
+    while (lshift < 4 && (int64_t(splits) + (int64_t(1) << lshift) - 1) >> lshift > 8) ++lshift;
+    const int64_t blocks = ((total4 << lshift) + 255) / 256;
+    if (blocks > (int64_t(1) << 31) - 1) return CNHWC_UNSUPPORTED;
     auto* out = static_cast<unsigned short*>(dw);
     if (p.dtype == CNHWC_BF16)
         hipLaunchKernelGGL(wgrad_reduce_kernel<BF16>, dim3(unsigned(blocks)), dim3(256), 0, st, ws,
-                           out, total4, total4, splits);
+                           out, total4, total4, splits, lshift);
     else
         hipLaunchKernelGGL(wgrad_reduce_kernel<F16>, dim3(unsigned(blocks)), dim3(256), 0, st, ws,
-                           out, total4, total4, splits);
+                           out, total4, total4, splits, lshift);
     return CNHWC_OK;
 }
 
