@@ -130,9 +130,11 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
     // ---- block -> (class, m tile, group, c tile) ----
     const int bid = blockIdx.x;
     int ci = 0;
-#pragma unroll 1
-    for (int i = 1; i < a.nclasses; ++i)
-        if (bid >= a.cls[i].tile_begin) ci = i;
+    // every class's first block is read at once (constant indices: the
+    // scalar loads issue together and one wait covers them)
+#pragma unroll
+    for (int i = 1; i < kMaxClasses; ++i)
+        if (i < a.nclasses && bid >= a.cls[i].tile_begin) ci = i;
     const ClassInfo cl = a.cls[ci];
     int local = bid - cl.tile_begin;
     if (a.remap) {
@@ -157,12 +159,13 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
 
     // ---- per-lane A (dY) sources: region q = wave + 4*i holds rows 8q .. 8q+7 ----
     // a_base: byte offset of the row's dY pixel at tap (0, 0) plus its chunk
-    // (kOob past the tile); a_inv: bit ti*nt + tj set when tap (ti, tj) of the
-    // class misses dY for this row.  The load offset of a tap is then
-    // (a_base - tap_bytes) with bit 31 set for a missing tap, which the buffer
-    // range check (views < 2^31 bytes) turns into a zero read.
+    // (kOob past the tile); (a_u, a_v): that pixel's dY row and column.  Tap
+    // (ti, tj) of the class reads dY pixel (a_u - ti, a_v - tj): the load
+    // offset is (a_base - tap_bytes), replaced by an out-of-range offset
+    // (a zero read through the buffer range check) when that pixel is outside
+    // dY.  Rows past the tile get a_u = a_v = -2^30, outside for every tap.
     uint32_t a_base[A_REG];
-    uint64_t a_inv[A_REG];
+    int a_u[A_REG], a_v[A_REG];
     int a_kq[A_REG];
 #pragma unroll
     for (int i = 0; i < A_REG; ++i) {
@@ -171,11 +174,10 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
         a_kq[i] = chunk * 8;
         const int m = m_lo + row;
         a_base[i] = kOob;
-        a_inv[i] = ~uint64_t(0);
+        a_u[i] = a_v[i] = -(1 << 30);
         if (row < a.bm && m < m_hi) {
             if (PW) {
                 a_base[i] = uint32_t((m * a.K + chunk * 8) * 2);
-                a_inv[i] = 0;
             } else {
                 const int hw = cl.hc * cl.wc;
                 const int n = fdiv(m, cl.fd_hw);
@@ -184,14 +186,8 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
                 const int wc = rem - hc * cl.wc;
                 const int u0 = hc + cl.u_off;
                 const int v0 = wc + cl.v_off;
-                uint64_t vmask = 0, valid = 0;
-#pragma unroll 1
-                for (int t = 0; t < cl.nt; ++t)
-                    if (v0 - t >= 0 && v0 - t < a.Wo) vmask |= uint64_t(1) << t;
-#pragma unroll 1
-                for (int t = 0; t < cl.nr; ++t)
-                    if (u0 - t >= 0 && u0 - t < a.Ho) valid |= vmask << (t * cl.nt);
-                a_inv[i] = ~valid;
+                a_u[i] = u0;
+                a_v[i] = v0;
                 a_base[i] = uint32_t((((n * a.Ho + u0) * a.Wo + v0) * a.K + g * a.Kg + chunk * 8) * 2);
             }
         }
@@ -244,10 +240,15 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
     // dY rows, else W k-rows)
     auto dma_one = [&](auto stg, auto dsc) {
         constexpr int STG = decltype(stg)::value, D = decltype(dsc)::value;
-        (void)a_base; (void)a_inv; (void)a_kq; (void)b_voff; (void)b_krow;
+        (void)a_base; (void)a_u; (void)a_v; (void)a_kq; (void)b_voff; (void)b_krow;
         if constexpr (D < A_REG) {
-            const uint32_t tap_bytes = PW ? 0u : uint32_t((cur_ti * a.Wo + cur_tj) * a.K * 2);
-            uint32_t v = (a_base[D] - tap_bytes) | (uint32_t(a_inv[D] >> cur_tap) << 31);
+            uint32_t v = a_base[D];
+            if constexpr (!PW) {
+                const uint32_t tap_bytes = uint32_t((cur_ti * a.Wo + cur_tj) * a.K * 2);
+                const bool in = uint32_t(a_u[D] - cur_ti) < uint32_t(a.Ho) &&
+                                uint32_t(a_v[D] - cur_tj) < uint32_t(a.Wo);
+                v = in ? v - tap_bytes : kOob;
+            }
             if (KR) v = (cur_kk + a_kq[D] < a.Kg) ? v : kOob;
             dma16(rdy, lds + STG * A_BYTES + (wave + 4 * D) * 1024, v, uint32_t(cur_kk * 2));
         } else {

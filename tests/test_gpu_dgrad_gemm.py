@@ -53,6 +53,8 @@ IGEMM = [
     P(2, 14, 14, 64, 64, 3, 3, 1, 1, 1, dtype="bf16"),
     P(1, 16, 16, 64, 64, 3, 3, 2, 1, 1, dtype="bf16"),
     P(1, 8, 8, 16, 16, 1, 1, 1, 1, 1),             # 1x1 padded: general path
+    P(1, 12, 12, 16, 16, 9, 9, 1, 4, 4),           # 81 taps in one class (more than 64)
+    P(1, 20, 20, 16, 16, 17, 17, 2, 8, 8),         # stride 2: classes of 81, 72, 72 and 64 taps
 ]
 
 

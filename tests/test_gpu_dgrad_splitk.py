@@ -34,6 +34,7 @@ SHAPES = [
     P(1, 7, 7, 128, 512, 5, 3, 1, 2, 0),            # non-square filter, per-axis padding
     P(1, 13, 13, 16, 32, 3, 3, 4, 1, 1),            # stride 4: classes with no taps write zeros
     P(2, 7, 7, 128, 512, 3, 3, 1, 1, 1, dtype="bf16"),
+    P(1, 12, 12, 16, 32, 9, 9, 1, 4, 4),            # 81 taps: step ranges cross many taps
 ]
 
 
