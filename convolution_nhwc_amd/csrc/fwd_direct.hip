@@ -547,13 +547,16 @@ struct GrowArgs {
     int halo_bytes;               // LDS of the halo (whole 1 KiB loads)
     int hmask, omask;             // chunk swizzle masks: 15 when a row has 16k chunks, else 7
     FastDiv fd_cpr, fd_iw, fd_tw, fd_kc;   // division by C/8, IW, TW, K/8
+    int dg_lds;                   // DG: stage each wave's filter slice through LDS (one set a wave)
+    FastDiv fd_kg, fd_cg;         // division by Kg, Cg
 };
 
-// DG: the same correlation run for grouped dgrad at stride 1 (x = dY, y = dX,
+// DG (1: filter gathered per fragment, 2: staged through LDS; 0: forward):
+// the same correlation run for grouped dgrad at stride 1 (x = dY, y = dX,
 // padding R-1-pad): element (o, tap, i) of the correlation's filter is then
 // W[g*Cg + i][R-1-r][S-1-t][o - g*Kg] of the stored filter (Cg, Kg here are the
 // correlation's input and output channels per group).
-template <typename T, int BN, int R, int S, bool DG>
+template <typename T, int BN, int R, int S, int DG>
 __global__ __launch_bounds__(kGrThreads, 1) void fwd_grouped_rows_kernel(const GrowArgs a) {
     constexpr int TAPS = R * S, FM = kBM / 16, FN = BN / 16;
     extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
@@ -602,15 +605,55 @@ __global__ __launch_bounds__(kGrThreads, 1) void fwd_grouped_rows_kernel(const G
     // output channel j*16 + frow of the set against merged channels
     // fgrp*8 .. +7, zero unless those belong to that output's group
     auto load_w = [&](int gs, i32x4 (&wf)[TAPS][FN]) {
+        if constexpr (DG == 2) {
+            {
+                // The set's filter slice is contiguous in W (stored rows g*Cg + i of
+                // its groups, each TAPS x Kg): coalesced 2-byte loads, written into
+                // this wave's part of the (not yet used) output tile in fragment
+                // order [o][tap][i] (i contiguous, tap rotated).
+                const int nel = a.bn * TAPS * a.Cg;
+                unsigned short* wl = reinterpret_cast<unsigned short*>(os) + wave * nel;
+                const uint32_t gbase = uint32_t(gs) * uint32_t(nel);
+#pragma unroll 1
+                for (int e0 = 0; e0 < nel; e0 += 4 * 64) {
+                    unsigned short v[4];
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int e = e0 + u * 64 + lane;
+                        v[u] = buf_load2(rw, e < nel ? (gbase + uint32_t(e)) * 2u : kOob);
+                    }
+#pragma unroll
+                    for (int u = 0; u < 4; ++u) {
+                        const int e = e0 + u * 64 + lane;
+                        if (e < nel) {
+                            // stored order: ((gl*Cg + i)*TAPS + tap_st)*Kg + ol
+                            const int q = fdiv(e, a.fd_kg), ol = e - q * a.Kg;
+                            const int q2 = q / TAPS, tap_st = q - q2 * TAPS;
+                            const int gl = fdiv(q2, a.fd_cg), i = q2 - gl * a.Cg;
+                            wl[((gl * a.Kg + ol) * TAPS + (TAPS - 1 - tap_st)) * a.Cg + i] = v[u];
+                        }
+                    }
+                }
+            }
+        }
 #pragma unroll
         for (int j = 0; j < FN; ++j) {
             const int kk = j * 16 + frow;
             const bool own = kk < a.bn && (fgrp * 8) / a.Cg == kk / a.Kg;
-            if constexpr (!DG) {
+            if constexpr (DG == 0) {
                 const uint32_t base = uint32_t(((gs * a.bn + kk) * TAPS) * a.Cg + (fgrp * 8) % a.Cg) * 2u;
 #pragma unroll
                 for (int tap = 0; tap < TAPS; ++tap)
                     wf[tap][j] = buf_load16(rw, own ? base + uint32_t(tap * a.Cg * 2) : kOob);
+            } else if constexpr (DG == 2) {
+                // fragment [tap][j] of lane (frow, fgrp): 16 bytes of the staged slice
+                const int nel = a.bn * TAPS * a.Cg;
+                const unsigned short* wl = reinterpret_cast<const unsigned short*>(os) + wave * nel;
+                const int i0 = (fgrp * 8) % a.Cg;
+#pragma unroll
+                for (int tap = 0; tap < TAPS; ++tap)
+                    wf[tap][j] = own ? *reinterpret_cast<const i32x4*>(wl + (kk * TAPS + tap) * a.Cg + i0)
+                                     : i32x4{0, 0, 0, 0};
             } else {
                 // the 8 merged channels are 8 filter rows k, TAPS * Kg elements apart
                 const int o = gs * a.bn + kk;
@@ -638,7 +681,8 @@ __global__ __launch_bounds__(kGrThreads, 1) void fwd_grouped_rows_kernel(const G
     const int out_cpr = a.K / 8;                   // 16-byte chunks per output pixel
 #pragma unroll 1
     for (int gs = wave; gs < a.gsets; gs += kGrThreads / 64) {
-        if (gs != wave) load_w(gs, wf);
+        // (DG 2 runs one set per wave: the host picks it only when gsets <= waves)
+        if constexpr (DG != 2) { if (gs != wave) load_w(gs, wf); }
         // opaque per set: keeps the per-(tap, row block) read addresses from
         // being hoisted out of the set loop (they would hold 72+ registers)
 #pragma unroll
@@ -936,6 +980,15 @@ static int launch_grouped_rows(const Prob& p, bool dg, const void* x, const void
     a.fd_kc = make_fastdiv(uint32_t(p.k / 8));
     a.hmask = (p.c / 8) % 16 == 0 ? 15 : 7;
     a.omask = (p.k / 8) % 16 == 0 ? 15 : 7;
+    a.fd_kg = make_fastdiv(uint32_t(p.kg));
+    a.fd_cg = make_fastdiv(uint32_t(p.cg));
+    {
+        // dgrad filter slices through LDS: one group set per wave, all slices
+        // within the output tile's LDS, 16-byte aligned fragment reads
+        const int64_t slice = int64_t(a.bn) * p.r * p.s * p.cg * 2;
+        a.dg_lds = dg && a.gsets <= kGrThreads / 64 && p.cg % 8 == 0 &&
+                   a.gsets * slice <= int64_t(a.TH) * a.TW * p.k * 2 ? 1 : 0;
+    }
     const int64_t blocks = p.n * a.ptiles_h * a.ptiles_w;
     const bool bf = p.dtype == CNHWC_BF16;
     const void* fn;
@@ -945,7 +998,8 @@ static int launch_grouped_rows(const Prob& p, bool dg, const void* x, const void
     launch = [](const GrowArgs& g, int64_t nb, size_t l, hipStream_t q) {                        \
         hipLaunchKernelGGL((fwd_grouped_rows_kernel<T, BN, R, S, DG>), dim3(nb), dim3(kGrThreads), l, q, g); \
     };
-#define CNHWC_GROW_DG(T, BN, R, S) if (dg) { CNHWC_GROW(T, BN, R, S, true) } else { CNHWC_GROW(T, BN, R, S, false) }
+#define CNHWC_GROW_DG(T, BN, R, S) if (dg && a.dg_lds) { CNHWC_GROW(T, BN, R, S, 2) } \
+    else if (dg) { CNHWC_GROW(T, BN, R, S, 1) } else { CNHWC_GROW(T, BN, R, S, 0) }
     if (p.r == 3) {
         if (bf) { CNHWC_GROW_DG(BF16, 32, 3, 3) } else { CNHWC_GROW_DG(F16, 32, 3, 3) }
     } else if (a.bn <= 32) {
