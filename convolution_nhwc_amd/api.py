@@ -23,7 +23,7 @@ OP_FWD, OP_DGRAD, OP_WGRAD = 1, 2, 4
 (VAR_AUTO, VAR_DGRAD_POINTWISE, VAR_DGRAD_IGEMM, VAR_DGRAD_DW_STREAM, VAR_DGRAD_DW_ROTATED,
  VAR_FWD_DIRECT, VAR_FWD_SPLITC, VAR_FWD_GROUPED, VAR_FWD_GENERIC, VAR_DGRAD_GENERIC,
  VAR_DGRAD_DW_TILED, VAR_FWD_DW_TILED, VAR_FWD_DW_ROTATED, VAR_DGRAD_GROUPED,
- VAR_WGRAD_GENERIC, VAR_WGRAD_POINTWISE, VAR_WGRAD_SPLITK, VAR_DGRAD_SPLITK) = range(18)
+ VAR_WGRAD_GENERIC, VAR_WGRAD_POINTWISE, VAR_WGRAD_SPLITK, VAR_DGRAD_SPLITK, VAR_FWD_IGEMM) = range(19)
 
 SYMBOLS = ("cnhwc_out_dims", "cnhwc_workspace_size", "cnhwc_plan", "cnhwc_chunk_plan",
            "cnhwc_fwd", "cnhwc_dgrad", "cnhwc_wgrad", "cnhwc_last_error", "cnhwc_set_override")

@@ -46,6 +46,13 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
                        void* ws, hipStream_t st);
 // Split-K dgrad: automatic number of reduction splits (1 = do not split).
 int dgrad_splitk_auto(const Prob& p);
+// Forward (stride 1, groups 1) as the dgrad of the rotated, transposed filter
+// on the implicit-GEMM dgrad kernels; ws receives the transformed filter
+// (fwd_igemm_workspace bytes, independent of the batch).
+int launch_fwd_igemm(const Prob& p, const Plan& pl, const void* x, const void* w, void* y, void* ws,
+                     hipStream_t st);
+int64_t fwd_igemm_workspace(const Prob& p);
+std::string fwd_igemm_reason(const Prob& p);
 int launch_dgrad_dw_stream(const Prob& p, const Plan& pl, const void* dy, const void* w,
                            void* dx, hipStream_t st);
 int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const void* w,

@@ -146,4 +146,8 @@ WORKLOADS = {
     # the weights keep that layer's distribution
     "f4_splitk_dgrad": dict(op="dgrad", seed=91, fan_in=2048 * 9,
                             prob=problem(8, 7, 7, 2048, 512, 3, 3, 1, 1, 1, dtype=BF16)),
+    # implicit-GEMM forward (the same row): the pointwise dgrad layer run
+    # forward, 64 -> 256 channels over 32 x 56 x 56 pixels
+    "f4_igemm_fwd_pointwise": dict(op="fwd", seed=92, fan_in=64,
+                                   prob=problem(32, 56, 56, 64, 256, 1, 1)),
 }

@@ -111,13 +111,18 @@ typedef struct cnhwc_problem {
                                       * reduction (small maps, many dY channels): the reduction steps
                                       * (filter taps x 64-deep dY channel chunks) of each tile split
                                       * over blocks, fp32 partials + the split reduce pass */
+#define CNHWC_VAR_FWD_IGEMM 18       /* forward, stride 1, groups 1, pad <= filter - 1: the dgrad of the
+                                      * 180-degree-rotated, transposed filter at padding R-1-pad on the
+                                      * implicit-GEMM dgrad kernels (large maps); the transformed filter
+                                      * goes to the workspace */
 
 /* Output dims by the floor formula above.  INVALID_ARG for a bad descriptor. */
 int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo);
 
 /* Workspace bytes the chosen kernel of pass `op` needs: split_c * N * Ho * Wo
  * * K * 4 bytes of fp32 partial sums for the split-C forward, splits * N * H *
- * W * C * 4 bytes for the split-K dgrad (N: the largest batch chunk), splits * K * R
+ * W * C * 4 bytes for the split-K dgrad (N: the largest batch chunk), K * R * S *
+ * C * 2 bytes (the transformed filter) for the implicit-GEMM forward, splits * K * R
  * * S * C/groups * 4 bytes for the split-K wgrad kernels (splits: the pixel
  * splits of all batch chunks together), 0 for every other kernel.  Pass at
  * least this many bytes to cnhwc_fwd / cnhwc_dgrad / cnhwc_wgrad. */

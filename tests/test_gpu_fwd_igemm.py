@@ -1,0 +1,74 @@
+"""Implicit-GEMM forward (stride 1): the dgrad kernels run on x with the filter
+rotated by 180 degrees and transposed, at padding R-1-pad, against the fp64
+oracle's forward, through the C ABI."""
+import numpy as np
+import pytest
+
+from convolution_nhwc_amd import api, synth
+from gpu_util import parity
+
+pytestmark = pytest.mark.gpu
+
+
+def P(n, h, w, c, k, r, s, stride=1, pad_h=0, pad_w=0, groups=1, dtype="f16"):
+    return synth.problem(n, h, w, c, k, r, s, stride, pad_h, pad_w, groups, dtype)
+
+
+def ident(p):
+    return "n%d_%dx%d_c%d_k%d_f%dx%d_p%dx%d_%s" % (p["n"], p["h"], p["w"], p["c"], p["k"], p["r"], p["s"],
+                                                 p["pad_h"], p["pad_w"], p["dtype"])
+
+
+SHAPES = [
+    P(2, 14, 14, 64, 64, 3, 3, 1, 1, 1),        # 'same' 3x3: window kernel, C_d = 64
+    P(1, 12, 13, 128, 256, 3, 3, 1, 1, 1),      # C_d = 256: two channel tiles
+    P(2, 11, 10, 64, 96, 5, 3, 1, 2, 1),        # non-square, per-axis padding
+    P(1, 9, 9, 64, 64, 3, 3, 1, 0, 0),          # no padding ('valid'): rotated padding R-1
+    P(1, 10, 10, 48, 80, 3, 3, 1, 1, 0),        # channels not tile multiples
+    P(2, 9, 9, 64, 64, 1, 1),                   # 1x1, C_d = K = 64: row-streamed pointwise kernel
+    P(1, 8, 9, 96, 128, 1, 1),                  # 1x1, C_d = 128: ring kernel, pointwise addressing
+    P(1, 10, 10, 16, 32, 9, 9, 1, 4, 4),        # 81 taps
+    P(2, 14, 14, 64, 64, 3, 3, 1, 1, 1, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("p", SHAPES, ids=ident)
+def test_fwd_igemm_parity(p):
+    with api.override(variant=api.VAR_FWD_IGEMM):
+        assert api.cnhwc_workspace_size(p, api.OP_FWD) == p["k"] * p["r"] * p["s"] * p["c"] * 2
+        parity(p, "fwd", 130)
+
+
+@pytest.mark.parametrize("p", [P(1, 8, 8, 64, 64, 3, 3, 1, 1, 1), P(1, 6, 7, 32, 64, 1, 1, dtype="bf16")],
+                         ids=ident)
+def test_fwd_igemm_exact_on_integer_inputs(p):
+    with api.override(variant=api.VAR_FWD_IGEMM):
+        parity(p, "fwd", 131, exact=True)
+
+
+def test_fwd_igemm_chunked_equals_unchunked():
+    p = P(5, 8, 8, 64, 64, 3, 3, 1, 1, 1)
+    img = 8 * 8 * 64 * 2
+    with api.override(variant=api.VAR_FWD_IGEMM):
+        _, a = parity(p, "fwd", 132)
+    with api.override(variant=api.VAR_FWD_IGEMM, chunk_limit_bytes=2 * img):
+        assert api.cnhwc_chunk_plan(p, api.OP_FWD) == [2, 2, 1]
+        _, b = parity(p, "fwd", 132)
+    assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+
+
+def test_fwd_igemm_workload_full_size_sampled():
+    """The benchmarked pointwise forward at full size, in the launch
+    configuration the benchmark times (automatic dispatch); the oracle checks 8
+    sampled output channels (each depends only on its own filter row)."""
+    import oracle
+    from gpu_util import check_close, from_device, run_gpu
+    wl = synth.WORKLOADS["f4_igemm_fwd_pointwise"]
+    p = wl["prob"]
+    assert api.cnhwc_plan(p, api.OP_FWD)[1] == api.VAR_FWD_IGEMM
+    (xb, xf), (wb, wf) = synth.operands(wl["seed"], (p["n"], p["h"], p["w"], p["c"]),
+                                        (p["k"], p["r"], p["s"], p["c"]), p["dtype"], w_fan_in=wl["fan_in"])
+    out = from_device(run_gpu(p, "fwd", xb, wb), p["dtype"])
+    ks = np.sort(np.random.default_rng(133).choice(p["k"], 8, replace=False))
+    ref = oracle.conv_fwd(xf, np.ascontiguousarray(wf[ks]), dict(p, k=len(ks)))
+    check_close(out[..., ks], ref, "f4_igemm_fwd_pointwise")

@@ -100,6 +100,7 @@ EXPECT = {
     "f3_wgrad_pointwise": api.VAR_WGRAD_POINTWISE,
     "f3_wgrad_3x3": api.VAR_WGRAD_SPLITK,
     "f4_splitk_dgrad": api.VAR_DGRAD_SPLITK,
+    "f4_igemm_fwd_pointwise": api.VAR_FWD_IGEMM,
 }
 
 OPC = {"fwd": api.OP_FWD, "dgrad": api.OP_DGRAD, "wgrad": api.OP_WGRAD}
@@ -380,4 +381,24 @@ def test_splitk_dgrad_workspace_follows_the_largest_chunk_and_is_checked():
         assert e.value.status == api.WORKSPACE_TOO_SMALL
         with pytest.raises(api.CnhwcError) as e:
             api.cnhwc_dgrad(p, 0x1000000, 0x4000000, 0x8000000, None, need, None)
+        assert e.value.status == api.INVALID_ARG
+
+
+def test_fwd_igemm_acceptance_and_workspace():
+    """The implicit-GEMM forward takes stride-1 ungrouped problems whose padding
+    leaves a non-negative rotated padding; its workspace is the transformed
+    filter, independent of the batch."""
+    p = P(4, 16, 16, 64, 96, 3, 3, 1, 1, 1)
+    with api.override(variant=api.VAR_FWD_IGEMM):
+        name, var = api.cnhwc_plan(p, api.OP_FWD)
+        assert var == api.VAR_FWD_IGEMM and name.startswith("fwd_igemm_")
+        assert api.cnhwc_workspace_size(p, api.OP_FWD) == 96 * 9 * 64 * 2
+        assert api.cnhwc_workspace_size(dict(p, n=40), api.OP_FWD) == 96 * 9 * 64 * 2
+        for bad, why in ((dict(p, stride=2), "stride 1"), (dict(p, pad_h=3), "R-1"),
+                         (dict(p, groups=2), "groups")):
+            with pytest.raises(api.CnhwcError) as e:
+                api.cnhwc_plan(bad, api.OP_FWD)
+            assert e.value.status == api.UNSUPPORTED and why in e.value.reason
+        with pytest.raises(api.CnhwcError) as e:   # the workspace is required
+            api.cnhwc_fwd(p, 0x1000000, 0x4000000, 0x8000000, None, 0, None)
         assert e.value.status == api.INVALID_ARG
