@@ -177,7 +177,7 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
         a_u[i] = a_v[i] = -(1 << 30);
         if (row < a.bm && m < m_hi) {
             if (PW) {
-                a_base[i] = uint32_t((m * a.K + chunk * 8) * 2);
+                a_base[i] = uint32_t((m * a.K + g * a.Kg + chunk * 8) * 2);
             } else {
                 const int hw = cl.hc * cl.wc;
                 const int n = fdiv(m, cl.fd_hw);
@@ -194,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
     }
     // ---- per-lane B (W) sources: region q = wave + 4*i holds k-rows B_ROWS_PER_REG*q .. ----
     const int taps_rs = PW ? 1 : a.R * a.S;
-    const int wk_stride = PW ? a.C : taps_rs * a.Cg;     // elements between W k-rows
+    const int wk_stride = taps_rs * a.Cg;                // elements between W k-rows
     uint32_t b_voff[B_REG];
     int b_krow[B_REG];
 #pragma unroll
@@ -1455,7 +1455,6 @@ std::string dgrad_igemm_reason(const Prob& p, bool pointwise) {
         if (p.r != 1 || p.s != 1) return "pointwise path needs a 1x1 filter";
         if (p.stride != 1) return "pointwise path needs stride 1";
         if (p.pad_h != 0 || p.pad_w != 0) return "pointwise path needs zero padding";
-        if (p.groups != 1) return "pointwise path needs groups == 1";
     }
     if (p.cg % 8 != 0) return "channels per group of dx must be a multiple of 8";
     if (p.kg % 8 != 0) return "channels per group of dy must be a multiple of 8";
@@ -1638,13 +1637,12 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
     const bool sk = pl.variant == CNHWC_VAR_DGRAD_SPLITK;
     if (sk && (pl.split_c < 2 || ws == nullptr)) return CNHWC_UNSUPPORTED;
     const bool pw = pl.variant == CNHWC_VAR_DGRAD_POINTWISE ||
-                    (sk && p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0 &&
-                     p.groups == 1);
+                    (sk && p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0);
     // pointwise with C <= 64: the row-streamed kernel for K = 64..256 in
     // steps of 64, else the LDS-persistent kernel while the filter fits LDS
     // (tune 1 asks for the ring kernel, tune 3 or >= 16 for the LDS-persistent
     // one)
-    if (pw && !sk && pl.tune != 1 && p.c <= kPwBN) {
+    if (pw && !sk && pl.tune != 1 && p.c <= kPwBN && p.groups == 1) {
         if (pw_rows_ok(p) && pl.tune != 3 && pl.tune < 16) return launch_pw_rows(p, dy, w, dx, st);
         if (pw_stages(p.k) > 0) return launch_pw_persist(p, pl, dy, w, dx, st);
     }

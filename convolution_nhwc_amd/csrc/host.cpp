@@ -231,7 +231,9 @@ int choose(const Prob& p, int op, Plan* out) {
             const int split = ov.split_c > 0 ? ov.split_c : dgrad_splitk_auto(p);
             if (split > 1) ok = take(CNHWC_VAR_DGRAD_SPLITK, 0, split);
         }
-        if (!ok && p.groups == 1 && p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0)
+        // 1x1 stride-1 unpadded: the pointwise fast path, grouped too (the
+        // group's dY channels by offset, C/groups as the filter row stride)
+        if (!ok && p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0)
             ok = take(CNHWC_VAR_DGRAD_POINTWISE, 0, 1);
         if (!ok) ok = take(CNHWC_VAR_DGRAD_IGEMM, 0, 1);
         if (!ok) ok = take(CNHWC_VAR_DGRAD_GENERIC, 0, 1);

@@ -84,7 +84,7 @@ typedef struct cnhwc_problem {
 
 /* Kernel variants the dispatcher chooses among (cnhwc_plan names them). */
 #define CNHWC_VAR_AUTO 0
-#define CNHWC_VAR_DGRAD_POINTWISE 1  /* 1x1, stride 1, unpadded, ungrouped: dX = dY * W on MFMA */
+#define CNHWC_VAR_DGRAD_POINTWISE 1  /* 1x1, stride 1, unpadded (grouped too): dX = dY * W per group on MFMA */
 #define CNHWC_VAR_DGRAD_IGEMM 2      /* general R x S strided implicit-GEMM dgrad on MFMA */
 #define CNHWC_VAR_DGRAD_DW_STREAM 3  /* depthwise dgrad, row-streaming, cpl channels per lane */
 #define CNHWC_VAR_DGRAD_DW_ROTATED 4 /* depthwise dgrad, stride 1, rotated-filter tiled */

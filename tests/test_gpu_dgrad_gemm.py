@@ -37,6 +37,25 @@ def test_pointwise_parity(p):
     parity(p, "dgrad", 101)
 
 
+GROUPED_POINTWISE = [
+    P(1, 8, 8, 16, 16, 1, 1, groups=2),          # 8 channels a group
+    P(2, 14, 14, 512, 512, 1, 1, groups=2),      # 256 a group: two channel tiles per group
+    P(1, 9, 10, 96, 144, 1, 1, groups=3, dtype="bf16"),  # ragged K per group (48)
+]
+
+
+@pytest.mark.parametrize("p", GROUPED_POINTWISE, ids=ident)
+def test_grouped_pointwise_parity_and_bitwise_equal_to_general(p):
+    """Grouped 1x1 dgrad on the pointwise fast path (each group's dY channels
+    by offset, C/groups as the filter row stride): within tolerance of the
+    oracle and bit-identical to the general implicit-GEMM kernel."""
+    assert api.cnhwc_plan(p, api.OP_DGRAD)[1] == api.VAR_DGRAD_POINTWISE
+    _, fast = parity(p, "dgrad", 109)
+    with api.override(variant=api.VAR_DGRAD_IGEMM):
+        _, general = parity(p, "dgrad", 109)
+    assert np.array_equal(fast.cpu().numpy(), general.cpu().numpy())
+
+
 IGEMM = [
     P(2, 12, 12, 64, 64, 3, 3, 1, 1, 1),
     P(2, 14, 14, 64, 128, 3, 3, 2, 1, 1),

@@ -138,8 +138,16 @@ def test_dispatcher_falls_back_to_generic():
 
 def test_pointwise_only_for_its_shape_class():
     for p in [P(1, 8, 8, 16, 16, 1, 1, 2), P(1, 8, 8, 16, 16, 1, 1, 1, 1, 1),
-              P(1, 8, 8, 16, 16, 1, 1, groups=2), P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1)]:
+              P(1, 8, 8, 16, 16, 3, 3, 1, 1, 1)]:
         assert api.cnhwc_plan(p, api.OP_DGRAD)[1] != api.VAR_DGRAD_POINTWISE
+
+
+def test_grouped_pointwise_dispatch():
+    """Grouped 1x1 dgrad: the block-diagonal merge when its groups merge into
+    one MFMA tile, else the pointwise fast path with the group offsets."""
+    assert api.cnhwc_plan(P(1, 8, 8, 16, 16, 1, 1, groups=2), api.OP_DGRAD)[1] == api.VAR_DGRAD_POINTWISE
+    assert api.cnhwc_plan(P(2, 14, 14, 512, 512, 1, 1, groups=2), api.OP_DGRAD)[1] == api.VAR_DGRAD_POINTWISE
+    assert api.cnhwc_plan(P(1, 9, 11, 256, 128, 1, 1, groups=16), api.OP_DGRAD)[1] == api.VAR_DGRAD_GROUPED
 
 
 def test_forced_variant_refusals_carry_reasons():
