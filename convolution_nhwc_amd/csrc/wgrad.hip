@@ -43,10 +43,15 @@
 namespace cnhwc {
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kWBK = 128;        // output channels (k) per block
 constexpr int kWBM = 32;         // output pixels per stage (one MFMA depth)
-constexpr int kWStages = 4;
+
+// Block shapes: NW waves over a (32 NW output channels k) x (BJ input channels
+// j) tile, each wave 64 x 64 (or 32 x 64); NS ring stages.  4 waves: k 128,
+// 4 stages, two blocks a CU; 8 waves: k 256, 3 stages (the stage offsets stay
+// within the LDS immediate), two blocks a CU -- half the input-tile bytes per
+// product and half the per-wave gather work for the same per-wave tile.
+constexpr int wg_kb(int nw) { return 32 * nw; }
+constexpr int wg_stages(int nw) { return nw == 8 ? 3 : 4; }
 
 struct WgArgs {
     const void* x;
@@ -69,14 +74,16 @@ struct WgArgs {
 // rows) or, with 128 B rows, over 4 positions x the two row parities.
 template <int CHUNKS>
 __device__ inline int wswz(int row) {
-    if constexpr (CHUNKS == 16) return 2 * ((row & 3) | ((row >> 1) & 4));
+    if constexpr (CHUNKS >= 16) return 2 * ((row & 3) | ((row >> 1) & 4));
     else return 2 * (((row >> 1) & 1) | ((row >> 2) & 2));
 }
 
-template <typename T, int BJ, bool PW>
-__global__ __launch_bounds__(kThreads, 2) void wgrad_splitk_kernel(const WgArgs a) {
+template <typename T, int BJ, bool PW, int NW>
+__global__ __launch_bounds__(NW * 64, 2) void wgrad_splitk_kernel(const WgArgs a) {
+    constexpr int kWBK = wg_kb(NW);                  // output channels (k) per block
+    constexpr int kWStages = wg_stages(NW);
     constexpr int WAVES_J = BJ / 64;                 // 1 or 2
-    constexpr int WAVES_K = 4 / WAVES_J;             // 4 or 2
+    constexpr int WAVES_K = NW / WAVES_J;
     constexpr int WJT = 4;                           // 16-wide j tiles per wave
     constexpr int WKT = kWBK / (WAVES_K * 16);       // 16-wide k tiles per wave: 2 or 4
     constexpr int XROW = BJ * 2;                     // bytes of one input row in a stage
@@ -87,8 +94,9 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_splitk_kernel(const WgArgs 
     constexpr int STAGE = XBYTES + kWBM * YROW;
     constexpr int XD = XBYTES / 1024;                // 1 KB DMAs of the input tile
     constexpr int ND = STAGE / 1024;
-    constexpr int LPS = ND / 4;                      // DMAs per wave per stage
-    static_assert(ND % 4 == 0, "stage must split evenly over the four waves");
+    constexpr int LPS = ND / NW;                     // DMAs per wave per stage
+    static_assert(ND % NW == 0, "stage must split evenly over the waves");
+    static_assert((kWStages - 1) * STAGE < 65536, "stage offsets fit the LDS immediate");
     __shared__ __attribute__((aligned(1024))) unsigned char lds[kWStages * STAGE];
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -117,16 +125,16 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_splitk_kernel(const WgArgs 
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(a.x, a.x_bytes);
     const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
 
-    // ---- per-lane DMA roles: DMA q = 4*d + wave covers bytes [1024q, 1024q+1024)
+    // ---- per-lane DMA roles: DMA q = NW*d + wave covers bytes [1024q, 1024q+1024)
     // of a stage.  The first XL slots of every wave are input rows, the rest dY
     // rows, so the input gather's address arithmetic is shared by all waves ----
-    constexpr int XL = XD / 4;                       // input DMAs per wave per stage
-    static_assert(XD % 4 == 0, "input tile must split evenly over the four waves");
+    constexpr int XL = XD / NW;                      // input DMAs per wave per stage
+    static_assert(XD % NW == 0, "input tile must split evenly over the waves");
     int d_row[LPS];              // stage row (pixel 0..31)
     uint32_t d_chan[LPS];        // channel byte offset within the pixel, or kOob
 #pragma unroll
     for (int d = 0; d < LPS; ++d) {
-        const int q = 4 * d + wave;
+        const int q = NW * d + wave;
         if (d < XL) {
             const int row = q * (1024 / XROW) + lane / XCH;
             const int chunk = (lane % XCH) ^ wswz<XCH>(row);
@@ -189,7 +197,7 @@ __global__ __launch_bounds__(kThreads, 2) void wgrad_splitk_kernel(const WgArgs 
 #pragma unroll
         for (int d = 0; d < LPS; ++d) {
             const int m = g_m + d_row[d];
-            unsigned char* dst = lds + SL * STAGE + (4 * d + wave) * 1024;
+            unsigned char* dst = lds + SL * STAGE + (NW * d + wave) * 1024;
             if (d < XL) {
                 uint32_t off = kOob;
                 if constexpr (PW) {
@@ -385,10 +393,12 @@ __global__ __launch_bounds__(256) void wgrad_generic_kernel(
 }
 
 int wg_bj(const Prob& p) { return p.cg >= 128 ? 128 : 64; }
+// waves per block: 8 (256 output channels) for wide groups on both sides
+int wg_nw(const Prob& p) { return (wg_bj(p) == 128 && p.kg > 128) ? 8 : 4; }
 
 int64_t wg_tiles(const Prob& p) {
-    const int bj = wg_bj(p);
-    return int64_t(p.groups) * ((p.kg + kWBK - 1) / kWBK) * p.r * p.s * ((p.cg + bj - 1) / bj);
+    const int bj = wg_bj(p), kb = wg_kb(wg_nw(p));
+    return int64_t(p.groups) * ((p.kg + kb - 1) / kb) * p.r * p.s * ((p.cg + bj - 1) / bj);
 }
 
 }  // namespace
@@ -409,10 +419,16 @@ int wgrad_splits(const Prob& p, int tune) {
     if (tune > 0) return int(std::min<int64_t>(tune, p.n * p.ho * p.wo));
     const int64_t tiles = wg_tiles(p);
     const int64_t P = p.n * p.ho * p.wo;
+    if (wg_nw(p) == 8) {
+        // 8-wave blocks: at most one per compute unit (a second block on a CU
+        // halves both; 3x3 256-channel workload: 14 splits = 252 blocks 51.0
+        // us, 16 splits = 288 blocks 74.8 us), every split at least 8 stages
+        int64_t s = std::max<int64_t>(1, kNumCUs / tiles);
+        return int(std::max<int64_t>(1, std::min<int64_t>(s, P / (8 * kWBM))));
+    }
     // One block per compute unit, every split at least 8 stages deep.  More
     // splits shorten the blocks but each adds a full fp32 partial of dW to
-    // the workspace traffic (written here, read by the reduce): on the 3x3
-    // 256-channel workload 8 splits measure 70.7 us, 16 73.6 us, 32 77.5 us.
+    // the workspace traffic (written here, read by the reduce).
     int64_t s = std::max<int64_t>(1, (kNumCUs + tiles - 1) / tiles);
     s = std::min<int64_t>(s, std::max<int64_t>(1, P / (8 * kWBM)));
     // a multiple of 8 blocks lets the XCD remap deal contiguous runs
@@ -433,7 +449,8 @@ int launch_wgrad_splitk(const Prob& p, const Plan& pl, const void* x, const void
     a.Ho = int(p.ho); a.Wo = int(p.wo); a.Cg = int(p.cg); a.Kg = int(p.kg);
     a.P = int(p.n * p.ho * p.wo);
     const int bj = wg_bj(p);
-    a.kblocks = int((p.kg + kWBK - 1) / kWBK);
+    const int nw = wg_nw(p);
+    a.kblocks = int((p.kg + wg_kb(nw) - 1) / wg_kb(nw));
     a.jblocks = int((p.cg + bj - 1) / bj);
     a.tiles = int(wg_tiles(p));
     a.splits = splits;
@@ -447,14 +464,17 @@ int launch_wgrad_splitk(const Prob& p, const Plan& pl, const void* x, const void
     a.remap = blocks % 8 == 0 ? 1 : 0;
     const bool pw = pl.variant == CNHWC_VAR_WGRAD_POINTWISE;
     const bool bf = p.dtype == CNHWC_BF16;
-#define CNHWC_WG(T, BJ, PW) hipLaunchKernelGGL((wgrad_splitk_kernel<T, BJ, PW>), dim3(unsigned(blocks)), \
-                                               dim3(kThreads), 0, st, a)
-    if (bj == 128) {
-        if (pw) { if (bf) CNHWC_WG(BF16, 128, true); else CNHWC_WG(F16, 128, true); }
-        else { if (bf) CNHWC_WG(BF16, 128, false); else CNHWC_WG(F16, 128, false); }
+#define CNHWC_WG(T, BJ, PW, NW) hipLaunchKernelGGL((wgrad_splitk_kernel<T, BJ, PW, NW>), dim3(unsigned(blocks)), \
+                                                   dim3(NW * 64), 0, st, a)
+    if (bj == 128 && nw == 8) {
+        if (pw) { if (bf) CNHWC_WG(BF16, 128, true, 8); else CNHWC_WG(F16, 128, true, 8); }
+        else { if (bf) CNHWC_WG(BF16, 128, false, 8); else CNHWC_WG(F16, 128, false, 8); }
+    } else if (bj == 128) {
+        if (pw) { if (bf) CNHWC_WG(BF16, 128, true, 4); else CNHWC_WG(F16, 128, true, 4); }
+        else { if (bf) CNHWC_WG(BF16, 128, false, 4); else CNHWC_WG(F16, 128, false, 4); }
     } else {
-        if (pw) { if (bf) CNHWC_WG(BF16, 64, true); else CNHWC_WG(F16, 64, true); }
-        else { if (bf) CNHWC_WG(BF16, 64, false); else CNHWC_WG(F16, 64, false); }
+        if (pw) { if (bf) CNHWC_WG(BF16, 64, true, 4); else CNHWC_WG(F16, 64, true, 4); }
+        else { if (bf) CNHWC_WG(BF16, 64, false, 4); else CNHWC_WG(F16, 64, false, 4); }
     }
 #undef CNHWC_WG
     return CNHWC_OK;

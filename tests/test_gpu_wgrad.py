@@ -34,12 +34,14 @@ SPLITK = [
     P(1, 5, 4, 32, 32, 3, 3, 1, 1, 1),                     # 20 output pixels: one partial stage
     P(2, 16, 16, 16, 16, 1, 1, 2),                         # 1x1 stride 2
     P(1, 9, 9, 24, 40, 4, 2, 3, 1, 0),                     # stride 3, even filter sizes
+    P(1, 8, 9, 128, 256, 3, 3, 1, 1, 1, dtype="bf16"),     # 8-wave block: 256 k x 128 j
 ]
 POINTWISE = [
     P(2, 14, 14, 64, 256, 1, 1),
     P(3, 7, 9, 200, 48, 1, 1, dtype="bf16"),               # ragged j blocks (128 + 72), 189 pixels
     P(1, 3, 5, 16, 16, 1, 1),                              # 15 pixels
     P(2, 8, 8, 64, 64, 1, 1, groups=4),                    # grouped pointwise, Cg = Kg = 16
+    P(2, 6, 7, 128, 384, 1, 1),                            # 8-wave blocks, ragged second k block
 ]
 GENERIC = [
     P(2, 8, 8, 3, 5, 3, 3, 1, 1, 1),
