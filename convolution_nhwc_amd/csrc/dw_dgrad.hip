@@ -269,8 +269,6 @@ constexpr int kTileCB = 64;                  // channels per block
 // (2 for 7x7: its 7 x 4 weight pairs and 2 x 7 x 2 accumulators fill the
 // register file)
 constexpr int tile_thl(int r) { return r >= 7 ? 2 : 4; }
-// weight pairs held in registers (else read from LDS at each use)
-constexpr bool tile_wreg(int) { return true; }
 constexpr int tile_th(int r) { return tile_thl(r) * kTilePBH; }
 
 struct TileArgs {
@@ -289,17 +287,20 @@ struct TileGeo {
     static constexpr int NL = (R + 1) / 2;                    // filter row pairs
     static constexpr int THL = tile_thl(R);
     static constexpr int TH = THL * kTilePBH;
-    static constexpr int WR = TH + R;                         // window rows (guard row first)
+    static constexpr int WR = TH + R - 1;                     // window rows
     static constexpr int WC = kTileTW + S - 1;                // window columns
     static constexpr int NPIX = WR * WC;
     static constexpr int WIN_BYTES = (NPIX + 7) / 8 * 1024;   // whole 8-pixel loads
     static constexpr int RAW_BYTES = (kTileCB * R * S * 2 + 1023) / 1024 * 1024;
-    static constexpr int WTS = NL * S * kTileCB;              // weight pair words
-    static constexpr int LDS = WIN_BYTES + RAW_BYTES + WTS * 4;
+    static constexpr int LDS = WIN_BYTES + RAW_BYTES;
 };
 
+// blocks per CU: 3x3 four (40 KiB of LDS, 100 VGPRs); 5x5 and 7x7 two (their
+// 180-230 VGPRs allow no more, whatever the LDS)
+constexpr int tile_occupancy(int r) { return r == 3 ? 4 : 2; }
+
 template <typename T, int R, int S>
-__global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
+__global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const TileArgs a) {
     using G = TileGeo<R, S>;
     constexpr int NL = G::NL, WC = G::WC, NPIX = G::NPIX;
     constexpr int kTileTHL = G::THL, kTileTH = G::TH;
@@ -307,7 +308,6 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
     constexpr int RV = kTileTWL + S - 1;                      // window columns a lane reads
     __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
     const unsigned short* const raw = reinterpret_cast<const unsigned short*>(lds + G::WIN_BYTES);
-    uint32_t* const wts = reinterpret_cast<uint32_t*>(lds + G::WIN_BYTES + G::RAW_BYTES);
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -328,7 +328,7 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
     const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
 
-    // ---- window: pixel q = (row, col) holds dY(h0 + pad_h - R + row, w0 + pad_w - (S-1) + col) ----
+    // ---- window: pixel q = (row, col) holds dY(h0 + pad_h - (R-1) + row, w0 + pad_w - (S-1) + col) ----
     {
         const int chunk = lane & 7;
         const bool cin = c0 + chunk * 8 < a.C;
@@ -338,7 +338,7 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
             if (q0 < NPIX) {
                 const int q = q0 + (lane >> 3);
                 const int row = q / WC, col = q - (q / WC) * WC;
-                const int u = h0 + a.pad_h - R + row, v = w0 + a.pad_w - (S - 1) + col;
+                const int u = h0 + a.pad_h - (R - 1) + row, v = w0 + a.pad_w - (S - 1) + col;
                 uint32_t off = kOob;
                 if (cin && q < NPIX && u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
                     off = uint32_t((((n * a.Ho + u) * a.Wo + v) * a.C + c0 + chunk * 8) * 2);
@@ -354,42 +354,54 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
                   uint32_t(c0 * R * S * 2));
     wait_vm<0>();
     __syncthreads();
-    // ---- weight pairs: word (i, t, ch) = (W[c][2i][t], W[c][2i+1][t]) ----
+    const int cp = lane & 31;                                 // channel pair
+    const int pb = 2 * wave + (lane >> 5);
+    const int lr0 = (pb / kTilePBW) * kTileTHL, lc0 = (pb % kTilePBW) * kTileTWL;
+
+    // ---- weight pairs: word (i, t, ch) = (W[c][2i][t], W[c][2i+1][t]), built
+    // in place over the staged filter (every thread first reads the taps of
+    // its words, then all write them), then each lane keeps its two channels'
+    // words in registers.  The rotated filter of the depthwise forward reads
+    // (R-1-r, S-1-t). ----
+    constexpr int WTS = NL * S * kTileCB;
+    constexpr int WPT = (WTS + 255) / 256;                    // words per thread
+    static_assert(WTS * 4 <= G::RAW_BYTES, "weight pairs fit over the staged filter");
+    uint32_t word[WPT];
 #pragma unroll
-    for (int k = 0; k < (G::WTS + 255) / 256; ++k) {
+    for (int k = 0; k < WPT; ++k) {
         const int e = tid + k * 256;
-        if (e < G::WTS) {
+        word[k] = 0u;
+        if (e < WTS) {
             const int ch = e % kTileCB;
             const int t = (e / kTileCB) % S;
             const int i = e / (kTileCB * S);
-            // tap (r, t) of the filter as used; the rotated filter reads (R-1-r, S-1-t)
             auto tap = [&](int r) {
                 return a.flip ? uint32_t(raw[ch * R * S + (R - 1 - r) * S + (S - 1 - t)])
                               : uint32_t(raw[ch * R * S + r * S + t]);
             };
             const uint32_t lo = tap(2 * i);
             const uint32_t hi = 2 * i + 1 < R ? tap(2 * i + 1) : 0u;
-            wts[e] = lo | (hi << 16);
+            word[k] = lo | (hi << 16);
         }
     }
     __syncthreads();
-
-    const int cp = lane & 31;                                 // channel pair
-    const int pb = 2 * wave + (lane >> 5);
-    const int lr0 = (pb / kTilePBW) * kTileTHL, lc0 = (pb % kTilePBW) * kTileTWL;
-
-    constexpr bool WREG = tile_wreg(R);
-    uint32_t wp[WREG ? NL : 1][WREG ? S : 1][2];
-    if constexpr (WREG) {
+    uint32_t* const wts = reinterpret_cast<uint32_t*>(lds + G::WIN_BYTES);
 #pragma unroll
-        for (int i = 0; i < NL; ++i)
-#pragma unroll
-            for (int t = 0; t < S; ++t) {
-                const i32x2 v = *reinterpret_cast<const i32x2*>(wts + (i * S + t) * kTileCB + cp * 2);
-                wp[i][t][0] = uint32_t(v[0]);
-                wp[i][t][1] = uint32_t(v[1]);
-            }
+    for (int k = 0; k < WPT; ++k) {
+        const int e = tid + k * 256;
+        if (e < WTS) wts[e] = word[k];
     }
+    __syncthreads();
+
+    uint32_t wp[NL][S][2];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            const i32x2 v = *reinterpret_cast<const i32x2*>(wts + (i * S + t) * kTileCB + cp * 2);
+            wp[i][t][0] = uint32_t(v[0]);
+            wp[i][t][1] = uint32_t(v[1]);
+        }
 
     float acc[kTileTHL][kTileTWL][2];
 #pragma unroll
@@ -397,6 +409,9 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
 #pragma unroll
         for (int w = 0; w < kTileTWL; ++w) acc[h][w][0] = acc[h][w][1] = 0.f;
 
+    // window row ul - 1 of the lane tile is walked at step ul; the pair partner
+    // of the first row (one row above the window) only ever meets the zero
+    // filter row R of odd R, so any finite value serves: the first row itself
     const uint32_t* const win = reinterpret_cast<const uint32_t*>(lds) + (lr0 * WC + lc0) * 32 + cp;
     uint32_t prev[RV], cur[RV];
 #pragma unroll
@@ -404,7 +419,7 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
 #pragma unroll
     for (int ul = 1; ul < kTileTHL + R; ++ul) {
 #pragma unroll
-        for (int v = 0; v < RV; ++v) cur[v] = win[(ul * WC + v) * 32];
+        for (int v = 0; v < RV; ++v) cur[v] = win[((ul - 1) * WC + v) * 32];
         uint32_t p0[RV], p1[RV];
 #pragma unroll
         for (int v = 0; v < RV; ++v) {
@@ -418,15 +433,7 @@ __global__ __launch_bounds__(256, 2) void dw_tile_kernel(const TileArgs a) {
             // tap-outer: consecutive dot2s update different accumulators
 #pragma unroll
             for (int t = 0; t < S; ++t) {
-                uint32_t w0, w1;
-                if constexpr (WREG) {
-                    w0 = wp[r / 2][t][0];
-                    w1 = wp[r / 2][t][1];
-                } else {
-                    const i32x2 v = *reinterpret_cast<const i32x2*>(wts + ((r / 2) * S + t) * kTileCB + cp * 2);
-                    w0 = uint32_t(v[0]);
-                    w1 = uint32_t(v[1]);
-                }
+                const uint32_t w0 = wp[r / 2][t][0], w1 = wp[r / 2][t][1];
 #pragma unroll
                 for (int wl = 0; wl < kTileTWL; ++wl) {
                     const int v = wl + S - 1 - t;
