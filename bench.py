@@ -200,6 +200,33 @@ def cpu_baseline():
                       "%d runs in %.1f s, %.3f s per run" % (reps, el, sec)}
 
 
+def cpl_matrix(args):
+    """The row-streaming depthwise dgrad kernel at every channels-per-lane
+    count on the depthwise workloads (forced through the test override),
+    beside the dispatcher's own pick; a refused count carries its reason."""
+    import torch
+    from convolution_nhwc_amd import api, synth
+    out = []
+    for name in ("c5_dw3x3", "c5_dw7x7", "c5_dw7x7_s2"):
+        ent = {"workload": name}
+        ent["dispatch"] = api.cnhwc_plan(synth.WORKLOADS[name]["prob"], api.OP_DGRAD)[0]
+        for cpl in (1, 2, 4, 8):
+            key = "cpl%d" % cpl
+            try:
+                with api.override(variant=api.VAR_DGRAD_DW_STREAM, cpl=cpl):
+                    wk = Workload(name)
+                    t = time_steps(wk, max(10, args.steps // 4), 3)
+                mm = metrics(name)
+                ent[key] = {"us": round(t * 1e3, 2), "GB/s": round(mm["bytes"] / (t * 1e-3) / 1e9, 1)}
+                del wk
+                torch.cuda.empty_cache()
+            except api.CnhwcError as e:
+                ent[key] = {"refused": e.reason[:160]}
+        out.append(ent)
+        print("# cpl %s" % json.dumps(ent), file=sys.stderr, flush=True)
+    return out
+
+
 def copy_calibration():
     """A plain device copy of 1 GiB, to scale the HBM byte counters."""
     import torch
@@ -290,6 +317,7 @@ def main():
             shapes.append(ent)
             print("# %s" % json.dumps(ent), file=sys.stderr, flush=True)
         line["shapes"] = shapes
+        line["cpl_matrix"] = cpl_matrix(args)
     if not args.no_cpu_baseline and not args.only:
         line["cpu_baseline"] = cpu_baseline()
     print(json.dumps(line), flush=True)

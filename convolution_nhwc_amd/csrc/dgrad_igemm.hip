@@ -222,15 +222,14 @@ __global__ __launch_bounds__(kThreads, 1) void dgrad_igemm_kernel(const IgemmArg
     // It runs two steps ahead of the multiply and is advanced without
     // branches; past the last step it keeps producing offsets whose loads are
     // either range-checked zeros or in-range data of stages never multiplied.
-    int cur_tap = step0 / kchunks;
-    int cur_kk = (step0 - cur_tap * kchunks) * kBK;
-    int cur_ti = cl.nt > 0 ? cur_tap / cl.nt : 0;
-    int cur_tj = cur_tap - cur_ti * cl.nt;
+    const int tap0 = step0 / kchunks;
+    int cur_kk = (step0 - tap0 * kchunks) * kBK;
+    int cur_ti = cl.nt > 0 ? tap0 / cl.nt : 0;
+    int cur_tj = tap0 - cur_ti * cl.nt;
     auto advance = [&]() {
         cur_kk += kBK;
         const bool wrap = cur_kk >= a.Kg;
         cur_kk = wrap ? 0 : cur_kk;
-        cur_tap += wrap ? 1 : 0;
         cur_tj += wrap ? 1 : 0;
         const bool wrap2 = cur_tj >= cl.nt;
         cur_tj = wrap2 ? 0 : cur_tj;

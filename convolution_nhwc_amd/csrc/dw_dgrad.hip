@@ -251,10 +251,10 @@ bool dispatch_stream(const StreamCfg& c, const StreamArgs& a, hipStream_t st) {
 // ============================ LDS-tiled (small filters) =====================
 //
 // Stride-1 depthwise dgrad for R x S <= 7 x 7 with the dY window of a tile
-// staged in LDS.  A block owns 8 x 28 dX pixels x 64 channels: the window (one
-// guard row above, R-1 rows and S-1 columns of halo) is loaded with 16-byte
-// asynchronous loads straight into LDS, 128 bytes per pixel, and the block's
-// weights go to LDS as row pairs.  Each lane then owns 4 x 7 pixels x 2
+// staged in LDS.  A block owns 8 x 28 dX pixels x 64 channels: the window (R-1
+// rows and S-1 columns of halo) is loaded with 16-byte asynchronous loads
+// straight into LDS, 128 bytes per pixel, and the block's weights go to LDS as
+// row pairs (over the staged filter).  Each lane then owns 4 x 7 pixels x 2
 // channels: it walks the window rows once, makes the vertical pairs
 // (dY[u][v], dY[u-1][v]) of its two channels with one byte permute each, and
 // feeds every pair to all the outputs and taps that use it

@@ -120,6 +120,10 @@ WORKLOADS = {
                      prob=problem(16, 56, 56, 384, 384, 3, 3, 1, 1, 1, groups=384)),
     "c5_dw7x7": dict(op="dgrad", seed=52, fan_in=49,
                      prob=problem(16, 56, 56, 384, 384, 7, 7, 1, 3, 3, groups=384)),
+    # the pages' stride-2 channel-packed cases (7x7) at the C5 shape: the
+    # row-streaming kernel's dispatch case
+    "c5_dw7x7_s2": dict(op="dgrad", seed=56, fan_in=49,
+                        prob=problem(16, 56, 56, 384, 384, 7, 7, 2, 3, 3, groups=384)),
     "c5_dw31x31": dict(op="dgrad", seed=53, fan_in=961,
                        prob=problem(8, 32, 32, 256, 256, 31, 31, 1, 15, 15, groups=256)),
     "c5_dw51x5": dict(op="dgrad", seed=54, fan_in=255,

@@ -128,7 +128,7 @@ def test_stream_and_rotated_agree():
 def test_cpl_matrix_on_the_3x3_and_7x7_workloads():
     """Every cpl the dispatcher admits for the two row-streaming workloads
     (on 2 of their 16 images); refusals must carry a register-budget reason."""
-    for name in ("c5_dw3x3", "c5_dw7x7"):
+    for name in ("c5_dw3x3", "c5_dw7x7", "c5_dw7x7_s2"):
         p = dict(synth.WORKLOADS[name]["prob"], n=2)
         for cpl in (8, 4, 2):
             try:
@@ -141,7 +141,7 @@ def test_cpl_matrix_on_the_3x3_and_7x7_workloads():
                 parity(p, "dgrad", 305)
 
 
-@pytest.mark.parametrize("name", ["c5_dw3x3", "c5_dw7x7", "c5_dw31x31", "c5_dw51x5", "c5_dw5x51"])
+@pytest.mark.parametrize("name", ["c5_dw3x3", "c5_dw7x7", "c5_dw7x7_s2", "c5_dw31x31", "c5_dw51x5", "c5_dw5x51"])
 def test_full_size_sampled_images(name):
     wl = synth.WORKLOADS[name]
     p = wl["prob"]

@@ -91,6 +91,7 @@ EXPECT = {
     "c4b_grouped_fwd": api.VAR_FWD_GROUPED,
     "c5_dw3x3": api.VAR_DGRAD_DW_TILED,
     "c5_dw7x7": api.VAR_DGRAD_DW_TILED,
+    "c5_dw7x7_s2": api.VAR_DGRAD_DW_STREAM,
     "c5_dw31x31": api.VAR_DGRAD_DW_ROTATED,
     "c5_dw51x5": api.VAR_DGRAD_DW_ROTATED,
     "c5_dw5x51": api.VAR_DGRAD_DW_ROTATED,
