@@ -103,18 +103,42 @@ __global__ __launch_bounds__(256, 2) void dw_stream_kernel(const StreamArgs a) {
 
     // weight pairs (W[c][r][t], W[c][r+ST][t]) per leader r, tap t, channel
     uint32_t wp[NL][S][CPL];
+    if constexpr (CPL >= 2) {
+        // the lane's CPL filters are one contiguous run of CPL*R*S elements
+        // starting at an even element (c0 is a multiple of CPL): dword loads,
+        // taps picked out at compile-time positions
+        constexpr int NWD = CPL * R * S / 2;
+        uint32_t fw[NWD];
+        const uint32_t base = uint32_t(c0) * (R * S) * 2u;
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        const int r = (i / ST) * 2 * ST + (i % ST);
+        for (int k = 0; k < NWD; ++k) fw[k] = uint32_t(buf_load4(rw, base + 4u * k));
+        auto elem = [&](int f) -> uint32_t { return (fw[f >> 1] >> ((f & 1) * 16)) & 0xffffu; };
 #pragma unroll
-        for (int t = 0; t < S; ++t)
+        for (int i = 0; i < NL; ++i) {
+            const int r = (i / ST) * 2 * ST + (i % ST);
 #pragma unroll
-            for (int ch = 0; ch < CPL; ++ch) {
-                const uint32_t base = uint32_t(c0 + ch) * (R * S);
-                const uint32_t lo = buf_load2(rw, (base + r * S + t) * 2u);
-                const uint32_t hi = r + ST < R ? uint32_t(buf_load2(rw, (base + (r + ST) * S + t) * 2u)) : 0u;
-                wp[i][t][ch] = lo | (hi << 16);
-            }
+            for (int t = 0; t < S; ++t)
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch) {
+                    const uint32_t lo = elem(ch * R * S + r * S + t);
+                    const uint32_t hi = r + ST < R ? elem(ch * R * S + (r + ST) * S + t) : 0u;
+                    wp[i][t][ch] = lo | (hi << 16);
+                }
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < NL; ++i) {
+            const int r = (i / ST) * 2 * ST + (i % ST);
+#pragma unroll
+            for (int t = 0; t < S; ++t)
+#pragma unroll
+                for (int ch = 0; ch < CPL; ++ch) {
+                    const uint32_t base = uint32_t(c0 + ch) * (R * S);
+                    const uint32_t lo = buf_load2(rw, (base + r * S + t) * 2u);
+                    const uint32_t hi = r + ST < R ? uint32_t(buf_load2(rw, (base + (r + ST) * S + t) * 2u)) : 0u;
+                    wp[i][t][ch] = lo | (hi << 16);
+                }
+        }
     }
 
     auto load_row = [&](int u, V (&row)[NV]) {
