@@ -35,9 +35,10 @@
 // which hands each lane four consecutive k of one channel.  Per-lane base
 // addresses are computed once; in the loop the uniform parts of the global
 // offsets go in the scalar offset field, the stage offsets in the LDS
-// instructions' immediate field, and a tap's validity per row is one bit of a
-// per-lane mask, folded into bit 31 of the load offset (out of range, so the
-// buffer descriptor returns zeros).  Each step's LDS reads and loads are
+// instructions' immediate field, and a tap is valid for a row when the row's
+// dY coordinates minus the tap's offsets fall inside dY (else the load offset
+// is out of range, so the buffer descriptor returns zeros).  Each step's LDS
+// reads and loads are
 // placed between its matrix instructions.  The MFMA computes the transposed
 // tile (channels x pixels) so each lane ends with four consecutive channels of
 // one pixel; the epilogue rounds to fp16/bf16 (RNE) and restages through LDS
