@@ -148,20 +148,24 @@ int cnhwc_chunk_plan(const cnhwc_problem* prob, int op, int64_t* counts, int64_t
 /* Forward pass.  x: device [N,H,W,C]; w: device [K,R,S,C/groups];
  * y: device [N,Ho,Wo,K] (written); ws: device scratch of ws_bytes (may be NULL
  * when cnhwc_workspace_size() reports 0; its contents on return are
- * unspecified). */
+ * unspecified: split-C partial sums, or the implicit-GEMM forward's
+ * transformed filter). */
 int cnhwc_fwd(const cnhwc_problem* prob, const void* x, const void* w, void* y,
               void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Backward-data pass.  dy: device [N,Ho,Wo,K]; w: device [K,R,S,C/groups];
- * dx: device [N,H,W,C] (written, every element).  ws as for cnhwc_fwd. */
+ * dx: device [N,H,W,C] (written, every element).  ws as for cnhwc_fwd (the
+ * split-K kernel keeps one fp32 partial dx per reduction split there, summed
+ * in ascending split order by a second launch). */
 int cnhwc_dgrad(const cnhwc_problem* prob, const void* dy, const void* w, void* dx,
                 void* ws, size_t ws_bytes, void* hip_stream);
 
 /* Weight-gradient pass.  x: device [N,H,W,C]; dy: device [N,Ho,Wo,K];
  * dw: device [K,R,S,C/groups] (written, every element).  ws as for cnhwc_fwd
  * (the split-K kernels keep one fp32 partial dw per pixel split there; a
- * second launch sums the splits in ascending order and rounds once; each
- * batch chunk contributes splits of its own). */
+ * second launch sums the splits in a fixed order -- ascending within
+ * contiguous split ranges, then the range sums ascending -- and rounds once;
+ * each batch chunk contributes splits of its own). */
 int cnhwc_wgrad(const cnhwc_problem* prob, const void* x, const void* dy, void* dw,
                 void* ws, size_t ws_bytes, void* hip_stream);
 
