@@ -534,7 +534,10 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
 
     // ---- stage the dY window: rows h0 - ph2 .., columns w0 - pw2 .., 8 channels ----
-    // word layout: [row][col][4 channel pairs], row stride a.row_dw words
+    // word layout: [row][col][4 channel pairs] with 4 pad words after every 8
+    // columns and a row stride of a.row_dw words (= 8 mod 32): the 64 lanes of
+    // a read (4 channel pairs x 4 column groups 8 columns apart x 4 row groups
+    // 2 rows apart) then fall on 32 distinct banks, two lanes each
     uint32_t* win = smem;
     const int npix = a.IHB * a.IWB;
     for (int q = tid; q < npix; q += NT) {
@@ -544,7 +547,7 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
         if (u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
             off = uint32_t(((n * a.Ho + u) * a.Wo + v) * a.C + c0) * 2u;
         const i32x4 val = buf_load16(rdy, off);
-        *reinterpret_cast<i32x4*>(win + ih * a.row_dw + iw * 4) = val;
+        *reinterpret_cast<i32x4*>(win + ih * a.row_dw + iw * 4 + (iw >> 3) * 4) = val;
     }
     // ---- stage rotated weight pairs: [rp][t][8 channels] words ----
     uint32_t* wpl = smem + a.IHB * a.row_dw;
@@ -618,11 +621,14 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
             f.w0[t] = uint32_t(v[0]);
             f.w1[t] = uint32_t(v[1]);
         }
-        const uint32_t* r0 = win + (orow + 2 * lrp) * a.row_dw + (ocol + lts * kRotTB) * 4 + cp;
+        // the slice starts on an 8-column boundary, so column vl of it carries
+        // (vl >> 3) more pad words than the first
+        const int iw0 = ocol + lts * kRotTB;
+        const uint32_t* r0 = win + (orow + 2 * lrp) * a.row_dw + iw0 * 4 + (iw0 >> 3) * 4 + cp;
 #pragma unroll
         for (int i = 0; i <= kRotTHT; ++i)
 #pragma unroll
-            for (int vl = 0; vl < NV; ++vl) f.x[i][vl] = r0[i * a.row_dw + vl * 4];
+            for (int vl = 0; vl < NV; ++vl) f.x[i][vl] = r0[i * a.row_dw + vl * 4 + (vl >> 3) * 4];
         ++lts;
         const bool wrap = lts >= ts_hi;
         lts = wrap ? ts_lo : lts;
@@ -707,7 +713,9 @@ bool rot_geometry(const Prob& p, RotArgs* a, size_t* lds) {
     // rows: tile rows + 2*rpairs (pairs reach row i + 2rp + 1); columns: tile + padded slices
     a->IHB = 32 + 2 * a->rpairs;
     a->IWB = 32 + a->tslices * kRotTB;
-    a->row_dw = a->IWB * 4 + 4;
+    // 4 words a column, 4 pad words after every 8 columns, stride = 8 mod 32
+    const int base = a->IWB * 4 + (a->IWB / kRotTB) * 4;
+    a->row_dw = base + ((8 - base % 32) + 32) % 32;
     const size_t win = size_t(a->IHB) * a->row_dw * 4;
     const size_t wts = size_t(a->rpairs) * a->tslices * kRotTB * kRotCB * 4;
     // the tap groups' partial sums reuse the window's LDS at the end
