@@ -323,13 +323,80 @@ struct TileGeo {
 // 180-230 VGPRs allow no more, whatever the LDS)
 constexpr int tile_occupancy(int r) { return r == 3 ? 4 : 2; }
 
+// Accumulates a lane tile (THL rows x kTileTWL columns x 2 channels) from a
+// staged window: win points at the lane tile's first window pixel and channel
+// pair (window pixels 128 bytes apart, rows kTileTW + S - 1 pixels long).
+// Window row ul - 1 of the lane tile is walked at step ul; the pair partner of
+// the first row (one row above the window) only ever meets the zero filter row
+// R of odd R, so any finite value serves: the first row itself.
+template <typename T, int R, int S, int THL>
+__device__ __forceinline__ void tile_accumulate(const uint32_t* win, const uint32_t (&wp)[(R + 1) / 2][S][2],
+                                                float (&acc)[THL][kTileTWL][2]) {
+    constexpr int WC = kTileTW + S - 1;
+    constexpr int RV = kTileTWL + S - 1;                      // window columns a lane reads
+#pragma unroll
+    for (int h = 0; h < THL; ++h)
+#pragma unroll
+        for (int w = 0; w < kTileTWL; ++w) acc[h][w][0] = acc[h][w][1] = 0.f;
+    uint32_t prev[RV], cur[RV];
+#pragma unroll
+    for (int v = 0; v < RV; ++v) prev[v] = win[v * 32];
+#pragma unroll
+    for (int ul = 1; ul < THL + R; ++ul) {
+#pragma unroll
+        for (int v = 0; v < RV; ++v) cur[v] = win[((ul - 1) * WC + v) * 32];
+        uint32_t p0[RV], p1[RV];
+#pragma unroll
+        for (int v = 0; v < RV; ++v) {
+            p0[v] = pair_lo(cur[v], prev[v]);   // channel 2cp: (row ul, row ul-1)
+            p1[v] = pair_hi(cur[v], prev[v]);   // channel 2cp+1
+        }
+#pragma unroll
+        for (int hl = 0; hl < THL; ++hl) {
+            const int r = hl + R - ul;         // first tap row of the pair
+            if (r < 0 || r >= R || (r & 1)) continue;
+            // tap-outer: consecutive dot2s update different accumulators
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+                const uint32_t w0 = wp[r / 2][t][0], w1 = wp[r / 2][t][1];
+#pragma unroll
+                for (int wl = 0; wl < kTileTWL; ++wl) {
+                    const int v = wl + S - 1 - t;
+                    acc[hl][wl][0] = dot2<T>(p0[v], w0, acc[hl][wl][0]);
+                    acc[hl][wl][1] = dot2<T>(p1[v], w1, acc[hl][wl][1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < RV; ++v) prev[v] = cur[v];
+    }
+}
+
+// Stores a lane tile at dX (n, h .., w .., channels c, c + 1): 4 bytes a pixel.
+template <typename T, int THL>
+__device__ __forceinline__ void tile_store(const TileArgs& a, __amdgpu_buffer_rsrc_t rdx,
+                                           const float (&acc)[THL][kTileTWL][2], int n, int h0, int w0,
+                                           int c) {
+    if (c >= a.C) return;
+#pragma unroll
+    for (int hl = 0; hl < THL; ++hl) {
+        const int h = h0 + hl;
+#pragma unroll
+        for (int wl = 0; wl < kTileTWL; ++wl) {
+            const int w = w0 + wl;
+            if (h < a.H && w < a.W)
+                buf_store4(int(pack2<T>(acc[hl][wl][0], acc[hl][wl][1])), rdx,
+                           uint32_t(((n * a.H + h) * a.W + w) * a.C + c) * 2u);
+        }
+    }
+}
+
 template <typename T, int R, int S>
 __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const TileArgs a) {
     using G = TileGeo<R, S>;
     constexpr int NL = G::NL, WC = G::WC, NPIX = G::NPIX;
     constexpr int kTileTHL = G::THL, kTileTH = G::TH;
     constexpr int LOADS = (NPIX + 31) / 32;                   // 8-pixel loads per wave
-    constexpr int RV = kTileTWL + S - 1;                      // window columns a lane reads
     __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
     const unsigned short* const raw = reinterpret_cast<const unsigned short*>(lds + G::WIN_BYTES);
 
@@ -371,11 +438,12 @@ __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const T
         }
     }
     // ---- the block's filters: 64 channels x R*S taps, contiguous in W ----
+    // (the block's base goes in the lane offset, which the range check covers:
+    // the last channel block's rows past C read zeros)
 #pragma unroll
     for (int i = 0; i < G::RAW_BYTES / 1024; ++i)
         if ((i & 3) == wave)
-            dma16(rw, lds + G::WIN_BYTES + i * 1024, uint32_t(i * 1024 + lane * 16),
-                  uint32_t(c0 * R * S * 2));
+            dma16(rw, lds + G::WIN_BYTES + i * 1024, uint32_t(c0 * R * S * 2 + i * 1024 + lane * 16), 0);
     wait_vm<0>();
     __syncthreads();
     const int cp = lane & 31;                                 // channel pair
@@ -428,63 +496,9 @@ __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const T
         }
 
     float acc[kTileTHL][kTileTWL][2];
-#pragma unroll
-    for (int h = 0; h < kTileTHL; ++h)
-#pragma unroll
-        for (int w = 0; w < kTileTWL; ++w) acc[h][w][0] = acc[h][w][1] = 0.f;
-
-    // window row ul - 1 of the lane tile is walked at step ul; the pair partner
-    // of the first row (one row above the window) only ever meets the zero
-    // filter row R of odd R, so any finite value serves: the first row itself
-    const uint32_t* const win = reinterpret_cast<const uint32_t*>(lds) + (lr0 * WC + lc0) * 32 + cp;
-    uint32_t prev[RV], cur[RV];
-#pragma unroll
-    for (int v = 0; v < RV; ++v) prev[v] = win[v * 32];
-#pragma unroll
-    for (int ul = 1; ul < kTileTHL + R; ++ul) {
-#pragma unroll
-        for (int v = 0; v < RV; ++v) cur[v] = win[((ul - 1) * WC + v) * 32];
-        uint32_t p0[RV], p1[RV];
-#pragma unroll
-        for (int v = 0; v < RV; ++v) {
-            p0[v] = pair_lo(cur[v], prev[v]);   // channel 2cp: (row ul, row ul-1)
-            p1[v] = pair_hi(cur[v], prev[v]);   // channel 2cp+1
-        }
-#pragma unroll
-        for (int hl = 0; hl < kTileTHL; ++hl) {
-            const int r = hl + R - ul;         // first tap row of the pair
-            if (r < 0 || r >= R || (r & 1)) continue;
-            // tap-outer: consecutive dot2s update different accumulators
-#pragma unroll
-            for (int t = 0; t < S; ++t) {
-                const uint32_t w0 = wp[r / 2][t][0], w1 = wp[r / 2][t][1];
-#pragma unroll
-                for (int wl = 0; wl < kTileTWL; ++wl) {
-                    const int v = wl + S - 1 - t;
-                    acc[hl][wl][0] = dot2<T>(p0[v], w0, acc[hl][wl][0]);
-                    acc[hl][wl][1] = dot2<T>(p1[v], w1, acc[hl][wl][1]);
-                }
-            }
-        }
-#pragma unroll
-        for (int v = 0; v < RV; ++v) prev[v] = cur[v];
-    }
-
-    // ---- store: 2 channels (4 bytes) per lane and pixel ----
-    const int c = c0 + 2 * cp;
-    if (c < a.C) {
-#pragma unroll
-        for (int hl = 0; hl < kTileTHL; ++hl) {
-            const int h = h0 + lr0 + hl;
-#pragma unroll
-            for (int wl = 0; wl < kTileTWL; ++wl) {
-                const int w = w0 + lc0 + wl;
-                if (h < a.H && w < a.W)
-                    buf_store4(int(pack2<T>(acc[hl][wl][0], acc[hl][wl][1])), rdx,
-                               uint32_t(((n * a.H + h) * a.W + w) * a.C + c) * 2u);
-            }
-        }
-    }
+    tile_accumulate<T, R, S, kTileTHL>(reinterpret_cast<const uint32_t*>(lds) + (lr0 * WC + lc0) * 32 + cp,
+                                       wp, acc);
+    tile_store<T, kTileTHL>(a, rdx, acc, n, h0 + lr0, w0 + lc0, c0 + 2 * cp);
 }
 
 // ============================ rotated filter ================================

@@ -182,8 +182,8 @@ const char* cnhwc_last_error(void);
  * every phase class on the ring kernel, 2 runs classes with two or more taps on
  * the dY-window kernel, a value of 16 or more sets the ring kernel's pixels per
  * tile; direct forward: 1 forces the register-staged kernel, 2 the input-window
- * kernel; split-K wgrad: the number of pixel splits per batch chunk; other
- * kernels ignore it);
+ * kernel; split-K wgrad: the number of pixel splits per batch chunk;
+ * depthwise rotated-filter: 1 runs one tap group; other kernels ignore it);
  * chunk_limit_bytes: the per-view byte limit of the chunk planner.  Pass NULL
  * to clear. */
 typedef struct cnhwc_override {

@@ -102,6 +102,22 @@ def test_tiled_and_stream_agree_on_exact_inputs():
     assert np.array_equal(a, b)
 
 
+TILED7 = [
+    DW(2, 37, 61, 200, 7, 7, 1, 3, 3),         # 5 x 3 tiles, 4 channel blocks (the last partial)
+    DW(3, 16, 28, 64, 7, 7, 1, 3, 3),          # whole tiles only
+    DW(1, 9, 12, 16, 7, 7, 1, 2, 5),           # one partial tile, odd pads
+    DW(2, 30, 33, 136, 7, 7, 1, 3, 3, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("p", TILED7, ids=ident)
+def test_tiled_7x7(p):
+    """7x7 over several tile rows, columns and channel blocks (the last one
+    partial), with the filter staged per channel block."""
+    with api.override(variant=api.VAR_DGRAD_DW_TILED):
+        parity(p, "dgrad", 308)
+
+
 @pytest.mark.parametrize("p,var,cpl", [(DW(1, 17, 19, 32, 3, 3, 1, 1, 1), api.VAR_DGRAD_DW_STREAM, 8),
                                        (DW(1, 17, 30, 64, 5, 5, 1, 2, 2), api.VAR_DGRAD_DW_TILED, 0),
                                        (DW(1, 17, 19, 32, 7, 7, 2, 3, 3), api.VAR_DGRAD_DW_STREAM, 2),

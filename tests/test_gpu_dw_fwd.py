@@ -55,6 +55,14 @@ def test_fwd_tiled_parity(p):
         parity(p, "fwd", 401)
 
 
+def test_fwd_tiled_7x7_several_channel_blocks():
+    """The depthwise forward at 7x7 over three channel blocks, the last one
+    partial, in bf16."""
+    p = DW(2, 30, 33, 136, 7, 7, 3, 3, dtype="bf16")
+    with api.override(variant=api.VAR_FWD_DW_TILED):
+        parity(p, "fwd", 402)
+
+
 @pytest.mark.parametrize("tune", [0, 1], ids=["split", "onegroup"])
 @pytest.mark.parametrize("p", ROT, ids=ident)
 def test_fwd_rotated_parity(p, tune):
