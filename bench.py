@@ -5,7 +5,10 @@ One step = one pass of the headline workload (the pointwise 1x1 dgrad,
 N=32, H=W=56, K=256 -> C=64, fp16) through the C ABI, on inputs already
 resident in HBM.  Steps rotate over enough copies of the operands that the
 256 MB Infinity Cache cannot serve a step from the previous one.  HIP events
-on the launch stream bracket exactly K steps after W warm-up steps.
+on the launch stream bracket exactly K steps after W warm-up steps; before
+those, each workload first runs back to back for 60 ms (settle_ms), since the
+GPU clock reaches its sustained value only after about 50 ms of load (a
+3x3 dgrad timed from idle reads ~8 % slow, a 7x7 depthwise one ~13 %).
 
 The JSON line also carries, per seeded workload of the method (forward, dgrad
 and weight-gradient shapes), the measured time and its fraction of the binding MI355X roof
@@ -160,8 +163,23 @@ class Workload:
           self.wss[j].data_ptr(), self.ws_bytes, self.stream)
 
 
+SETTLE_S = 0.06
+
+
+def settle(wk, seconds=SETTLE_S):
+    """Run steps back to back for `seconds` of host time so the GPU clock is
+    at its sustained value before warm-up and timing."""
+    import torch
+    t0 = time.time()
+    while time.time() - t0 < seconds:
+        for _ in range(100):
+            wk.step()
+        torch.cuda.synchronize()
+
+
 def time_steps(wk, steps, warmup):
     import torch
+    settle(wk)
     for _ in range(warmup):
         wk.step()
     torch.cuda.synchronize()
@@ -281,7 +299,7 @@ def main():
     line = {
         "metric": "effective conv TFLOP/s and HBM GB/s per shape, % of MI355X roofline",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "settle_ms": int(SETTLE_S * 1000), "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": head.p["dtype"], "data": "synthetic",
         "config": {"workload": head.name, "op": head.op, "kernel": head.kernel,
                    **{k: head.p[k] for k in ("n", "h", "w", "c", "k", "r", "s", "stride",
