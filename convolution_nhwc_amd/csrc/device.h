@@ -9,6 +9,8 @@
 #include <type_traits>
 #include <utility>
 
+#include "fastdiv.h"
+
 namespace cnhwc {
 
 typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
@@ -156,23 +158,6 @@ __device__ inline void wait_vm() {
 // LDS byte address (what ds_* instructions take) of a pointer into __shared__.
 __device__ inline uint32_t lds_addr(const void* p) {
     return uint32_t(reinterpret_cast<uintptr_t>((const __attribute__((address_space(3))) void*)p));
-}
-
-// Division by a launch-time constant d >= 1 as a multiply and a shift
-// (round-up reciprocal, the "add" form): exact for every dividend below 2^31.
-// The kernels use it for per-lane index arithmetic, where an integer divide
-// would cost tens of VALU instructions.
-struct FastDiv {
-    uint32_t mul, shift;
-};
-inline FastDiv make_fastdiv(uint32_t d) {
-    uint32_t l = 0;
-    while ((uint64_t(1) << l) < d) ++l;
-    const uint64_t m = ((uint64_t(1) << 32) * ((uint64_t(1) << l) - d)) / d + 1;
-    return FastDiv{uint32_t(m), l};
-}
-__device__ inline int fdiv(int q, FastDiv f) {
-    return int((__umulhi(uint32_t(q), f.mul) + uint32_t(q)) >> f.shift);
 }
 
 template <int I>

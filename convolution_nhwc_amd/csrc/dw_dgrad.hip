@@ -12,8 +12,12 @@
 //    dY moves as one cpl-wide vector per lane per column, lanes run along the
 //    flattened (column strip, channel) index so a wave's loads are contiguous.
 //  * dw_rotated (stride 1, filters up to 64 a side, non-square, per-axis
-//    padding): a stride-1 depthwise dgrad is the forward correlation of dY with
-//    the filter turned by 180 degrees at padding R-1-pad_h / S-1-pad_w.  A block
+//    padding; the Rotated-filter dgrad section of that page).  At stride 1 the
+//    adjoint's index relation dX[h][w] = sum_{r,t} dY[h+pad_h-r][w+pad_w-t] W[r][t]
+//    becomes, with r' = R-1-r and t' = S-1-t,
+//    dX[h][w] = sum_{r',t'} dY[h-(R-1-pad_h)+r'][w-(S-1-pad_w)+t'] W[R-1-r'][S-1-t'],
+//    a plain correlation with the reversed filter whose zero border is
+//    R-1-pad_h rows and S-1-pad_w columns.  A block
 //    owns a tile of dX rows x columns x 8 channels; the dY window of the tile
 //    and the rotated filter are staged in LDS, and each lane accumulates 2 rows
 //    x 8 columns x 2 channels, walking the filter one row pair and 8 columns at
@@ -761,7 +765,8 @@ std::string dw_stream_reason(const Prob& p, int cpl) {
         return "no row-streaming instance for filter " + std::to_string(p.r) + " stride " +
                std::to_string(p.stride) + " cpl " + std::to_string(cpl) +
                " (register budget: filter <= 7; cpl 8 only at 3x3, cpl 4 up to 5x5)";
-    if (p.n * p.h * p.w * p.c > (int64_t(1) << 30)) return "tensor exceeds the 32-bit element range";
+    if (p.h * p.w * p.c > (int64_t(1) << 30) || p.ho * p.wo * p.k > (int64_t(1) << 30))
+        return "one image exceeds the 32-bit element range";
     return "";
 }
 
@@ -771,8 +776,8 @@ std::string dw_tiled_reason(const Prob& p) {
     if (p.r != p.s || (p.r != 3 && p.r != 5 && p.r != 7))
         return "the LDS-tiled depthwise dgrad has 3x3, 5x5 and 7x7 instances";
     if (p.c % 8 != 0) return "the LDS-tiled depthwise dgrad needs C a multiple of 8";
-    if (p.n * p.h * p.w * p.c > (int64_t(1) << 30) || p.n * p.ho * p.wo * p.c > (int64_t(1) << 30))
-        return "tensor exceeds the 32-bit element range";
+    if (p.h * p.w * p.c > (int64_t(1) << 30) || p.ho * p.wo * p.c > (int64_t(1) << 30))
+        return "one image exceeds the 32-bit element range";
     return "";
 }
 
@@ -786,7 +791,8 @@ std::string dw_rotated_reason(const Prob& p) {
     RotArgs a{};
     size_t lds;
     if (!rot_geometry(p, &a, &lds)) return "staged dY window exceeds LDS";
-    if (p.n * p.h * p.w * p.c > (int64_t(1) << 30)) return "tensor exceeds the 32-bit element range";
+    if (p.h * p.w * p.c > (int64_t(1) << 30) || p.ho * p.wo * p.k > (int64_t(1) << 30))
+        return "one image exceeds the 32-bit element range";
     return "";
 }
 

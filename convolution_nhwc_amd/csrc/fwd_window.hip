@@ -501,7 +501,6 @@ std::string fwd_window_reason(const Prob& p, int split_c) {
     if (p.kg % 8 != 0) return "output channels per group must be a multiple of 8";
     if (p.h * p.w * p.c > (int64_t(1) << 30) || p.ho * p.wo * p.k > (int64_t(1) << 30))
         return "one image exceeds the 32-bit element range";
-    if (p.n * p.ho * p.wo > (int64_t(1) << 30)) return "too many output pixels";
     WinGeo g;
     if (!win_geo(p, win_bn(p), kBMC, &g)) return "input window of the smallest tile exceeds LDS";
     if (split_c > 1) {

@@ -292,7 +292,10 @@ ChunkBytes chunk_bytes(const Prob& p, int op, const Plan& pl) {
     return b;
 }
 
-int64_t limit_bytes() { return g_ov.chunk_limit_bytes > 0 ? g_ov.chunk_limit_bytes : kBufferLimit; }
+// The override may only lower the limit: no view may pass the kernels' 32-bit range.
+int64_t limit_bytes() {
+    return g_ov.chunk_limit_bytes > 0 ? std::min(g_ov.chunk_limit_bytes, kBufferLimit) : kBufferLimit;
+}
 
 // Balanced batch split: the fewest chunks that keep each per-chunk view within
 // the limit, sizes floor(N/chunks) or ceil(N/chunks), larger ones first.

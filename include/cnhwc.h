@@ -116,10 +116,17 @@ typedef struct cnhwc_problem {
                                       * implicit-GEMM dgrad kernels (large maps); the transformed filter
                                       * goes to the workspace */
 
-/* Output dims by the floor formula above.  INVALID_ARG for a bad descriptor. */
+/* Output dims by the floor formula above, the column count following pad_w
+ * ("feat(rocke): channel-packed and large-filter depthwise dgrad", Per-axis
+ * padding, and its review's count of output columns when pad_w differs from
+ * pad_h).  INVALID_ARG for a bad descriptor. */
 int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo);
 
-/* Workspace bytes the chosen kernel of pass `op` needs: split_c * N * Ho * Wo
+/* Workspace bytes the chosen kernel of pass `op` needs.  The workspace is where
+ * a split reduction keeps its fp32 partial sums until a second launch folds
+ * them into the output ("feat(rocke): split-C and grouped LDS-halo direct conv
+ * fwd kernels", description: the split_c variant and its second-pass
+ * reduction); the same scheme serves split-K dgrad and wgrad.  Sizes: split_c * N * Ho * Wo
  * * K * 4 bytes of fp32 partial sums for the split-C forward, splits * N * H *
  * W * C * 4 bytes for the split-K dgrad (N: the largest batch chunk), K * R * S *
  * C * 2 bytes (the transformed filter) for the implicit-GEMM forward, splits * K * R
@@ -128,7 +135,10 @@ int cnhwc_out_dims(const cnhwc_problem* prob, int64_t* ho, int64_t* wo);
  * least this many bytes to cnhwc_fwd / cnhwc_dgrad / cnhwc_wgrad. */
 int cnhwc_workspace_size(const cnhwc_problem* prob, int op, size_t* bytes);
 
-/* The dispatcher's choice for pass `op`: writes the kernel name (variant,
+/* The dispatcher's choice for pass `op`.  The pages' kernels ship with no
+ * dispatcher ("feat(rocke): channel-packed and large-filter depthwise dgrad",
+ * Motivation: the new binaries have no dispatcher wiring); this library adds
+ * one, and this call exposes its decision.  Writes the kernel name (variant,
  * element type, tile or channels-per-lane) into name[0..cap) (truncated,
  * always NUL-terminated when cap > 0) and, if `variant` is not NULL, the
  * CNHWC_VAR_* number.  UNSUPPORTED with a reason when no kernel accepts. */
@@ -136,7 +146,7 @@ int cnhwc_plan(const cnhwc_problem* prob, int op, char* name, size_t cap, int32_
 
 /* Batch split of the launches for pass `op`: every per-image view of x/dx,
  * y/dy and the workspace must stay within the kernels' 32-bit buffer range
- * (2^31 - 1 bytes, or the test override's limit), so the batch runs as
+ * (2^31 - 1 bytes, or a lower limit set by the test override), so the batch runs as
  * balanced chunks of floor(N/chunks) or ceil(N/chunks) images ("feat(rocke):
  * split-C and grouped LDS-halo direct conv fwd kernels", supporting changes).
  * Writes up to `cap` chunk sizes (in images, in launch order) into counts and
@@ -169,10 +179,21 @@ int cnhwc_dgrad(const cnhwc_problem* prob, const void* dy, const void* w, void* 
 int cnhwc_wgrad(const cnhwc_problem* prob, const void* x, const void* dy, void* dw,
                 void* ws, size_t ws_bytes, void* hip_stream);
 
-/* Reason for the last non-zero status on this thread ("" after success). */
+/* Reason for the last non-zero status on this thread ("" after success).  The
+ * checks run in a fixed order and the first failing one is reported, as the
+ * pages' C++ engine keeps its validators in the same order and with the same
+ * reason text as the Python one ("feat(rocke): channel-packed and large-filter
+ * depthwise dgrad", Technical Details, C++ engine).  The string is owned by
+ * the library and valid until the next call on the same thread. */
 const char* cnhwc_last_error(void);
 
-/* Test-only override of the dispatcher's choices, thread-local.  A zero field
+/* Test-only override of the dispatcher's choices, thread-local.  It is an A/B
+ * switch for tests and tuning sweeps, not a user knob: the kernel a shape
+ * gets in normal use is the dispatcher's selection alone, and an override
+ * only makes a comparison against that selection possible ("perf(rocke/conv):
+ * add the pointwise fast path dgrad was missing", the commit that takes the
+ * LDS-layout switch out of the sweep driver again because a sweep must only
+ * measure kernels that dispatch can select).  A zero field
  * keeps the automatic choice.  variant: a CNHWC_VAR_* to force (the call fails
  * with UNSUPPORTED and the variant's reason if it cannot run the problem);
  * cpl: depthwise channels per lane (1, 2, 4 or 8); split_c: number of channel

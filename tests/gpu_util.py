@@ -99,3 +99,51 @@ def parity(p, op, seed, exact=False):
         assert np.array_equal(got, ref), "exact mode: %d mismatches" % int(np.sum(got != ref))
         return 0.0, out
     return check_close(got, ref, str(p)), out
+
+
+def run_wgrad(p, xb, yb):
+    """Weight gradient through the C ABI on a NaN-poisoned dw and a NaN-filled
+    workspace."""
+    t = torch()
+    x, dy = to_device(xb), to_device(yb)
+    dw = poisoned((p["k"], p["r"], p["s"], p["c"] // p["groups"]), p["dtype"])
+    need = api.cnhwc_workspace_size(p, api.OP_WGRAD)
+    ws = t.full((max(need, 16) // 4,), float("nan"), dtype=t.float32, device="cuda")
+    api.cnhwc_wgrad(p, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), ws.data_ptr() if need else None,
+                    need, t.cuda.current_stream().cuda_stream)
+    t.cuda.synchronize()
+    return dw
+
+
+def workload_operands(name):
+    """The named workload's seeded operands exactly as the benchmark draws them:
+    (problem, op, (act_bits, act_f64), (second_bits, second_f64))."""
+    wl = synth.WORKLOADS[name]
+    p, op = wl["prob"], wl["op"]
+    ho, wo = oracle.out_dims(p)
+    x_shape = (p["n"], p["h"], p["w"], p["c"])
+    y_shape = (p["n"], ho, wo, p["k"])
+    w_shape = (p["k"], p["r"], p["s"], p["c"] // p["groups"])
+    if op == "wgrad":
+        a, b = synth.wgrad_operands(wl["seed"], x_shape, y_shape, p["dtype"])
+    else:
+        kw = dict(w_dist=wl["w_dist"]) if wl.get("w_dist") else dict(w_fan_in=wl["fan_in"])
+        a, b = synth.operands(wl["seed"], x_shape if op == "fwd" else y_shape, w_shape, p["dtype"], **kw)
+    return p, op, a, b
+
+
+def full_size_parity(name):
+    """The named workload at its full size, in the launch configuration the
+    benchmark times (automatic dispatch), compared with the oracle on every
+    output element (every image, channel and filter tap); returns the output
+    bits as a numpy uint16 array."""
+    p, op, (ab, af), (bb, bf) = workload_operands(name)
+    if op == "wgrad":
+        out = run_wgrad(p, ab, bb)
+        ref = oracle.conv_wgrad(af, bf, p)
+    else:
+        out = run_gpu(p, op, ab, bb)
+        ref = reference(p, op, af, bf)
+    bits = out.cpu().numpy().view(np.uint16)
+    check_close(synth.bits_to_f64(bits, p["dtype"]), ref, name)
+    return bits

@@ -7,7 +7,7 @@ import pytest
 import oracle
 from convolution_nhwc_amd import api, synth
 
-from gpu_util import check_close, from_device, operands, parity, run_gpu
+from gpu_util import check_close, from_device, full_size_parity, operands, parity, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -158,13 +158,5 @@ def test_cpl_matrix_on_the_3x3_and_7x7_workloads():
 
 
 @pytest.mark.parametrize("name", ["c5_dw3x3", "c5_dw7x7", "c5_dw7x7_s2", "c5_dw31x31", "c5_dw51x5", "c5_dw5x51"])
-def test_full_size_sampled_images(name):
-    wl = synth.WORKLOADS[name]
-    p = wl["prob"]
-    ho, wo = oracle.out_dims(p)
-    (ab, af), (wb, wf) = synth.operands(wl["seed"], (p["n"], ho, wo, p["k"]), (p["k"], p["r"], p["s"], 1),
-                                        p["dtype"], w_fan_in=wl["fan_in"])
-    got = from_device(run_gpu(p, "dgrad", ab, wb), p["dtype"])
-    one = dict(p, n=1)
-    for img in sorted({0, p["n"] // 2, p["n"] - 1}):
-        check_close(got[img:img + 1], oracle.conv_dgrad(af[img:img + 1], wf, one), "%s image %d" % (name, img))
+def test_full_size_all_images(name):
+    full_size_parity(name)

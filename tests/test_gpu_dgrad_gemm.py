@@ -6,7 +6,7 @@ import pytest
 import oracle
 from convolution_nhwc_amd import api, synth
 
-from gpu_util import check_close, from_device, operands, parity, run_gpu
+from gpu_util import check_close, from_device, full_size_parity, operands, parity, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -201,17 +201,7 @@ FULL = ["c2_pointwise", "c3a_3x3_s1", "c3b_3x3_s2", "f2_grouped_dgrad"]
 
 
 @pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled_images(name):
-    """The workload at its full size in the benchmark's launch configuration;
-    images 0, N/2 and N-1 are checked against the oracle run on that image."""
-    wl = synth.WORKLOADS[name]
-    p = wl["prob"]
-    ho, wo = oracle.out_dims(p)
-    (ab, af), (wb, wf) = synth.operands(wl["seed"], (p["n"], ho, wo, p["k"]),
-                                        (p["k"], p["r"], p["s"], p["c"] // p["groups"]),
-                                        p["dtype"], w_fan_in=wl["fan_in"])
-    got = from_device(run_gpu(p, "dgrad", ab, wb), p["dtype"])
-    one = dict(p, n=1)
-    for img in sorted({0, p["n"] // 2, p["n"] - 1}):
-        ref = oracle.conv_dgrad(af[img:img + 1], wf, one)
-        check_close(got[img:img + 1], ref, "%s image %d" % (name, img))
+def test_full_size_all_images(name):
+    """The workload at its full size in the benchmark's launch configuration,
+    every output element against the oracle."""
+    full_size_parity(name)

@@ -8,7 +8,7 @@ import pytest
 import oracle
 from convolution_nhwc_amd import api, synth
 
-from gpu_util import check_close, from_device, operands, parity, run_gpu
+from gpu_util import check_close, from_device, full_size_parity, operands, parity, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -86,12 +86,5 @@ def test_fwd_kernels_agree_on_exact_inputs(p):
 
 
 @pytest.mark.parametrize("name", ["f1_dwfwd3x3", "f1_dwfwd31x31"])
-def test_full_size_sampled_images(name):
-    wl = synth.WORKLOADS[name]
-    p = wl["prob"]
-    (ab, af), (wb, wf) = synth.operands(wl["seed"], (p["n"], p["h"], p["w"], p["c"]), (p["k"], p["r"], p["s"], 1),
-                                        p["dtype"], w_fan_in=wl["fan_in"])
-    got = from_device(run_gpu(p, "fwd", ab, wb), p["dtype"])
-    one = dict(p, n=1)
-    for img in sorted({0, p["n"] // 2, p["n"] - 1}):
-        check_close(got[img:img + 1], oracle.conv_fwd(af[img:img + 1], wf, one), "%s image %d" % (name, img))
+def test_full_size_all_images(name):
+    full_size_parity(name)

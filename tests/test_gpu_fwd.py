@@ -6,7 +6,7 @@ import pytest
 import oracle
 from convolution_nhwc_amd import api, synth
 
-from gpu_util import check_close, from_device, operands, parity, run_gpu
+from gpu_util import check_close, from_device, full_size_parity, operands, parity, run_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -124,13 +124,5 @@ def test_split_c_chunked_equals_unchunked():
 
 
 @pytest.mark.parametrize("name", ["c4a_splitc_fwd", "c4b_grouped_fwd"])
-def test_full_size_sampled_images(name):
-    wl = synth.WORKLOADS[name]
-    p = wl["prob"]
-    (ab, af), (wb, wf) = synth.operands(wl["seed"], (p["n"], p["h"], p["w"], p["c"]),
-                                        (p["k"], p["r"], p["s"], p["c"] // p["groups"]),
-                                        p["dtype"], w_fan_in=wl["fan_in"])
-    got = from_device(run_gpu(p, "fwd", ab, wb), p["dtype"])
-    one = dict(p, n=1)
-    for img in sorted({0, p["n"] // 2, p["n"] - 1}):
-        check_close(got[img:img + 1], oracle.conv_fwd(af[img:img + 1], wf, one), "%s image %d" % (name, img))
+def test_full_size_all_images(name):
+    full_size_parity(name)

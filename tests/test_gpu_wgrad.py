@@ -3,15 +3,14 @@
 Every case calls the C ABI on NaN-poisoned dw and a NaN-filled workspace and
 compares all K*R*S*Cg elements with oracle.conv_wgrad on the exact values of
 the same 16-bit inputs, to |gpu - ref| <= 1e-2 * (1 + |ref|).  The full-size
-workloads are checked on sampled output channels: dW[k] depends on dY[..., k]
-only, so the oracle runs on the sampled dY channels alone (groups = 1).
+workloads are checked the same way, every element, at their full size.
 """
 import numpy as np
 import pytest
 
 import oracle
 from convolution_nhwc_amd import api, synth
-from gpu_util import check_close, from_device, poisoned, to_device, torch
+from gpu_util import check_close, from_device, full_size_parity, run_wgrad
 
 pytestmark = pytest.mark.gpu
 
@@ -55,18 +54,6 @@ def operands(p, seed, exact=False):
     dist = ("ints", (-1.0, 0.0, 1.0)) if exact else ("uniform", -1.0, 1.0)
     return synth.wgrad_operands(seed, (p["n"], p["h"], p["w"], p["c"]), (p["n"], ho, wo, p["k"]),
                                 p["dtype"], dist)
-
-
-def run_wgrad(p, xb, yb):
-    t = torch()
-    x, dy = to_device(xb), to_device(yb)
-    dw = poisoned((p["k"], p["r"], p["s"], p["c"] // p["groups"]), p["dtype"])
-    need = api.cnhwc_workspace_size(p, api.OP_WGRAD)
-    ws = t.full((max(need, 16) // 4,), float("nan"), dtype=t.float32, device="cuda")
-    api.cnhwc_wgrad(p, x.data_ptr(), dy.data_ptr(), dw.data_ptr(), ws.data_ptr() if need else None,
-                    need, t.cuda.current_stream().cuda_stream)
-    t.cuda.synchronize()
-    return dw
 
 
 def parity(p, seed, exact=False, **ov):
@@ -154,15 +141,7 @@ def test_wgrad_is_deterministic():
 
 
 @pytest.mark.parametrize("name", ["f3_wgrad_pointwise", "f3_wgrad_3x3"])
-def test_wgrad_workload_full_size_sampled(name):
+def test_wgrad_workload_full_size(name):
     """The benchmarked workloads at full size, in the launch configuration the
-    benchmark times; the oracle checks 6 sampled output channels."""
-    wl = synth.WORKLOADS[name]
-    p = wl["prob"]
-    ho, wo = oracle.out_dims(p)
-    (xb, xf), (yb, yf) = synth.wgrad_operands(wl["seed"], (p["n"], p["h"], p["w"], p["c"]),
-                                              (p["n"], ho, wo, p["k"]), p["dtype"])
-    out = from_device(run_wgrad(p, xb, yb), p["dtype"])
-    ks = np.random.default_rng(111).choice(p["k"], 6, replace=False)
-    ref = oracle.conv_wgrad(xf, np.ascontiguousarray(yf[..., ks]), dict(p, k=len(ks)))
-    check_close(out[ks], ref, name)
+    benchmark times, every dW element against the oracle."""
+    full_size_parity(name)

@@ -203,6 +203,49 @@ def test_chunk_planner_default_is_one_chunk_for_every_workload():
         assert api.cnhwc_chunk_plan(w["prob"], OPC[w["op"]]) == [w["prob"]["n"]], name
 
 
+LARGE_BATCH = [("c5_dw3x3", api.VAR_DGRAD_DW_TILED), ("c5_dw7x7", api.VAR_DGRAD_DW_TILED),
+               ("c5_dw7x7_s2", api.VAR_DGRAD_DW_STREAM), ("c5_dw31x31", api.VAR_DGRAD_DW_ROTATED),
+               ("c5_dw51x5", api.VAR_DGRAD_DW_ROTATED), ("f1_dwfwd3x3", api.VAR_FWD_DW_TILED),
+               ("f1_dwfwd31x31", api.VAR_FWD_DW_ROTATED), ("c4a_splitc_fwd", api.VAR_FWD_DIRECT),
+               ("c4b_grouped_fwd", api.VAR_FWD_GROUPED), ("c3a_3x3_s1", api.VAR_DGRAD_IGEMM),
+               ("c2_pointwise", api.VAR_DGRAD_POINTWISE)]
+
+
+@pytest.mark.parametrize("name,var", LARGE_BATCH, ids=[n for n, _ in LARGE_BATCH])
+def test_large_batch_keeps_the_kernel_and_chunks(name, var):
+    """A batch past the 32-bit buffer range keeps the kernel its shape selects
+    (the split-C layer has enough output tiles at that batch to run unsplit)
+    and runs as balanced chunks: the per-kernel checks look at one image, the
+    batch is the chunk planner's ("feat(rocke): split-C and grouped LDS-halo
+    direct conv fwd kernels", supporting changes: balanced per-chunk launches)."""
+    w = wl(name)
+    p = dict(w["prob"])
+    ho, wo = oracle.out_dims(p)
+    per_image = max(p["h"] * p["w"] * p["c"], ho * wo * p["k"]) * 2
+    n_one = (2 ** 31 - 1) // per_image
+    p["n"] = 2 * n_one + 3
+    assert api.cnhwc_plan(p, OPC[w["op"]])[1] == var
+    counts = api.cnhwc_chunk_plan(p, OPC[w["op"]])
+    assert len(counts) == 3 and sum(counts) == p["n"] and max(counts) <= n_one
+    assert max(counts) - min(counts) <= 1
+
+
+def test_dw3x3_at_1024_images_is_two_chunks_of_512():
+    p = dict(wl("c5_dw3x3")["prob"], n=1024)
+    assert api.cnhwc_plan(p, api.OP_DGRAD)[1] == api.VAR_DGRAD_DW_TILED
+    assert api.cnhwc_chunk_plan(p, api.OP_DGRAD) == [512, 512]
+    f = dict(wl("f1_dwfwd3x3")["prob"], n=1024)
+    assert api.cnhwc_plan(f, api.OP_FWD)[1] == api.VAR_FWD_DW_TILED
+    assert api.cnhwc_chunk_plan(f, api.OP_FWD) == [512, 512]
+
+
+def test_override_cannot_raise_the_chunk_limit():
+    """A test limit above the 32-bit range is clamped to it."""
+    p = dict(wl("c5_dw3x3")["prob"], n=1024)
+    with api.override(chunk_limit_bytes=1 << 40):
+        assert api.cnhwc_chunk_plan(p, api.OP_DGRAD) == [512, 512]
+
+
 def test_chunk_planner_refuses_an_oversized_image():
     p = P(2, 8, 8, 16, 16, 3, 3, 1, 1, 1)
     with api.override(chunk_limit_bytes=1000):
