@@ -26,7 +26,9 @@ OP_FWD, OP_DGRAD, OP_WGRAD = 1, 2, 4
  VAR_WGRAD_GENERIC, VAR_WGRAD_POINTWISE, VAR_WGRAD_SPLITK, VAR_DGRAD_SPLITK, VAR_FWD_IGEMM) = range(19)
 
 SYMBOLS = ("cnhwc_out_dims", "cnhwc_workspace_size", "cnhwc_plan", "cnhwc_chunk_plan",
-           "cnhwc_fwd", "cnhwc_dgrad", "cnhwc_wgrad", "cnhwc_last_error", "cnhwc_set_override")
+           "cnhwc_fwd", "cnhwc_dgrad", "cnhwc_wgrad", "cnhwc_last_error", "cnhwc_set_override",
+           "cnhwc_fwd_static_ws")
+STATIC_WS_BYTES = 32 << 20   # CNHWC_STATIC_WS_BYTES
 
 
 class CnhwcError(RuntimeError):
@@ -77,6 +79,7 @@ def lib():
         L.cnhwc_fwd.argtypes = [P, vp, vp, vp, vp, sz, vp]
         L.cnhwc_dgrad.argtypes = [P, vp, vp, vp, vp, sz, vp]
         L.cnhwc_wgrad.argtypes = [P, vp, vp, vp, vp, sz, vp]
+        L.cnhwc_fwd_static_ws.argtypes = [P, vp, vp, vp, vp]
         L.cnhwc_last_error.argtypes = []
         L.cnhwc_last_error.restype = ctypes.c_char_p
         L.cnhwc_set_override.argtypes = [ctypes.POINTER(Override)]
@@ -135,6 +138,11 @@ def cnhwc_chunk_plan(p, op, cap=4096):
 def cnhwc_fwd(p, x, w, y, ws, ws_bytes, stream):
     """Raw entry point: pointers as ints (device addresses), stream as int."""
     _check(lib().cnhwc_fwd(ctypes.byref(_problem(p)), x, w, y, ws, ws_bytes, stream))
+
+
+def cnhwc_fwd_static_ws(p, x, w, y, stream):
+    """Forward pass with the library's static device workspace (no allocation)."""
+    _check(lib().cnhwc_fwd_static_ws(ctypes.byref(_problem(p)), x, w, y, stream))
 
 
 def cnhwc_dgrad(p, dy, w, dx, ws, ws_bytes, stream):

@@ -495,6 +495,9 @@ int run_wgrad(const cnhwc_problem* prob, const void* x, const void* dy, void* dw
 }
 
 }  // namespace
+
+int set_error(int status, const std::string& why) { return fail(status, why); }
+
 }  // namespace cnhwc
 
 using namespace cnhwc;

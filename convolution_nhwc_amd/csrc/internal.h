@@ -92,6 +92,9 @@ int launch_wgrad_generic(const Prob& p, const void* x, const void* dy, void* dw,
 int wgrad_splits(const Prob& p, int tune);
 int64_t wgrad_split_elems(const Prob& p);
 
+// Records `why` as this thread's cnhwc_last_error() reason and returns status.
+int set_error(int status, const std::string& why);
+
 // ---- per-variant acceptance (empty string = accepted, else the reason) ------
 std::string dgrad_igemm_reason(const Prob& p, bool pointwise);
 std::string dw_stream_reason(const Prob& p, int cpl);

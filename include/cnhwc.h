@@ -179,6 +179,24 @@ int cnhwc_dgrad(const cnhwc_problem* prob, const void* dy, const void* w, void* 
 int cnhwc_wgrad(const cnhwc_problem* prob, const void* x, const void* dy, void* dw,
                 void* ws, size_t ws_bytes, void* hip_stream);
 
+/* Forward pass for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation): the
+ * same dispatcher, kernels and results as cnhwc_fwd, with the workspace taken
+ * from a static device array of CNHWC_STATIC_WS_BYTES that the library's code
+ * object reserves on each GPU it runs on and keeps until the process ends.
+ * The caller still passes x, w and y as for cnhwc_fwd.  Problems whose
+ * workspace (cnhwc_workspace_size) exceeds CNHWC_STATIC_WS_BYTES are refused
+ * with CNHWC_WORKSPACE_TOO_SMALL before any device call.  The call itself
+ * allocates nothing (no hipMalloc / hipFree); its first call on a device looks
+ * up the array's address there.  Every call on one GPU shares that GPU's
+ * array and leaves its contents behind (nothing in it has to start at zero),
+ * so calls that may overlap on one GPU -- on different streams, or from
+ * different threads -- race on the workspace and must be ordered by the
+ * caller. */
+#define CNHWC_STATIC_WS_BYTES ((size_t)32 << 20)
+int cnhwc_fwd_static_ws(const cnhwc_problem* prob, const void* x, const void* w, void* y,
+                        void* hip_stream);
+
 /* Reason for the last non-zero status on this thread ("" after success).  The
  * checks run in a fixed order and the first failing one is reported, as the
  * pages' C++ engine keeps its validators in the same order and with the same

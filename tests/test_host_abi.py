@@ -454,3 +454,21 @@ def test_fwd_igemm_acceptance_and_workspace():
         with pytest.raises(api.CnhwcError) as e:   # the workspace is required
             api.cnhwc_fwd(p, 0x1000000, 0x4000000, 0x8000000, None, 0, None)
         assert e.value.status == api.INVALID_ARG
+
+
+def test_static_workspace_forward_refuses_before_any_device_call():
+    """cnhwc_fwd_static_ws checks the workspace against its static array
+    first: a split count whose partial sums exceed it is refused with the
+    reason, without touching a device (this runs on the CPU)."""
+    p = synth.WORKLOADS["c4a_splitc_fwd"]["prob"]
+    with api.override(variant=api.VAR_FWD_SPLITC, split_c=64):
+        assert api.cnhwc_workspace_size(p, api.OP_FWD) > api.STATIC_WS_BYTES
+        with pytest.raises(api.CnhwcError) as e:
+            api.cnhwc_fwd_static_ws(p, 16, 32, 48, None)
+    assert e.value.status == api.WORKSPACE_TOO_SMALL and "static workspace" in e.value.reason
+    # an invalid descriptor is refused by the shared validation
+    with pytest.raises(api.CnhwcError) as e:
+        api.cnhwc_fwd_static_ws(dict(p, groups=0), 16, 32, 48, None)
+    assert e.value.status == api.INVALID_ARG
+    # the default split of the workload fits the array
+    assert api.cnhwc_workspace_size(p, api.OP_FWD) <= api.STATIC_WS_BYTES
