@@ -10,12 +10,20 @@ those, each workload first runs back to back for 60 ms (settle_ms), since the
 GPU clock reaches its sustained value only after about 50 ms of load (a
 3x3 dgrad timed from idle reads ~8 % slow, a 7x7 depthwise one ~13 %).
 
+Every operand rotates (activations, filter, output, workspace).
+
 The JSON line also carries, per seeded workload of the method (forward, dgrad
-and weight-gradient shapes), the measured time and its fraction of the binding MI355X roof
-(HBM 8 TB/s, dense fp16/bf16 MFMA 2.5 PFLOP/s, fp32 vector 157.3 TFLOP/s), and
-the fp64 CPU oracle timed on a bounded sample of the headline workload.
+and weight-gradient shapes), the measured time and its fraction of the binding
+MI355X roof (HBM 8 TB/s, dense fp16/bf16 MFMA 2.5 PFLOP/s, fp32 vector
+157.3 TFLOP/s) and of the same roof as measured on this GPU by the ceiling
+microbenchmarks (libcnhwc_ceiling.so: HBM streams at the workload's
+read:write share, MFMA and dot2 issue at their best occupancy), the HBM bytes
+per launch from the committed rocprofv3 counter runs where the kernel source
+still matches them, and the fp64 CPU oracle on the headline workload (whole
+batch on every host thread, ~10 s of repeats; one thread on two images).
 
     python bench.py [--gpus 1] [--steps K] [--warmup W] [--only NAME] [--no-shapes]
+                    [--no-ceilings] [--ceilings-only] [--no-cpu-baseline]
 """
 import argparse
 import hashlib
@@ -44,7 +52,13 @@ def parse():
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--only", default=None, help="time one workload only (for profiling)")
     ap.add_argument("--no-shapes", action="store_true")
+    ap.add_argument("--settle-ms", type=float, default=60.0,
+                    help="back-to-back run before each workload's warm-up (GPU clock settling)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-ceilings", action="store_true",
+                    help="skip the measured machine ceilings (fractions against the spec peaks only)")
+    ap.add_argument("--ceilings-only", action="store_true",
+                    help="only measure and print the machine ceilings")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (scales the HBM byte counters)")
     ap.add_argument("--source-hash", nargs="+", metavar="FILE",
@@ -139,12 +153,12 @@ class Workload:
         self.opc = opc
         self.kernel, self.variant = api.cnhwc_plan(p, opc)
         self.ws_bytes = api.cnhwc_workspace_size(p, opc)
-        rot_b = self.op == "wgrad"
-        per_set = a0.numel() * 2 + (b0.numel() * 2 if rot_b else 0) + \
-            int(np.prod(out_shape)) * 2 + self.ws_bytes
+        # every operand rotates (activations, filter or second activation,
+        # output, workspace), so no step finds its inputs in the Infinity Cache
+        per_set = a0.numel() * 2 + b0.numel() * 2 + int(np.prod(out_shape)) * 2 + self.ws_bytes
         nsets = int(max(1, min(64, -(-ROTATE_BYTES // per_set))))
         self.acts = [a0] + [a0.clone() for _ in range(nsets - 1)]
-        self.bs = [b0] + [b0.clone() if rot_b else b0 for _ in range(nsets - 1)]
+        self.bs = [b0] + [b0.clone() for _ in range(nsets - 1)]
         self.outs = [torch.empty(out_shape, dtype=torch.int16, device=dev) for _ in range(nsets)]
         self.wss = [torch.empty(max(self.ws_bytes, 16), dtype=torch.uint8, device=dev)
                     for _ in range(nsets)]
@@ -165,10 +179,11 @@ class Workload:
 SETTLE_S = 0.06
 
 
-def settle(wk, seconds=SETTLE_S):
+def settle(wk, seconds=None):
     """Run steps back to back for `seconds` of host time so the GPU clock is
     at its sustained value before warm-up and timing."""
     import torch
+    seconds = SETTLE_S if seconds is None else seconds
     t0 = time.time()
     while time.time() - t0 < seconds:
         for _ in range(100):
@@ -191,8 +206,31 @@ def time_steps(wk, steps, warmup):
     return start.elapsed_time(end) / steps  # ms per step
 
 
+def cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def _time_runs(fn, budget_s, min_runs=3):
+    """Run fn repeatedly for about budget_s; per-run wall times."""
+    times, t_all = [], time.perf_counter()
+    while len(times) < min_runs or time.perf_counter() - t_all < budget_s:
+        t0 = time.perf_counter()
+        fn()
+        times.append(time.perf_counter() - t0)
+    return times
+
+
 def cpu_baseline():
-    """The fp64 oracle, untuned, on the headline workload, repeated for ~10 s."""
+    """The fp64 oracle, untuned, on the headline workload: the whole batch on
+    every host thread OpenMP gives it (about 10 s of repeats), then one thread
+    on a two-image sample (about 5 s), each reported as median and min."""
     import oracle
     from convolution_nhwc_amd import synth
     wl = synth.WORKLOADS[HEADLINE]
@@ -202,19 +240,188 @@ def cpu_baseline():
                                       (p["k"], p["r"], p["s"], p["c"]), p["dtype"],
                                       w_fan_in=wl["fan_in"])
     oracle.conv_dgrad(af[:1], wf, dict(p, n=1))  # load / warm
-    reps, t0 = 0, time.perf_counter()
-    while True:
-        oracle.conv_dgrad(af, wf, p)
-        reps += 1
-        el = time.perf_counter() - t0
-        if el > 10.0:
-            break
-    sec = el / reps
-    full = metrics(HEADLINE)
-    return {"value": round(full["bytes"] / sec / 1e9, 4), "unit": "GB/s", "cores": oracle.num_threads(),
+    full_bytes = metrics(HEADLINE)["bytes"]
+    threads = oracle.num_threads()
+    multi = sorted(_time_runs(lambda: oracle.conv_dgrad(af, wf, p), 10.0))
+    med = multi[len(multi) // 2]
+    one_n = 2
+    oracle.set_num_threads(1)
+    try:
+        single = sorted(_time_runs(lambda: oracle.conv_dgrad(af[:one_n], wf, dict(p, n=one_n)), 5.0))
+    finally:
+        oracle.set_num_threads(threads)
+    smed = single[len(single) // 2]
+    scale = one_n / p["n"]
+    return {"value": round(full_bytes / med / 1e9, 4), "unit": "GB/s", "cores": threads,
             "kind": "oracle",
-            "sample": "fp64 nested-loop oracle on the whole headline workload (32 images), "
-                      "%d runs in %.1f s, %.3f s per run" % (reps, el, sec)}
+            "sample": "fp64 nested-loop oracle on the whole headline workload (%d images), %d runs, "
+                      "median %.4f s, min %.4f s per run" % (p["n"], len(multi), med, multi[0]),
+            "median_s": round(med, 5), "min_s": round(multi[0], 5),
+            "best_GB/s": round(full_bytes / multi[0] / 1e9, 4),
+            "cpu_model": cpu_model(),
+            "single_thread": {"value": round(full_bytes * scale / smed / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "sample": "%d of the %d images, %d runs" % (one_n, p["n"], len(single)),
+                              "median_s": round(smed, 5), "min_s": round(single[0], 5)}}
+
+
+# ---- measured machine ceilings -------------------------------------------------
+
+CEILING_LIB = os.path.join(ROOT, "convolution_nhwc_amd", "libcnhwc_ceiling.so")
+
+
+def _ceiling_lib():
+    import ctypes
+    if not os.path.exists(CEILING_LIB):
+        raise RuntimeError("libcnhwc_ceiling.so is not built (%s); run "
+                           "`python -m convolution_nhwc_amd.build`" % CEILING_LIB)
+    L = ctypes.CDLL(CEILING_LIB)
+    vp = ctypes.c_void_p
+    L.ceiling_stream.argtypes = [ctypes.c_int, vp, vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int, vp, vp]
+    L.ceiling_mfma.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    L.ceiling_dot2.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    L.ceiling_lds.argtypes = [ctypes.c_int, ctypes.c_int, vp, vp]
+    L.ceiling_empty.argtypes = [ctypes.c_int, vp]
+    for f in (L.ceiling_stream, L.ceiling_mfma, L.ceiling_dot2, L.ceiling_lds, L.ceiling_empty):
+        f.restype = ctypes.c_int
+    return L
+
+
+def _event_time_ms(launch, reps, settle_s=None):
+    """Mean ms per launch over `reps` back-to-back launches, after the clock
+    has settled under the same load."""
+    import torch
+    settle_s = SETTLE_S if settle_s is None else settle_s
+    t0 = time.time()
+    while time.time() - t0 < settle_s:
+        for _ in range(10):
+            launch()
+        torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(reps):
+        launch()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def ceilings():
+    """What one MI355X delivers under the convolution kernels' kinds of load
+    (libcnhwc_ceiling.so): HBM streams with R reads to one write and a
+    read-only stream (best of three grid sizes), MFMA 16x16x32 f16 and dot2
+    issue at 1, 2 and 4 waves per SIMD, LDS read bandwidth at 1, 2 and 4
+    blocks of 4 waves a CU, and the back-to-back cost of an empty launch."""
+    import torch
+    L = _ceiling_lib()
+    st = torch.cuda.current_stream().cuda_stream
+    sink = torch.zeros(16, dtype=torch.float32, device="cuda")
+    out = {}
+    chunk = 512 << 20
+    bufs = [torch.empty(chunk, dtype=torch.uint8, device="cuda") for _ in range(5)]
+    for b in bufs:
+        b.fill_(1)
+    n16 = chunk // 16
+    ptr = [b.data_ptr() for b in bufs]
+    stream = {}
+    for reads in (0, 1, 2, 3, 4):
+        if reads == 0:
+            # read-only: the first four chunks' worth as one 2 GiB stream
+            big = torch.empty(4 * chunk, dtype=torch.uint8, device="cuda")
+            big.fill_(1)
+            nb, args, moved = 4 * n16, (big.data_ptr(), 0, 0, 0, 0), 4 * chunk
+        else:
+            big = None
+            nb, args, moved = n16, tuple(ptr[:reads]) + (0,) * (4 - reads) + (ptr[4],), (reads + 1) * chunk
+        best = 0.0
+        for blocks in (1024, 2048, 4096):
+            def launch(a=args, nb=nb, blocks=blocks, reads=reads):
+                rc = L.ceiling_stream(reads, *a, nb, blocks, sink.data_ptr(), st)
+                if rc:
+                    raise RuntimeError("ceiling_stream failed: %d" % rc)
+            ms = _event_time_ms(launch, 10)
+            best = max(best, moved / (ms * 1e-3) / 1e9)
+        del big
+        stream[reads] = round(best, 1)
+    out["hbm_GBs"] = {"read_only": stream[0], "1r:1w": stream[1], "2r:1w": stream[2],
+                      "3r:1w": stream[3], "4r:1w": stream[4]}
+    del bufs
+    torch.cuda.empty_cache()
+    mf = {}
+    iters = 2000
+    for wps in (1, 2, 4):
+        blocks = 256 * wps
+        ms = _event_time_ms(lambda: L.ceiling_mfma(blocks, iters, sink.data_ptr(), st), 5)
+        mf["%d_wave_per_simd" % wps] = round(blocks * 4 * iters * 8 * 16384 / (ms * 1e-3) / 1e12, 1)
+    out["mfma_f16_TFLOPs"] = mf
+    d2 = {}
+    for wps in (1, 2, 4, 8):
+        blocks = 256 * wps
+        ms = _event_time_ms(lambda: L.ceiling_dot2(blocks, iters, sink.data_ptr(), st), 5)
+        d2["%d_wave_per_simd" % wps] = round(blocks * 256 * iters * 8 * 4 / (ms * 1e-3) / 1e12, 1)
+    out["dot2_TFLOPs"] = d2
+    lds = {}
+    for bpc in (1, 2, 4):
+        blocks = 256 * bpc
+        ms = _event_time_ms(lambda: L.ceiling_lds(blocks, iters, sink.data_ptr(), st), 5)
+        gbs = blocks * 256 * iters * 8 * 16 / (ms * 1e-3) / 1e9
+        lds["%d_block_per_cu" % bpc] = {"GB/s_per_CU": round(gbs / 256, 1),
+                                         "B/clk_per_CU_at_2.4GHz": round(gbs / 256 / 2.4, 1)}
+    out["lds_read"] = lds
+    em = {}
+    for blocks in (256, 1024):
+        ms = _event_time_ms(lambda: L.ceiling_empty(blocks, st), 200)
+        em["%d_blocks" % blocks] = round(ms * 1e3, 3)
+    out["empty_launch_us"] = em
+    return out
+
+
+def hbm_ceiling_for(name, ceil):
+    """Measured HBM ceiling at a workload's read share: piecewise linear in
+    the read fraction between the measured streams (1:1, 2:1, 3:1, 4:1 reads
+    to writes and read-only)."""
+    from convolution_nhwc_amd import synth
+    wl = synth.WORKLOADS[name]
+    p = wl["prob"]
+    ho = (p["h"] + 2 * p["pad_h"] - p["r"]) // p["stride"] + 1
+    wo = (p["w"] + 2 * p["pad_w"] - p["s"]) // p["stride"] + 1
+    act = p["n"] * p["h"] * p["w"] * p["c"] * 2
+    res = p["n"] * ho * wo * p["k"] * 2
+    wb = p["k"] * p["r"] * p["s"] * (p["c"] // p["groups"]) * 2
+    written = {"fwd": res, "dgrad": act, "wgrad": wb}[wl["op"]]
+    f = 1.0 - written / float(act + res + wb)
+    pts = [(0.5, ceil["1r:1w"]), (2 / 3, ceil["2r:1w"]), (0.75, ceil["3r:1w"]), (0.8, ceil["4r:1w"]),
+           (1.0, ceil["read_only"])]
+    if f <= pts[0][0]:
+        return pts[0][1]
+    for (f0, v0), (f1, v1) in zip(pts, pts[1:]):
+        if f <= f1:
+            return v0 + (v1 - v0) * (f - f0) / (f1 - f0)
+    return pts[-1][1]
+
+
+def measured_ceiling(name, mm, ceil):
+    """The measured ceiling of a workload's binding roof: HBM GB/s at its read
+    share, or the best MFMA / dot2 TFLOP/s over the waves-per-SIMD counts."""
+    if ceil is None:
+        return None
+    if mm["bound"] == "hbm":
+        return round(hbm_ceiling_for(name, ceil["hbm_GBs"]), 1)
+    if mm["bound"] == "mfma":
+        return max(ceil["mfma_f16_TFLOPs"].values())
+    return max(ceil["dot2_TFLOPs"].values())
+
+
+def frac_of_ceiling(name, mm, t_s, ceil):
+    """Achieved rate over the measured ceiling of the workload's binding roof
+    (bytes for HBM, nominal flops for MFMA, valid flops for the vector ALUs)."""
+    c = measured_ceiling(name, mm, ceil)
+    if c is None:
+        return None
+    if mm["bound"] == "hbm":
+        return round(mm["bytes"] / t_s / 1e9 / c, 4)
+    if mm["bound"] == "mfma":
+        return round(mm["nominal_flops"] / t_s / 1e12 / c, 4)
+    return round(mm["valid_flops"] / t_s / 1e12 / c, 4)
 
 
 def cpl_matrix(args):
@@ -262,6 +469,8 @@ def main():
     if args.source_hash:
         print(source_hash(args.source_hash))
         return
+    global SETTLE_S
+    SETTLE_S = args.settle_ms / 1000.0
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
               "(each image is independent; see the design notes on sharding over N).",
@@ -274,8 +483,14 @@ def main():
     if args.copy_calibration:
         copy_calibration()
         return
+    if args.ceilings_only:
+        print(json.dumps({"ceilings": ceilings()}), flush=True)
+        return
     from convolution_nhwc_amd import api, synth
     api.lib()
+    ceil = None if (args.no_ceilings or args.only) else ceilings()
+    if ceil is not None:
+        print("# ceilings %s" % json.dumps(ceil), file=sys.stderr, flush=True)
 
     names = [args.only] if args.only else [HEADLINE]
     head = Workload(names[0])
@@ -295,10 +510,13 @@ def main():
                 "unit": "TFLOP/s", "frac": round(vt / VALU_PEAK_TFLOPS, 4)}
     roof["traffic"] = recorded_traffic(head.name)
     roof["algorithmic_bytes"] = int(m["bytes"])
+    if ceil is not None:
+        roof["frac_of_measured_ceiling"] = frac_of_ceiling(head.name, m, ms * 1e-3, ceil)
+        roof["measured_ceiling"] = measured_ceiling(head.name, m, ceil)
     line = {
         "metric": "effective conv TFLOP/s and HBM GB/s per shape, % of MI355X roofline",
         "value": round(gbs, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "settle_ms": int(SETTLE_S * 1000), "ms_per_step": round(ms, 5), "higher_is_better": True,
+        "warmup": args.warmup, "settle_ms": round(SETTLE_S * 1000, 1), "ms_per_step": round(ms, 5), "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": head.p["dtype"], "data": "synthetic",
         "config": {"workload": head.name, "op": head.op, "kernel": head.kernel,
                    **{k: head.p[k] for k in ("n", "h", "w", "c", "k", "r", "s", "stride",
@@ -306,6 +524,8 @@ def main():
         "effective_tflops": round(tflops, 3),
         "roofline": roof,
     }
+    if ceil is not None:
+        line["ceilings"] = ceil
     del head
     torch.cuda.empty_cache()
     if not args.no_shapes and not args.only:
@@ -327,6 +547,8 @@ def main():
                     ent["frac_of_peak"] = round(mm["nominal_flops"] / (t * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)
                 else:
                     ent["frac_of_peak"] = round(mm["valid_flops"] / (t * 1e-3) / 1e12 / VALU_PEAK_TFLOPS, 4)
+                ent["frac_of_measured_ceiling"] = frac_of_ceiling(name, mm, t * 1e-3, ceil)
+                ent["traffic"] = recorded_traffic(name)
                 del wk
                 torch.cuda.empty_cache()
             except Exception as e:  # a workload whose kernel is not available yet

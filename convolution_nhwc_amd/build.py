@@ -1,4 +1,5 @@
-"""Build libcnhwc.so (gfx950) in-tree from csrc/ with hipcc.
+"""Build libcnhwc.so (gfx950) in-tree from csrc/ with hipcc, and the benchmark's
+machine-ceiling microbenchmarks (ceiling/ceiling.hip) into libcnhwc_ceiling.so.
 
 Every translation unit is compiled with packed-fp32 instruction selection
 disabled (-Xclang -target-feature -Xclang -packed-fp32-ops) and a per-kernel
@@ -17,6 +18,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libcnhwc.so")
+CEILING_SRC = os.path.join(HERE, "ceiling", "ceiling.hip")
+CEILING_LIB = os.path.join(HERE, "libcnhwc_ceiling.so")
 ARCH = "gfx950"
 
 FLAGS = ["--offload-arch=" + ARCH, "-O3", "-std=c++17", "-fPIC", "-Wall",
@@ -74,7 +77,19 @@ def build(jobs=None, verbose=False, allow_scratch=False):
     if res.returncode != 0:
         raise RuntimeError("link failed:\n" + res.stdout + res.stderr)
     os.replace(tmp, LIB)
+    build_ceiling()
     return LIB
+
+
+def build_ceiling():
+    """The machine-ceiling microbenchmarks the benchmark reports against."""
+    tmp = CEILING_LIB + ".tmp%d" % os.getpid()
+    cmd = [_hipcc()] + FLAGS + ["-shared", CEILING_SRC, "-o", tmp]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("hipcc failed for %s:\n%s" % (CEILING_SRC, res.stdout + res.stderr))
+    os.replace(tmp, CEILING_LIB)
+    return CEILING_LIB
 
 
 if __name__ == "__main__":

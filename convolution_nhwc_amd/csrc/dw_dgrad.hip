@@ -510,7 +510,8 @@ __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const T
 constexpr int kRotCB = 8;      // channels per block
 constexpr int kRotTHT = 2;     // output rows per lane
 constexpr int kRotTWT = 8;     // output columns per lane
-constexpr int kRotTB = 8;      // filter columns per register slice
+constexpr int kRotTB = 8;      // filter columns per register slice (wide filters)
+constexpr int kRotPadCols = 8; // window columns between LDS pad words
 constexpr int kRotMaxF = 64;   // largest filter side
 constexpr int kRotSplit = 2;   // lane groups splitting the filter steps of a tile
 
@@ -530,8 +531,10 @@ struct RotArgs {
 };
 
 // Block: 256 lanes = 4 channel pairs x 4 column groups (8 columns) x 16 row
-// groups (2 rows): a 32 x 32 x 8 output tile.
-template <typename T, int SPLIT>
+// groups (2 rows): a 32 x 32 x 8 output tile.  TB: filter columns per
+// register slice -- 8 for filters wider than 7 columns, else the filter
+// width itself (one slice, no zero columns multiplied).
+template <typename T, int SPLIT, int TB>
 __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArgs a) {
     extern __shared__ __attribute__((aligned(16))) uint32_t smem[];
     constexpr int NT = 256 * SPLIT;
@@ -556,38 +559,58 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     // columns and a row stride of a.row_dw words (= 8 mod 32): the 64 lanes of
     // a read (4 channel pairs x 4 column groups 8 columns apart x 4 row groups
     // 2 rows apart) then fall on 32 distinct banks, two lanes each
+    // Every lane issues a batch of its loads before writing any of them to
+    // LDS, so the batch's memory latencies overlap instead of adding up.
     uint32_t* win = smem;
     const int npix = a.IHB * a.IWB;
-    for (int q = tid; q < npix; q += NT) {
-        const int ih = q / a.IWB, iw = q - (q / a.IWB) * a.IWB;
-        const int u = h0 - a.ph2 + ih, v = w0 - a.pw2 + iw;
-        uint32_t off = kOob;
-        if (u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
-            off = uint32_t(((n * a.Ho + u) * a.Wo + v) * a.C + c0) * 2u;
-        const i32x4 val = buf_load16(rdy, off);
-        *reinterpret_cast<i32x4*>(win + ih * a.row_dw + iw * 4 + (iw >> 3) * 4) = val;
+    constexpr int kWinBatch = 8;
+    for (int q0 = tid; q0 < npix; q0 += kWinBatch * NT) {
+        i32x4 val[kWinBatch];
+#pragma unroll
+        for (int b = 0; b < kWinBatch; ++b) {
+            const int q = q0 + b * NT;
+            const int ih = q / a.IWB, iw = q - ih * a.IWB;
+            const int u = h0 - a.ph2 + ih, v = w0 - a.pw2 + iw;
+            uint32_t off = kOob;
+            if (q < npix && u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
+                off = uint32_t(((n * a.Ho + u) * a.Wo + v) * a.C + c0) * 2u;
+            val[b] = buf_load16(rdy, off);
+        }
+#pragma unroll
+        for (int b = 0; b < kWinBatch; ++b) {
+            const int q = q0 + b * NT;
+            const int ih = q / a.IWB, iw = q - ih * a.IWB;
+            if (q < npix) *reinterpret_cast<i32x4*>(win + ih * a.row_dw + iw * 4 + (iw / kRotPadCols) * 4) = val[b];
+        }
     }
     // ---- stage rotated weight pairs: [rp][t][8 channels] words ----
     uint32_t* wpl = smem + a.IHB * a.row_dw;
-    const int tpad = a.tslices * kRotTB;
+    const int tpad = a.tslices * TB;
     const int nwp = a.rpairs * tpad * kRotCB;
-    for (int q = tid; q < nwp; q += NT) {
-        const int ch = q % kRotCB;
-        const int t = (q / kRotCB) % tpad;
-        const int rp = q / (kRotCB * tpad);
-        uint32_t v = 0;
-        if (t < a.S) {
+    constexpr int kWBatch = 8;
+    for (int q0 = tid; q0 < nwp; q0 += kWBatch * NT) {
+        uint32_t lo[kWBatch], hi[kWBatch];
+#pragma unroll
+        for (int b = 0; b < kWBatch; ++b) {
+            const int q = q0 + b * NT;
+            const int ch = q % kRotCB;
+            const int t = (q / kRotCB) % tpad;
+            const int rp = q / (kRotCB * tpad);
             const int r0 = 2 * rp, r1 = 2 * rp + 1;   // rotated rows
             const uint32_t base = uint32_t(c0 + ch) * (a.R * a.S);
-            auto tap = [&](int r) {
+            auto tap_off = [&](int r) {
+                if (q >= nwp || t >= a.S || r >= a.R) return kOob;
                 const uint32_t e = a.rot ? (a.R - 1 - r) * a.S + (a.S - 1 - t) : r * a.S + t;
-                return uint32_t(buf_load2(rw, (base + e) * 2u));
+                return (base + e) * 2u;
             };
-            const uint32_t lo = r0 < a.R ? tap(r0) : 0u;
-            const uint32_t hi = r1 < a.R ? tap(r1) : 0u;
-            v = lo | (hi << 16);
+            lo[b] = buf_load2(rw, tap_off(r0));
+            hi[b] = buf_load2(rw, tap_off(r1));
         }
-        wpl[q] = v;
+#pragma unroll
+        for (int b = 0; b < kWBatch; ++b) {
+            const int q = q0 + b * NT;
+            if (q < nwp) wpl[q] = lo[b] | (hi[b] << 16);
+        }
     }
     __syncthreads();
 
@@ -611,18 +634,19 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     int ts_lo = 0, ts_hi = a.tslices;
     {
         const int base = w0 - a.pw2;
-        while (ts_lo < ts_hi && base + a.OWB - 1 + (ts_lo + 1) * kRotTB - 1 < 0) ++ts_lo;
-        while (ts_hi > ts_lo && base + (ts_hi - 1) * kRotTB >= a.Wo) --ts_hi;
+        while (ts_lo < ts_hi && base + a.OWB - 1 + (ts_lo + 1) * TB - 1 < 0) ++ts_lo;
+        while (ts_hi > ts_lo && base + (ts_hi - 1) * TB >= a.Wo) --ts_hi;
     }
     const int orow = rg * kRotTHT, ocol = cg * kRotTWT;
     // The (row pair, column slice) steps are software-pipelined: the LDS reads
     // of the next step (3 window rows x 15 columns -- the middle row serves
     // both output rows -- and 8 weight pairs) are issued before the dot2s of
     // the current one, so one wave per SIMD keeps its VALU busy.
-    constexpr int NV = kRotTWT + kRotTB - 1;
+    constexpr int NV = kRotTWT + TB - 1;
+    static_assert(TB == kRotTB || TB < kRotPadCols, "a narrow slice is the only one: it starts on a pad group");
     struct Frag {
         uint32_t x[kRotTHT + 1][NV];
-        uint32_t w0[kRotTB], w1[kRotTB];
+        uint32_t w0[TB], w1[TB];
     };
     // SPLIT groups of 256 lanes compute the same outputs over disjoint runs
     // of the flattened (row pair, column slice) steps; their fp32 sums are
@@ -633,15 +657,15 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     int lrp = rp_lo + (nts > 0 ? it_lo / nts : 0), lts = ts_lo + (nts > 0 ? it_lo % nts : 0);   // load cursor
     auto load = [&](Frag& f) {
 #pragma unroll
-        for (int t = 0; t < kRotTB; ++t) {
+        for (int t = 0; t < TB; ++t) {
             const i32x2 v = *reinterpret_cast<const i32x2*>(
-                wpl + (lrp * tpad + lts * kRotTB + t) * kRotCB + cp * 2);
+                wpl + (lrp * tpad + lts * TB + t) * kRotCB + cp * 2);
             f.w0[t] = uint32_t(v[0]);
             f.w1[t] = uint32_t(v[1]);
         }
         // the slice starts on an 8-column boundary, so column vl of it carries
         // (vl >> 3) more pad words than the first
-        const int iw0 = ocol + lts * kRotTB;
+        const int iw0 = ocol + lts * TB;
         const uint32_t* r0 = win + (orow + 2 * lrp) * a.row_dw + iw0 * 4 + (iw0 >> 3) * 4 + cp;
 #pragma unroll
         for (int i = 0; i <= kRotTHT; ++i)
@@ -662,7 +686,7 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
                 p1[vl] = pair_hi(f.x[i][vl], f.x[i + 1][vl]);   // channel 2cp+1
             }
 #pragma unroll
-            for (int t = 0; t < kRotTB; ++t)
+            for (int t = 0; t < TB; ++t)
 #pragma unroll
                 for (int j = 0; j < kRotTWT; ++j) {
                     acc[i][j][0] = dot2<T>(p0[j + t], f.w0[t], acc[i][j][0]);
@@ -723,19 +747,23 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     }
 }
 
-bool rot_geometry(const Prob& p, RotArgs* a, size_t* lds) {
+// Filter columns per register slice: the filter width itself up to 7 (one
+// slice, no zero columns), else 8-column slices.
+int rot_tb(const Prob& p) { return p.s < kRotTB ? int(p.s) : kRotTB; }
+
+bool rot_geometry(const Prob& p, int tb, RotArgs* a, size_t* lds) {
     a->OHB = int(std::min<int64_t>(32, p.h));
     a->OWB = int(std::min<int64_t>(32, p.w));
     a->rpairs = int((p.r + 1) / 2);
-    a->tslices = int((p.s + kRotTB - 1) / kRotTB);
+    a->tslices = int((p.s + tb - 1) / tb);
     // rows: tile rows + 2*rpairs (pairs reach row i + 2rp + 1); columns: tile + padded slices
     a->IHB = 32 + 2 * a->rpairs;
-    a->IWB = 32 + a->tslices * kRotTB;
+    a->IWB = 32 + a->tslices * tb;
     // 4 words a column, 4 pad words after every 8 columns, stride = 8 mod 32
-    const int base = a->IWB * 4 + (a->IWB / kRotTB) * 4;
+    const int base = a->IWB * 4 + (a->IWB / kRotPadCols) * 4;
     a->row_dw = base + ((8 - base % 32) + 32) % 32;
     const size_t win = size_t(a->IHB) * a->row_dw * 4;
-    const size_t wts = size_t(a->rpairs) * a->tslices * kRotTB * kRotCB * 4;
+    const size_t wts = size_t(a->rpairs) * a->tslices * tb * kRotCB * 4;
     // the tap groups' partial sums reuse the window's LDS at the end
     const size_t parts = size_t(kRotSplit - 1) * 256 * kRotTHT * kRotTWT * 2 * 4;
     *lds = std::max(win + wts, parts);
@@ -790,7 +818,7 @@ std::string dw_rotated_reason(const Prob& p) {
     if (p.c % kRotCB != 0) return "the rotated-filter dgrad needs C a multiple of 8";
     RotArgs a{};
     size_t lds;
-    if (!rot_geometry(p, &a, &lds)) return "staged dY window exceeds LDS";
+    if (!rot_geometry(p, kRotTB, &a, &lds)) return "staged dY window exceeds LDS";
     if (p.h * p.w * p.c > (int64_t(1) << 30) || p.ho * p.wo * p.k > (int64_t(1) << 30))
         return "one image exceeds the 32-bit element range";
     return "";
@@ -867,13 +895,33 @@ int launch_tiled(const Prob& p, int flip, const void* dy, const void* w, void* d
                                  : launch_tile_t<F16>(p, a, int(blocks), st);
 }
 
+template <typename T, int SPLIT, int TB>
+int launch_rot_inst(const RotArgs& a, int64_t blocks, size_t lds, hipStream_t st) {
+    auto kern = dw_rotated_kernel<T, SPLIT, TB>;
+    // dynamic LDS above 64 KiB must be opted into per kernel
+    static bool attr_set = false;   // per instance; idempotent if raced
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                160 * 1024) != hipSuccess)
+            return CNHWC_HIP_ERROR;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(unsigned(blocks)), dim3(256 * SPLIT), lds, st, a);
+    return CNHWC_OK;
+}
+
 // p in dgrad terms; rot: correlate with the filter rotated by 180 degrees at
 // padding R-1-pad (dgrad), else with the filter as stored at padding R-1-pad
 int launch_rotated(const Prob& p, const Plan& pl, int rot, const void* dy, const void* w, void* dx,
                    hipStream_t st) {
+    // tap groups: kRotSplit (two waves per SIMD at one block per CU); tune 1
+    // asks for one group, tune 2 for two groups with 8-column slices whatever
+    // the filter width (both with 8-column slices)
+    const bool split = pl.tune != 1;
+    const int tb = pl.tune == 1 || pl.tune == 2 ? kRotTB : rot_tb(p);
     RotArgs a{};
     size_t lds;
-    if (!rot_geometry(p, &a, &lds)) return CNHWC_UNSUPPORTED;
+    if (!rot_geometry(p, tb, &a, &lds)) return CNHWC_UNSUPPORTED;
     a.rot = rot;
     a.dy = dy; a.w = w; a.dx = dx;
     a.dy_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
@@ -887,29 +935,22 @@ int launch_rotated(const Prob& p, const Plan& pl, int rot, const void* dy, const
     a.tiles_w = int((p.w + a.OWB - 1) / a.OWB);
     a.cblocks = int(p.c / kRotCB);
     const int64_t blocks = int64_t(a.N) * a.tiles_h * a.tiles_w * a.cblocks;
-    // tap groups: kRotSplit (two waves per SIMD at one block per CU); tune 1
-    // asks for one group
-    const bool split = pl.tune != 1;
-    if (!split) lds = size_t(a.IHB) * a.row_dw * 4 + size_t(a.rpairs) * a.tslices * kRotTB * kRotCB * 4;
-    // dynamic LDS above 64 KiB must be opted into per kernel
-    static bool attr_set[4] = {false, false, false, false};
-    const int which = (p.dtype == CNHWC_BF16 ? 1 : 0) + (split ? 2 : 0);
-    const void* fns[4] = {reinterpret_cast<const void*>(&dw_rotated_kernel<F16, 1>),
-                          reinterpret_cast<const void*>(&dw_rotated_kernel<BF16, 1>),
-                          reinterpret_cast<const void*>(&dw_rotated_kernel<F16, kRotSplit>),
-                          reinterpret_cast<const void*>(&dw_rotated_kernel<BF16, kRotSplit>)};
-    if (!attr_set[which]) {
-        if (hipFuncSetAttribute(fns[which], hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024) != hipSuccess)
-            return CNHWC_HIP_ERROR;
-        attr_set[which] = true;
+    if (!split) lds = size_t(a.IHB) * a.row_dw * 4 + size_t(a.rpairs) * a.tslices * tb * kRotCB * 4;
+    const bool bf = p.dtype == CNHWC_BF16;
+    if (!split)
+        return bf ? launch_rot_inst<BF16, 1, kRotTB>(a, blocks, lds, st)
+                  : launch_rot_inst<F16, 1, kRotTB>(a, blocks, lds, st);
+    switch (tb) {
+    case 1: return bf ? launch_rot_inst<BF16, kRotSplit, 1>(a, blocks, lds, st) : launch_rot_inst<F16, kRotSplit, 1>(a, blocks, lds, st);
+    case 2: return bf ? launch_rot_inst<BF16, kRotSplit, 2>(a, blocks, lds, st) : launch_rot_inst<F16, kRotSplit, 2>(a, blocks, lds, st);
+    case 3: return bf ? launch_rot_inst<BF16, kRotSplit, 3>(a, blocks, lds, st) : launch_rot_inst<F16, kRotSplit, 3>(a, blocks, lds, st);
+    case 4: return bf ? launch_rot_inst<BF16, kRotSplit, 4>(a, blocks, lds, st) : launch_rot_inst<F16, kRotSplit, 4>(a, blocks, lds, st);
+    case 5: return bf ? launch_rot_inst<BF16, kRotSplit, 5>(a, blocks, lds, st) : launch_rot_inst<F16, kRotSplit, 5>(a, blocks, lds, st);
+    case 6: return bf ? launch_rot_inst<BF16, kRotSplit, 6>(a, blocks, lds, st) : launch_rot_inst<F16, kRotSplit, 6>(a, blocks, lds, st);
+    case 7: return bf ? launch_rot_inst<BF16, kRotSplit, 7>(a, blocks, lds, st) : launch_rot_inst<F16, kRotSplit, 7>(a, blocks, lds, st);
+    default: return bf ? launch_rot_inst<BF16, kRotSplit, kRotTB>(a, blocks, lds, st)
+                       : launch_rot_inst<F16, kRotSplit, kRotTB>(a, blocks, lds, st);
     }
-    switch (which) {
-    case 0: hipLaunchKernelGGL((dw_rotated_kernel<F16, 1>), dim3(blocks), dim3(256), lds, st, a); break;
-    case 1: hipLaunchKernelGGL((dw_rotated_kernel<BF16, 1>), dim3(blocks), dim3(256), lds, st, a); break;
-    case 2: hipLaunchKernelGGL((dw_rotated_kernel<F16, kRotSplit>), dim3(blocks), dim3(256 * kRotSplit), lds, st, a); break;
-    default: hipLaunchKernelGGL((dw_rotated_kernel<BF16, kRotSplit>), dim3(blocks), dim3(256 * kRotSplit), lds, st, a); break;
-    }
-    return CNHWC_OK;
 }
 
 }  // namespace

@@ -222,7 +222,9 @@ const char* cnhwc_last_error(void);
  * the dY-window kernel, a value of 16 or more sets the ring kernel's pixels per
  * tile; direct forward: 1 forces the register-staged kernel, 2 the input-window
  * kernel; split-K wgrad: the number of pixel splits per batch chunk;
- * depthwise rotated-filter: 1 runs one tap group; other kernels ignore it);
+ * depthwise rotated-filter: 1 runs one tap group, 2 two groups, both with
+ * 8-column filter slices even for filters narrower than 8 columns; other
+ * kernels ignore it);
  * chunk_limit_bytes: the per-view byte limit of the chunk planner.  Pass NULL
  * to clear. */
 typedef struct cnhwc_override {

@@ -57,14 +57,23 @@ ROT = [
     DW(1, 9, 11, 8, 17, 15, 1, 8, 7),          # filter larger than the image
     DW(1, 33, 30, 16, 31, 31, 1, 15, 15, dtype="bf16"),
     DW(1, 24, 24, 8, 51, 5, 1, 25, 2, dtype="bf16"),
+    # filters narrower than 8 columns: one slice of exactly S columns
+    DW(1, 30, 26, 8, 15, 1, 1, 7, 0),
+    DW(1, 25, 27, 16, 13, 2, 1, 6, 1),
+    DW(1, 40, 37, 8, 21, 3, 1, 10, 1),
+    DW(1, 33, 35, 8, 12, 4, 1, 5, 2),          # even filter rows
+    DW(2, 28, 30, 16, 9, 6, 1, 4, 3, dtype="bf16"),
+    DW(1, 36, 34, 8, 19, 7, 1, 9, 3),
 ]
 
 
-@pytest.mark.parametrize("tune", [0, 1], ids=["split", "onegroup"])
+@pytest.mark.parametrize("tune", [0, 1, 2], ids=["split", "onegroup", "wideslice"])
 @pytest.mark.parametrize("p", ROT, ids=ident)
 def test_rotated_parity(p, tune):
     """The rotated-filter kernel with its filter steps split over two lane
-    groups (default) and with one group (tune 1)."""
+    groups (default), with one group (tune 1), and with 8-column filter
+    slices for every width (tune 2; by default a filter narrower than 8
+    columns is one slice of its own width)."""
     with api.override(variant=api.VAR_DGRAD_DW_ROTATED, tune=tune):
         parity(p, "dgrad", 302)
 

@@ -63,7 +63,7 @@ def test_fwd_tiled_7x7_several_channel_blocks():
         parity(p, "fwd", 402)
 
 
-@pytest.mark.parametrize("tune", [0, 1], ids=["split", "onegroup"])
+@pytest.mark.parametrize("tune", [0, 1, 2], ids=["split", "onegroup", "wideslice"])
 @pytest.mark.parametrize("p", ROT, ids=ident)
 def test_fwd_rotated_parity(p, tune):
     with api.override(variant=api.VAR_FWD_DW_ROTATED, tune=tune):
