@@ -321,15 +321,16 @@ __global__ __launch_bounds__(256) void split_reduce_kernel(const float* __restri
     for (int64_t i = int64_t(blockIdx.x) * blockDim.x + threadIdx.x; i < total4;
          i += int64_t(gridDim.x) * blockDim.x) {
         f32x4 s = reinterpret_cast<const f32x4*>(ws)[i];
-        // eight splits' loads are in flight at once; the adds stay in
-        // ascending split order
-        for (int sp0 = 1; sp0 < splits; sp0 += 8) {
-            f32x4 v[8];
+        // sixteen splits' loads are in flight at once (one memory round trip
+        // for up to 17 splits); the adds stay in ascending split order
+        constexpr int kBatch = 16;
+        for (int sp0 = 1; sp0 < splits; sp0 += kBatch) {
+            f32x4 v[kBatch];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < kBatch; ++j)
                 if (sp0 + j < splits) v[j] = reinterpret_cast<const f32x4*>(ws)[i + (sp0 + j) * stride4];
 #pragma unroll
-            for (int j = 0; j < 8; ++j)
+            for (int j = 0; j < kBatch; ++j)
                 if (sp0 + j < splits) {
                     s[0] += v[j][0]; s[1] += v[j][1]; s[2] += v[j][2]; s[3] += v[j][3];
                 }
@@ -848,7 +849,15 @@ int64_t fwd_direct_tiles(const Prob& p) {
 // count within the CU count and at least 128 channels per split.
 int fwd_direct_auto_split(const Prob& p) {
     if (p.groups != 1) return 1;
-    if (fwd_window_reason(p, 1).empty()) return fwd_window_auto_split(p);
+    if (fwd_window_reason(p, 1).empty()) {
+        const int win = fwd_window_auto_split(p);
+        // a split is wanted: small maps take the filter-streaming kernel and its split count
+        if (win > 1) {
+            const int sp = fwd_stream_splits(p);
+            if (sp > 1 && fwd_stream_reason(p, sp).empty()) return sp;
+        }
+        return win;
+    }
     const int64_t tiles = fwd_direct_tiles(p);
     if (tiles <= 0 || tiles >= kNumCUs / 2) return 1;
     // two blocks fit a CU (LDS), so aim for up to 2 * CUs blocks
@@ -876,14 +885,23 @@ int launch_split_reduce(const Prob& p, int splits, const void* ws, void* y, hipS
     return CNHWC_OK;
 }
 
-// Direct forward (split or not): the window kernel when it accepts the
-// problem, else the register-staged kernel above.  (tune: 1 forces the
-// register-staged kernel, 2 the window kernel.)
+// Direct forward (split or not): the filter-streaming kernel for split-C over
+// a small map, the window kernel when it accepts the problem, else the
+// register-staged kernel above.  (tune: 1 forces the register-staged kernel,
+// 2 or 3 the window kernel.)
+bool fwd_stream_taken(const Prob& p, const Plan& pl) {
+    return pl.variant == CNHWC_VAR_FWD_SPLITC && pl.split_c > 1 && pl.tune != 1 && pl.tune != 2 &&
+           pl.tune != 3 && fwd_stream_reason(p, pl.split_c).empty();
+}
+
 int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                       void* ws, hipStream_t st) {
+    // split-C over a small map: the filter-streaming kernel (tune 3 keeps the
+    // input-window kernel)
+    if (fwd_stream_taken(p, pl)) return launch_fwd_stream(p, pl, x, w, y, ws, st);
     if (pl.tune != 1 && fwd_window_reason(p, pl.split_c).empty())
         return launch_fwd_window(p, pl, x, w, y, ws, st);
-    if (pl.tune == 2) return CNHWC_UNSUPPORTED;
+    if (pl.tune == 2 || pl.tune == 3) return CNHWC_UNSUPPORTED;
     FwdArgs a{};
     const bool split = pl.variant == CNHWC_VAR_FWD_SPLITC && pl.split_c > 1;
     if (!pick_geo(p, kHaloMax, &a.geo)) return CNHWC_UNSUPPORTED;

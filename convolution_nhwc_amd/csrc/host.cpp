@@ -150,7 +150,11 @@ std::string plan_name(const Prob& p, const Plan& pl) {
     case CNHWC_VAR_FWD_DIRECT:
         std::snprintf(buf, sizeof buf, "fwd_direct_%s", dt(p)); break;
     case CNHWC_VAR_FWD_SPLITC:
-        std::snprintf(buf, sizeof buf, "fwd_direct_splitc%d_%s+split_reduce", pl.split_c, dt(p)); break;
+        if (fwd_stream_taken(p, pl))
+            std::snprintf(buf, sizeof buf, "fwd_stream_splitc%d_%s+split_reduce", pl.split_c, dt(p));
+        else
+            std::snprintf(buf, sizeof buf, "fwd_direct_splitc%d_%s+split_reduce", pl.split_c, dt(p));
+        break;
     case CNHWC_VAR_FWD_GROUPED:
         std::snprintf(buf, sizeof buf, "fwd_grouped_merge_%s", dt(p)); break;
     case CNHWC_VAR_FWD_IGEMM:
@@ -193,8 +197,8 @@ int choose(const Prob& p, int op, Plan* out) {
         std::string why = variant_reason(p, op, pl.variant, pl.cpl, pl.split_c);
         if (!why.empty()) return fail(CNHWC_UNSUPPORTED, why);
         if (pl.variant != CNHWC_VAR_FWD_SPLITC && pl.variant != CNHWC_VAR_DGRAD_SPLITK) pl.split_c = 1;
-        pl.name = plan_name(p, pl);
         pl.tune = ov.tune;
+        pl.name = plan_name(p, pl);
         *out = pl;
         return CNHWC_OK;
     }
@@ -262,8 +266,8 @@ int choose(const Prob& p, int op, Plan* out) {
         if (!ok) ok = take(CNHWC_VAR_FWD_GENERIC, 0, 1);
     }
     if (!ok) return fail(CNHWC_UNSUPPORTED, "no kernel accepts the problem: " + tried);
-    pl.name = plan_name(p, pl);
     pl.tune = ov.tune;
+    pl.name = plan_name(p, pl);
     *out = pl;
     return CNHWC_OK;
 }

@@ -65,6 +65,15 @@ int launch_fwd_direct(const Prob& p, const Plan& pl, const void* x, const void* 
                       void* ws, hipStream_t st);
 int launch_fwd_window(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                       void* ws, hipStream_t st);
+// Split-C forward for small output maps (N*Ho*Wo <= 448) that streams the
+// filter once: its split count (0 if it does not apply), acceptance and launch
+// (main pass + the split reduce).
+int fwd_stream_splits(const Prob& p);
+std::string fwd_stream_reason(const Prob& p, int splits);
+int launch_fwd_stream(const Prob& p, const Plan& pl, const void* x, const void* w, void* y, void* ws,
+                      hipStream_t st);
+// Whether the split-C forward of this plan runs on the filter-streaming kernel.
+bool fwd_stream_taken(const Prob& p, const Plan& pl);
 // Second pass of split-C: y = round(sum over splits of ws[split]), ascending.
 int launch_split_reduce(const Prob& p, int splits, const void* ws, void* y, hipStream_t st);
 int launch_fwd_grouped(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,

@@ -61,6 +61,62 @@ def test_split_c_parity(p, split, tune):
         parity(p, "fwd", 202)
 
 
+STREAM = [
+    P(2, 7, 7, 512, 128, 3, 3, 1, 1, 1),
+    P(3, 5, 6, 256, 96, 3, 3, 1, 1, 1, dtype="f16"),    # 90 pixels: ragged last tile, K % 64 != 0
+    P(2, 14, 14, 256, 64, 3, 3, 2, 1, 1, dtype="f16"),  # stride 2: 15 x 15 windows, one image a group
+    P(4, 7, 7, 512, 64, 1, 1),                          # 1x1
+    P(2, 9, 9, 256, 32, 3, 3, 1, 0, 0, dtype="f16"),    # no padding, one k tile
+    P(1, 8, 6, 256, 32, 3, 3, 1, 1, 0),                 # per-axis padding
+    P(6, 7, 7, 1024, 32, 3, 3, 1, 1, 1),                # 294 pixels: two groups of 3 images
+    P(8, 7, 7, 256, 64, 3, 3, 1, 1, 1),                 # 392 pixels: two groups of 4 images
+]
+
+
+@pytest.mark.parametrize("p", STREAM, ids=ident)
+def test_filter_streaming_split_c_parity(p):
+    """Split-C over a small map on the filter-streaming kernel (the automatic
+    choice for these shapes), every element against the oracle."""
+    name, var = api.cnhwc_plan(p, api.OP_FWD)
+    assert var == api.VAR_FWD_SPLITC and name.startswith("fwd_stream_"), name
+    parity(p, "fwd", 204)
+
+
+@pytest.mark.parametrize("split", [2, 4, 8, 16])
+def test_filter_streaming_forced_splits(split):
+    p = P(2, 7, 7, 1024, 64, 3, 3, 1, 1, 1)
+    with api.override(variant=api.VAR_FWD_SPLITC, split_c=split):
+        assert api.cnhwc_plan(p, api.OP_FWD)[0].startswith("fwd_stream_splitc%d" % split)
+        parity(p, "fwd", 205)
+
+
+@pytest.mark.parametrize("p", STREAM[:3], ids=ident)
+def test_filter_streaming_matches_window_kernel_on_exact_inputs(p):
+    """Inputs in {-1, 0, 1}: exact partial sums, so the filter-streaming kernel
+    and the input-window kernel (tune 3) agree bit for bit."""
+    ab, _, wb, _ = operands(p, "fwd", 206, exact=True)
+    stream = run_gpu(p, "fwd", ab, wb).cpu().numpy()
+    with api.override(tune=3):
+        assert api.cnhwc_plan(p, api.OP_FWD)[0].startswith("fwd_direct_")
+        window = run_gpu(p, "fwd", ab, wb).cpu().numpy()
+    assert np.array_equal(stream, window)
+    parity(p, "fwd", 206, exact=True)
+
+
+def test_filter_streaming_reproducible_and_chunked():
+    p = P(5, 7, 7, 512, 64, 3, 3, 1, 1, 1)
+    ab, _, wb, _ = operands(p, "fwd", 207)
+    a = run_gpu(p, "fwd", ab, wb).cpu().numpy()
+    b = run_gpu(p, "fwd", ab, wb).cpu().numpy()
+    assert np.array_equal(a, b)
+    split = int(api.cnhwc_plan(p, api.OP_FWD)[0].split("splitc")[1].split("_")[0])
+    ws_img = split * 7 * 7 * 64 * 4
+    with api.override(chunk_limit_bytes=2 * ws_img):
+        assert api.cnhwc_chunk_plan(p, api.OP_FWD) == [2, 2, 1]
+        c = run_gpu(p, "fwd", ab, wb).cpu().numpy()
+    assert np.array_equal(a, c)
+
+
 def test_split_c_reproducible_and_close_to_unsplit():
     p = P(2, 7, 7, 512, 64, 3, 3, 1, 1, 1)
     ab, af, wb, wf = operands(p, "fwd", 203)
