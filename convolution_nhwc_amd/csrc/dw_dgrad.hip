@@ -308,6 +308,7 @@ struct TileArgs {
     int tiles_h, tiles_w, cblocks;
     int nblocks, remap;
     int flip;          // 1: use the filter rotated by 180 degrees (depthwise forward)
+    FastDiv fd_tw, fd_th, fd_cb;   // division by tiles_w, tiles_h, cblocks
 };
 
 template <int R, int S>
@@ -382,16 +383,19 @@ __device__ __forceinline__ void tile_store(const TileArgs& a, __amdgpu_buffer_rs
                                            const float (&acc)[THL][kTileTWL][2], int n, int h0, int w0,
                                            int c) {
     if (c >= a.C) return;
+    // offsets step by a pixel (2C bytes) along the row and by a row (2WC)
+    const uint32_t pix = uint32_t(a.C) * 2u, row = uint32_t(a.W) * pix;
+    uint32_t off0 = uint32_t(((n * a.H + h0) * a.W + w0) * a.C + c) * 2u;
 #pragma unroll
     for (int hl = 0; hl < THL; ++hl) {
-        const int h = h0 + hl;
+        uint32_t off = off0;
 #pragma unroll
         for (int wl = 0; wl < kTileTWL; ++wl) {
-            const int w = w0 + wl;
-            if (h < a.H && w < a.W)
-                buf_store4(int(pack2<T>(acc[hl][wl][0], acc[hl][wl][1])), rdx,
-                           uint32_t(((n * a.H + h) * a.W + w) * a.C + c) * 2u);
+            if (h0 + hl < a.H && w0 + wl < a.W)
+                buf_store4(int(pack2<T>(acc[hl][wl][0], acc[hl][wl][1])), rdx, off);
+            off += pix;
         }
+        off0 += row;
     }
 }
 
@@ -400,7 +404,6 @@ __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const T
     using G = TileGeo<R, S>;
     constexpr int NL = G::NL, WC = G::WC, NPIX = G::NPIX;
     constexpr int kTileTHL = G::THL, kTileTH = G::TH;
-    constexpr int LOADS = (NPIX + 31) / 32;                   // 8-pixel loads per wave
     __shared__ __attribute__((aligned(16))) unsigned char lds[G::LDS];
     const unsigned short* const raw = reinterpret_cast<const unsigned short*>(lds + G::WIN_BYTES);
 
@@ -411,12 +414,8 @@ __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const T
     // neighbouring tiles, which share halo rows, meet in the same L2.
     int bid = blockIdx.x;
     if (a.remap) bid = (bid & 7) * (a.nblocks >> 3) + (bid >> 3);
-    const int tw_i = bid % a.tiles_w;
-    bid /= a.tiles_w;
-    const int th_i = bid % a.tiles_h;
-    bid /= a.tiles_h;
-    const int cb = bid % a.cblocks;
-    const int n = bid / a.cblocks;
+    const int b1 = fdiv(bid, a.fd_tw), b2 = fdiv(b1, a.fd_th), n = fdiv(b2, a.fd_cb);
+    const int tw_i = bid - b1 * a.tiles_w, th_i = b1 - b2 * a.tiles_h, cb = b2 - n * a.cblocks;
     const int h0 = th_i * kTileTH, w0 = tw_i * kTileTW, c0 = cb * kTileCB;
 
     const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
@@ -424,20 +423,27 @@ __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const T
     const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
 
     // ---- window: pixel q = (row, col) holds dY(h0 + pad_h - (R-1) + row, w0 + pad_w - (S-1) + col) ----
+    // One load instruction stages 8 consecutive pixels of one window row
+    // (8 lanes a pixel, 16 bytes each): its row and column group are uniform,
+    // so only the lane's column and the range checks are per-lane work.  Lanes
+    // past the row's end load nothing (their LDS slots are the next row's).
     {
-        const int chunk = lane & 7;
+        constexpr int CG = (WC + 7) / 8;                      // column groups a row
+        constexpr int NLD = G::WR * CG;                       // load instructions a block
+        const int chunk = lane & 7, lpx = lane >> 3;
         const bool cin = c0 + chunk * 8 < a.C;
+        const int u0 = h0 + a.pad_h - (R - 1), v0 = w0 + a.pad_w - (S - 1);
+        const int pix_b = a.C * 2;
+        const int lane_off = lpx * pix_b + (c0 + chunk * 8) * 2;
 #pragma unroll
-        for (int i = 0; i < LOADS; ++i) {
-            const int q0 = (wave + 4 * i) * 8;
-            if (q0 < NPIX) {
-                const int q = q0 + (lane >> 3);
-                const int row = q / WC, col = q - (q / WC) * WC;
-                const int u = h0 + a.pad_h - (R - 1) + row, v = w0 + a.pad_w - (S - 1) + col;
-                uint32_t off = kOob;
-                if (cin && q < NPIX && u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
-                    off = uint32_t((((n * a.Ho + u) * a.Wo + v) * a.C + c0 + chunk * 8) * 2);
-                dma16(rdy, lds + q0 * 128, off, 0);
+        for (int i = 0; i < (NLD + 3) / 4; ++i) {
+            const int j = wave + 4 * i;
+            if (j < NLD) {
+                const int r = j / CG, g = j - (j / CG) * CG;
+                const int u = u0 + r, col = 8 * g + lpx, v = v0 + col;
+                const bool ok = cin && unsigned(u) < unsigned(a.Ho) && unsigned(v) < unsigned(a.Wo);
+                const int off = ((n * a.Ho + u) * a.Wo + v0 + 8 * g) * pix_b + lane_off;
+                if (col < WC) dma16(rdy, lds + (r * WC + 8 * g) * 128, ok ? uint32_t(off) : kOob, 0);
             }
         }
     }
@@ -459,21 +465,22 @@ __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const T
     // its words, then all write them), then each lane keeps its two channels'
     // words in registers.  The rotated filter of the depthwise forward reads
     // (R-1-r, S-1-t). ----
+    // Word e = (i * S + t) * 64 + ch; a thread's words are e = tid + 256 k, so
+    // its channel is tid % 64 and (i, t) depend on the wave and k only.
     constexpr int WTS = NL * S * kTileCB;
     constexpr int WPT = (WTS + 255) / 256;                    // words per thread
     static_assert(WTS * 4 <= G::RAW_BYTES, "weight pairs fit over the staged filter");
+    static_assert(256 % kTileCB == 0, "a thread keeps one channel");
+    const unsigned short* const wch = raw + (tid % kTileCB) * R * S;
     uint32_t word[WPT];
 #pragma unroll
     for (int k = 0; k < WPT; ++k) {
-        const int e = tid + k * 256;
+        const int it = wave + (256 / kTileCB) * k;            // i * S + t
         word[k] = 0u;
-        if (e < WTS) {
-            const int ch = e % kTileCB;
-            const int t = (e / kTileCB) % S;
-            const int i = e / (kTileCB * S);
+        if (it < NL * S) {
+            const int i = it / S, t = it - (it / S) * S;
             auto tap = [&](int r) {
-                return a.flip ? uint32_t(raw[ch * R * S + (R - 1 - r) * S + (S - 1 - t)])
-                              : uint32_t(raw[ch * R * S + r * S + t]);
+                return a.flip ? uint32_t(wch[(R - 1 - r) * S + (S - 1 - t)]) : uint32_t(wch[r * S + t]);
             };
             const uint32_t lo = tap(2 * i);
             const uint32_t hi = 2 * i + 1 < R ? tap(2 * i + 1) : 0u;
@@ -483,10 +490,8 @@ __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const T
     __syncthreads();
     uint32_t* const wts = reinterpret_cast<uint32_t*>(lds + G::WIN_BYTES);
 #pragma unroll
-    for (int k = 0; k < WPT; ++k) {
-        const int e = tid + k * 256;
-        if (e < WTS) wts[e] = word[k];
-    }
+    for (int k = 0; k < WPT; ++k)
+        if (wave + (256 / kTileCB) * k < NL * S) wts[tid + 256 * k] = word[k];
     __syncthreads();
 
     uint32_t wp[NL][S][2];
@@ -891,6 +896,9 @@ int launch_tiled(const Prob& p, int flip, const void* dy, const void* w, void* d
     const int64_t blocks = int64_t(a.N) * a.tiles_h * a.tiles_w * a.cblocks;
     a.nblocks = int(blocks);
     a.remap = blocks % 8 == 0 ? 1 : 0;
+    a.fd_tw = make_fastdiv(uint32_t(a.tiles_w));
+    a.fd_th = make_fastdiv(uint32_t(a.tiles_h));
+    a.fd_cb = make_fastdiv(uint32_t(a.cblocks));
     return p.dtype == CNHWC_BF16 ? launch_tile_t<BF16>(p, a, int(blocks), st)
                                  : launch_tile_t<F16>(p, a, int(blocks), st);
 }
