@@ -19,10 +19,14 @@
 //    a plain correlation with the reversed filter whose zero border is
 //    R-1-pad_h rows and S-1-pad_w columns.  A block
 //    owns a tile of dX rows x columns x 8 channels; the dY window of the tile
-//    and the rotated filter are staged in LDS, and each lane accumulates 2 rows
-//    x 8 columns x 2 channels, walking the filter one row pair and 8 columns at
-//    a time so only that slice of the filter sits in registers.  Filter rows
-//    whose dY rows are all padding for a wave's rows are skipped.
+//    is staged in LDS as row-pair words (dY[2m][v], dY[2m+1][v]) of one
+//    channel, and each lane accumulates 2 rows (an even and an odd one) x 8
+//    columns x 2 channels: the even row takes the pair with the filter rows
+//    (2k, 2k+1), the odd row the same pair with (2k-1, 2k), so one read pair
+//    feeds both rows and no pair is built in the inner loop.  The filter is
+//    walked one row pair and 8 columns at a time so only that slice of it sits
+//    in registers.  Row pairs whose dY rows are all padding for a wave's rows
+//    are skipped.
 //
 // Arithmetic: pairs of taps along the filter's rows go through one
 // v_dot2_f32_{f16,bf16} (two products of the 16-bit inputs added to an fp32
@@ -529,10 +533,10 @@ struct RotArgs {
     int ph2, pw2;          // padding of the correlation (dgrad: R-1-pad_h, S-1-pad_w)
     int rot;               // 1: correlate with the filter rotated by 180 degrees (dgrad)
     int OHB, OWB;          // output tile of a block
-    int IHB, IWB;          // staged dY window (rows padded to pairs, columns to slices)
-    int rpairs, tslices;   // ceil(R/2), ceil(S/8)
+    int IHB, IWB;          // staged dY window (rows: 2 x pair rows; columns padded to slices)
+    int rpairs, tslices;   // R/2 + 1 filter row pairs, ceil(S/TB) column slices
     int tiles_h, tiles_w, cblocks;
-    int row_dw;            // LDS row stride in 32-bit words
+    int row_dw;            // LDS words of one pair row
 };
 
 // Block: 256 lanes = 4 channel pairs x 4 column groups (8 columns) x 16 row
@@ -559,62 +563,80 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
     const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
 
-    // ---- stage the dY window: rows h0 - ph2 .., columns w0 - pw2 .., 8 channels ----
-    // word layout: [row][col][4 channel pairs] with 4 pad words after every 8
-    // columns and a row stride of a.row_dw words (= 8 mod 32): the 64 lanes of
-    // a read (4 channel pairs x 4 column groups 8 columns apart x 4 row groups
-    // 2 rows apart) then fall on 32 distinct banks, two lanes each
-    // Every lane issues a batch of its loads before writing any of them to
-    // LDS, so the batch's memory latencies overlap instead of adding up.
+    // ---- stage the dY window as row-pair words: pair row m, column v holds
+    // for each of the 8 channels (dY(h0 - ph2 + 2m, w0 - pw2 + v), the row
+    // below) in one word.  Layout [m][v][8 channels] with 8 pad words after
+    // every 8 columns and a pair-row stride of a.row_dw words (= 32 mod 64):
+    // a 64-bit read of 32 lanes (4 channel pairs x 4 column groups 8 columns
+    // apart x 2 row groups one pair row apart) then covers the 64 banks once.
+    // Every lane issues a batch of its loads before writing any of them.
     uint32_t* win = smem;
-    const int npix = a.IHB * a.IWB;
-    constexpr int kWinBatch = 8;
-    for (int q0 = tid; q0 < npix; q0 += kWinBatch * NT) {
-        i32x4 val[kWinBatch];
+    const int npp = (a.IHB / 2) * a.IWB;
+    constexpr int kWinBatch = 4;
+    for (int q0 = tid; q0 < npp; q0 += kWinBatch * NT) {
+        i32x4 top[kWinBatch], bot[kWinBatch];
 #pragma unroll
         for (int b = 0; b < kWinBatch; ++b) {
             const int q = q0 + b * NT;
-            const int ih = q / a.IWB, iw = q - ih * a.IWB;
-            const int u = h0 - a.ph2 + ih, v = w0 - a.pw2 + iw;
-            uint32_t off = kOob;
-            if (q < npix && u >= 0 && u < a.Ho && v >= 0 && v < a.Wo)
-                off = uint32_t(((n * a.Ho + u) * a.Wo + v) * a.C + c0) * 2u;
-            val[b] = buf_load16(rdy, off);
+            const int m = q / a.IWB, iw = q - m * a.IWB;
+            const int u = h0 - a.ph2 + 2 * m, v = w0 - a.pw2 + iw;
+            const bool vin = q < npp && v >= 0 && v < a.Wo;
+            const uint32_t off = uint32_t(((n * a.Ho + u) * a.Wo + v) * a.C + c0) * 2u;
+            top[b] = buf_load16(rdy, vin && u >= 0 && u < a.Ho ? off : kOob);
+            bot[b] = buf_load16(rdy, vin && u + 1 >= 0 && u + 1 < a.Ho ? off + uint32_t(a.Wo * a.C * 2) : kOob);
         }
 #pragma unroll
         for (int b = 0; b < kWinBatch; ++b) {
             const int q = q0 + b * NT;
-            const int ih = q / a.IWB, iw = q - ih * a.IWB;
-            if (q < npix) *reinterpret_cast<i32x4*>(win + ih * a.row_dw + iw * 4 + (iw / kRotPadCols) * 4) = val[b];
+            const int m = q / a.IWB, iw = q - m * a.IWB;
+            if (q < npp) {
+                i32x4 lo, hi;
+#pragma unroll
+                for (int j = 0; j < 2; ++j) {
+                    lo[2 * j] = int(pair_lo(uint32_t(top[b][j]), uint32_t(bot[b][j])));
+                    lo[2 * j + 1] = int(pair_hi(uint32_t(top[b][j]), uint32_t(bot[b][j])));
+                    hi[2 * j] = int(pair_lo(uint32_t(top[b][j + 2]), uint32_t(bot[b][j + 2])));
+                    hi[2 * j + 1] = int(pair_hi(uint32_t(top[b][j + 2]), uint32_t(bot[b][j + 2])));
+                }
+                i32x4* dst = reinterpret_cast<i32x4*>(win + m * a.row_dw + iw * 8 + (iw / kRotPadCols) * 8);
+                dst[0] = lo;
+                dst[1] = hi;
+            }
         }
     }
-    // ---- stage rotated weight pairs: [rp][t][8 channels] words ----
-    uint32_t* wpl = smem + a.IHB * a.row_dw;
+    // ---- stage the filter pair words: even set [k][t][8 channels] =
+    // (W'(2k, t), W'(2k+1, t)), odd set = (W'(2k-1, t), W'(2k, t)), with W'
+    // the correlation's filter (rotated for the dgrad), zero outside it ----
+    uint32_t* wpe = smem + (a.IHB / 2) * a.row_dw;
     const int tpad = a.tslices * TB;
     const int nwp = a.rpairs * tpad * kRotCB;
+    uint32_t* wpo = wpe + nwp;
     constexpr int kWBatch = 8;
     for (int q0 = tid; q0 < nwp; q0 += kWBatch * NT) {
-        uint32_t lo[kWBatch], hi[kWBatch];
+        uint32_t t0[kWBatch], t1[kWBatch], t2[kWBatch];   // rows 2k-1, 2k, 2k+1
 #pragma unroll
         for (int b = 0; b < kWBatch; ++b) {
             const int q = q0 + b * NT;
             const int ch = q % kRotCB;
             const int t = (q / kRotCB) % tpad;
-            const int rp = q / (kRotCB * tpad);
-            const int r0 = 2 * rp, r1 = 2 * rp + 1;   // rotated rows
+            const int k = q / (kRotCB * tpad);
             const uint32_t base = uint32_t(c0 + ch) * (a.R * a.S);
             auto tap_off = [&](int r) {
-                if (q >= nwp || t >= a.S || r >= a.R) return kOob;
+                if (q >= nwp || t >= a.S || r < 0 || r >= a.R) return kOob;
                 const uint32_t e = a.rot ? (a.R - 1 - r) * a.S + (a.S - 1 - t) : r * a.S + t;
                 return (base + e) * 2u;
             };
-            lo[b] = buf_load2(rw, tap_off(r0));
-            hi[b] = buf_load2(rw, tap_off(r1));
+            t0[b] = buf_load2(rw, tap_off(2 * k - 1));
+            t1[b] = buf_load2(rw, tap_off(2 * k));
+            t2[b] = buf_load2(rw, tap_off(2 * k + 1));
         }
 #pragma unroll
         for (int b = 0; b < kWBatch; ++b) {
             const int q = q0 + b * NT;
-            if (q < nwp) wpl[q] = lo[b] | (hi[b] << 16);
+            if (q < nwp) {
+                wpe[q] = t1[b] | (t2[b] << 16);
+                wpo[q] = t0[b] | (t1[b] << 16);
+            }
         }
     }
     __syncthreads();
@@ -625,15 +647,14 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
 #pragma unroll
         for (int j = 0; j < kRotTWT; ++j) acc[i][j][0] = acc[i][j][1] = 0.f;
 
-    // rows of this wave: 4 row groups x 2 rows; skip row pairs that only meet padding
+    // rows of this wave: 4 row groups x 2 rows; pair k reads dY rows
+    // base + 2k .. base + 2k + 7 over the wave: skip the pairs that only
+    // meet padding
     const int wave_row0 = (rg & ~3) * kRotTHT;     // first tile row of the wave
-    const int wave_rows = 4 * kRotTHT;
     int rp_lo = 0, rp_hi = a.rpairs;
     {
-        // dY row of (tile row i, rotated row r) is h0 - ph2 + i + r; need some in [0, Ho)
         const int base = h0 + wave_row0 - a.ph2;
-        // largest r with base + wave_rows - 1 + r < 0 -> all below
-        while (rp_lo < rp_hi && base + wave_rows - 1 + 2 * rp_lo + 1 < 0) ++rp_lo;
+        while (rp_lo < rp_hi && base + 2 * rp_lo + 7 < 0) ++rp_lo;
         while (rp_hi > rp_lo && base + 2 * (rp_hi - 1) >= a.Ho) --rp_hi;
     }
     int ts_lo = 0, ts_hi = a.tslices;
@@ -644,14 +665,13 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     }
     const int orow = rg * kRotTHT, ocol = cg * kRotTWT;
     // The (row pair, column slice) steps are software-pipelined: the LDS reads
-    // of the next step (3 window rows x 15 columns -- the middle row serves
-    // both output rows -- and 8 weight pairs) are issued before the dot2s of
-    // the current one, so one wave per SIMD keeps its VALU busy.
+    // of the next step (one pair row x 15 columns, 8 even and 8 odd filter
+    // pair words) are issued before the dot2s of the current one.
     constexpr int NV = kRotTWT + TB - 1;
     static_assert(TB == kRotTB || TB < kRotPadCols, "a narrow slice is the only one: it starts on a pad group");
     struct Frag {
-        uint32_t x[kRotTHT + 1][NV];
-        uint32_t w0[TB], w1[TB];
+        uint32_t x[NV][2];
+        uint32_t we[TB][2], wo[TB][2];
     };
     // SPLIT groups of 256 lanes compute the same outputs over disjoint runs
     // of the flattened (row pair, column slice) steps; their fp32 sums are
@@ -663,19 +683,24 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     auto load = [&](Frag& f) {
 #pragma unroll
         for (int t = 0; t < TB; ++t) {
-            const i32x2 v = *reinterpret_cast<const i32x2*>(
-                wpl + (lrp * tpad + lts * TB + t) * kRotCB + cp * 2);
-            f.w0[t] = uint32_t(v[0]);
-            f.w1[t] = uint32_t(v[1]);
+            const int wi = (lrp * tpad + lts * TB + t) * kRotCB + cp * 2;
+            const i32x2 ve = *reinterpret_cast<const i32x2*>(wpe + wi);
+            const i32x2 vo = *reinterpret_cast<const i32x2*>(wpo + wi);
+            f.we[t][0] = uint32_t(ve[0]);
+            f.we[t][1] = uint32_t(ve[1]);
+            f.wo[t][0] = uint32_t(vo[0]);
+            f.wo[t][1] = uint32_t(vo[1]);
         }
         // the slice starts on an 8-column boundary, so column vl of it carries
-        // (vl >> 3) more pad words than the first
+        // (vl >> 3) more pad groups than the first
         const int iw0 = ocol + lts * TB;
-        const uint32_t* r0 = win + (orow + 2 * lrp) * a.row_dw + iw0 * 4 + (iw0 >> 3) * 4 + cp;
+        const uint32_t* r0 = win + (rg + lrp) * a.row_dw + iw0 * 8 + (iw0 >> 3) * 8 + cp * 2;
 #pragma unroll
-        for (int i = 0; i <= kRotTHT; ++i)
-#pragma unroll
-            for (int vl = 0; vl < NV; ++vl) f.x[i][vl] = r0[i * a.row_dw + vl * 4 + (vl >> 3) * 4];
+        for (int vl = 0; vl < NV; ++vl) {
+            const i32x2 v = *reinterpret_cast<const i32x2*>(r0 + vl * 8 + (vl >> 3) * 8);
+            f.x[vl][0] = uint32_t(v[0]);
+            f.x[vl][1] = uint32_t(v[1]);
+        }
         ++lts;
         const bool wrap = lts >= ts_hi;
         lts = wrap ? ts_lo : lts;
@@ -683,21 +708,14 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     };
     auto compute = [&](const Frag& f) {
 #pragma unroll
-        for (int i = 0; i < kRotTHT; ++i) {
-            uint32_t p0[NV], p1[NV];
+        for (int t = 0; t < TB; ++t)
 #pragma unroll
-            for (int vl = 0; vl < NV; ++vl) {
-                p0[vl] = pair_lo(f.x[i][vl], f.x[i + 1][vl]);   // channel 2cp: (row u, row u+1)
-                p1[vl] = pair_hi(f.x[i][vl], f.x[i + 1][vl]);   // channel 2cp+1
-            }
+            for (int j = 0; j < kRotTWT; ++j)
 #pragma unroll
-            for (int t = 0; t < TB; ++t)
-#pragma unroll
-                for (int j = 0; j < kRotTWT; ++j) {
-                    acc[i][j][0] = dot2<T>(p0[j + t], f.w0[t], acc[i][j][0]);
-                    acc[i][j][1] = dot2<T>(p1[j + t], f.w1[t], acc[i][j][1]);
+                for (int c = 0; c < 2; ++c) {
+                    acc[0][j][c] = dot2<T>(f.x[j + t][c], f.we[t][c], acc[0][j][c]);
+                    acc[1][j][c] = dot2<T>(f.x[j + t][c], f.wo[t][c], acc[1][j][c]);
                 }
-        }
     };
     Frag fa, fb;
     if (it_lo < it_hi) load(fa);
@@ -759,16 +777,17 @@ int rot_tb(const Prob& p) { return p.s < kRotTB ? int(p.s) : kRotTB; }
 bool rot_geometry(const Prob& p, int tb, RotArgs* a, size_t* lds) {
     a->OHB = int(std::min<int64_t>(32, p.h));
     a->OWB = int(std::min<int64_t>(32, p.w));
-    a->rpairs = int((p.r + 1) / 2);
+    a->rpairs = int(p.r / 2 + 1);   // even rows use taps 2k, 2k+1; odd rows 2k-1, 2k
     a->tslices = int((p.s + tb - 1) / tb);
-    // rows: tile rows + 2*rpairs (pairs reach row i + 2rp + 1); columns: tile + padded slices
+    // rows: tile rows + 2*rpairs (pair k of row group g is pair row g + k);
+    // columns: tile + padded slices
     a->IHB = 32 + 2 * a->rpairs;
     a->IWB = 32 + a->tslices * tb;
-    // 4 words a column, 4 pad words after every 8 columns, stride = 8 mod 32
-    const int base = a->IWB * 4 + (a->IWB / kRotPadCols) * 4;
-    a->row_dw = base + ((8 - base % 32) + 32) % 32;
-    const size_t win = size_t(a->IHB) * a->row_dw * 4;
-    const size_t wts = size_t(a->rpairs) * a->tslices * tb * kRotCB * 4;
+    // 8 words a column, 8 pad words after every 8 columns, stride = 32 mod 64
+    const int base = a->IWB * 8 + (a->IWB / kRotPadCols) * 8;
+    a->row_dw = base + ((32 - base % 64) + 64) % 64;
+    const size_t win = size_t(a->IHB / 2) * a->row_dw * 4;
+    const size_t wts = 2 * size_t(a->rpairs) * a->tslices * tb * kRotCB * 4;
     // the tap groups' partial sums reuse the window's LDS at the end
     const size_t parts = size_t(kRotSplit - 1) * 256 * kRotTHT * kRotTWT * 2 * 4;
     *lds = std::max(win + wts, parts);
@@ -943,7 +962,7 @@ int launch_rotated(const Prob& p, const Plan& pl, int rot, const void* dy, const
     a.tiles_w = int((p.w + a.OWB - 1) / a.OWB);
     a.cblocks = int(p.c / kRotCB);
     const int64_t blocks = int64_t(a.N) * a.tiles_h * a.tiles_w * a.cblocks;
-    if (!split) lds = size_t(a.IHB) * a.row_dw * 4 + size_t(a.rpairs) * a.tslices * tb * kRotCB * 4;
+    if (!split) lds = size_t(a.IHB / 2) * a.row_dw * 4 + 2 * size_t(a.rpairs) * a.tslices * tb * kRotCB * 4;
     const bool bf = p.dtype == CNHWC_BF16;
     if (!split)
         return bf ? launch_rot_inst<BF16, 1, kRotTB>(a, blocks, lds, st)
