@@ -1629,6 +1629,11 @@ int dgrad_splitk_auto(const Prob& p) {
     const int64_t steps = max_taps * ((p.kg + kBK - 1) / kBK);
     if (tiles <= 0 || tiles >= kNumCUs / 2 || steps < 16) return 1;
     const int64_t sp = std::min<int64_t>({(kNumCUs + tiles - 1) / tiles, steps / 4, 64});
+    if (sp > 1) {
+        // a split is wanted: small maps take the filter-streaming kernel and its split count
+        const int ss = dgrad_stream_splits(p);
+        if (ss > 1 && dgrad_stream_reason(p, ss).empty()) return ss;
+    }
     return int(std::max<int64_t>(sp, 1));
 }
 
@@ -1636,6 +1641,9 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
                        void* ws, hipStream_t st) {
     const bool sk = pl.variant == CNHWC_VAR_DGRAD_SPLITK;
     if (sk && (pl.split_c < 2 || ws == nullptr)) return CNHWC_UNSUPPORTED;
+    // split-K over a small map: the filter-streaming kernel (any tune keeps
+    // the ring kernel)
+    if (dgrad_stream_taken(p, pl)) return launch_dgrad_stream(p, pl, dy, w, dx, ws, st);
     const bool pw = pl.variant == CNHWC_VAR_DGRAD_POINTWISE ||
                     (sk && p.r == 1 && p.s == 1 && p.stride == 1 && p.pad_h == 0 && p.pad_w == 0);
     // pointwise with C <= 64: the row-streamed kernel for K = 64..256 in

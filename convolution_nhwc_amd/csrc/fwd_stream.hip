@@ -9,8 +9,8 @@
 // traffic: at 7 x 7, 2048 -> 512 channels, 3 x 3, it is 18.9 MB against 1.6 MB
 // of input and 0.4 MB of output.  A block here owns 32 output channels, one
 // group of whole images (16 tiles of 16 pixels) and a contiguous range of
-// input channels; the image groups of one channel range run on one XCD, so
-// each filter element is fetched from memory once.  The block walks its range
+// input channels; the blocks that read the same filter lines run on one XCD,
+// so each filter element is fetched from memory once.  The block walks its range
 // in 32-channel chunks: a chunk's filter rows (32 output channels x R*S taps x
 // 32 channels) and its input window for the group's images
 // (((Ho-1)*s + R) x ((Wo-1)*s + S) pixels an image, zero outside the image)
@@ -69,11 +69,22 @@ struct StreamFwdArgs {
     int wrow_bytes;     // filter region of a stage (R*S*32 rows)
     int stage_bytes;
     int x_loads;        // 16-byte window loads per lane per stage
+    uint32_t wchunk_bytes;   // filter source advance per 32-channel chunk
     int ktiles, splits, csplit, npairs;
+    int mparts, nblocks;   // image groups; ktiles * splits * mparts
     FastDiv fd_win, fd_iw, fd_hv, fd_vw;   // division by IH*IW, IW, Ho*VW, VW
 };
 
 __device__ inline int sw_chunk(int row) { return (row >> 2) & 3; }
+
+// 64-bit LDS transpose read of 16-bit elements (ds_read_b64_tr_b16): within a
+// 16-lane group, lane i gets element i % 4 ... of the four rows the group's
+// lanes address, so 4 x 4 tiles come back transposed.
+__device__ inline i32x2 lds_read_tr16(const unsigned char* p) {
+    typedef short v4i16 __attribute__((ext_vector_type(4)));
+    return __builtin_bit_cast(
+        i32x2, __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) v4i16*)p));
+}
 
 // Workgroup barrier without the full wait for outstanding memory operations
 // that __syncthreads() implies: the loads of the next chunk pair stay in
@@ -81,7 +92,13 @@ __device__ inline int sw_chunk(int row) { return (row >> 2) & 3; }
 // clobber keeps the compiler from moving LDS accesses across it.
 __device__ inline void ring_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-template <typename T, int TAPS>
+// DG: the backward-data pass of a stride-1 convolution as this forward
+// correlation (of dY, at padding R-1-pad, with the filter rotated by 180
+// degrees and its two channel axes swapped).  The filter as stored has the
+// output channels of that correlation contiguous, so a stage's filter rows
+// are (tap, reduction channel) rows of 32 output channels, read back into the
+// MFMA layout with the LDS transpose read.
+template <typename T, int TAPS, bool DG>
 __global__ __launch_bounds__(kSThreads, 1) void fwd_stream_kernel(const StreamFwdArgs a) {
     constexpr int kS = TAPS == 9 ? 3 : 1;           // filter width
     constexpr int kWRows = TAPS * kSKB;             // filter rows of a stage
@@ -92,13 +109,18 @@ __global__ __launch_bounds__(kSThreads, 1) void fwd_stream_kernel(const StreamFw
     const int half = wave >> 2;    // chunk parity this wave multiplies
     const int grp = wave & 3;      // its tiles: 4 grp .. 4 grp + 3 of the image group
 
-    // block -> (image group, k tile, split); the image groups of one
-    // (k tile, split) are ktiles * splits blocks apart
-    const int per_part = a.ktiles * a.splits;
-    const int mp = blockIdx.x / per_part;
-    const int rest = blockIdx.x - mp * per_part;
+    // block -> (image group, k tile, split).  Blocks are dealt to the 8 XCDs
+    // round-robin; the remap gives each XCD a contiguous run of the order
+    // (split, k tile, image group), so the image groups of a k tile and
+    // neighbouring k tiles -- the blocks that read the same filter lines (the
+    // same 128-byte lines of a dgrad filter row hold two k tiles) -- and one
+    // split's input channels share an L2
+    int lb = blockIdx.x;
+    if ((a.nblocks & 7) == 0) lb = (lb & 7) * (a.nblocks >> 3) + (lb >> 3);
+    const int mp = lb % a.mparts;
+    const int rest = lb / a.mparts;
+    const int kt = rest % a.ktiles;
     const int sp = rest / a.ktiles;
-    const int kt = rest - sp * a.ktiles;
     const int k0 = kt * kSKB;
     const int c_lo = sp * a.csplit;
     const int img0 = mp * a.part_imgs;
@@ -122,7 +144,11 @@ __global__ __launch_bounds__(kSThreads, 1) void fwd_stream_kernel(const StreamFw
         if (i < kWLoads && e < wslots) {
             const int row = e >> 2, pos = e & 3;
             const int tap = row / kSKB, k = row - tap * kSKB;
-            wsrc[i] = uint32_t(((size_t(k0 + k) * TAPS + tap) * a.C + c_lo + (pos ^ sw_chunk(row)) * 8) * 2);
+            if constexpr (DG)   // row (tap, reduction channel c_lo + k): 32 output channels from k0
+                wsrc[i] = uint32_t(((size_t(c_lo + k) * TAPS + (TAPS - 1 - tap)) * a.K + k0 +
+                                    (pos ^ sw_chunk(row)) * 8) * 2);
+            else                // row (tap, output channel k0 + k): 32 reduction channels from c_lo
+                wsrc[i] = uint32_t(((size_t(k0 + k) * TAPS + tap) * a.C + c_lo + (pos ^ sw_chunk(row)) * 8) * 2);
         }
         xsrc[i] = kOob;
         if (i < a.x_loads && e < xslots) {
@@ -152,7 +178,7 @@ __global__ __launch_bounds__(kSThreads, 1) void fwd_stream_kernel(const StreamFw
             constexpr int h = q / kWLoads, i = q % kWLoads;
             if (i * kSThreads + tid < wslots)
                 dma16(rw, lds + (set + h) * a.stage_bytes + (i * kSThreads + wave * 64) * 16, wsrc[i],
-                      uint32_t((2 * jj + h) * kSCK * 2));
+                      uint32_t(2 * jj + h) * a.wchunk_bytes);
         } else {
             constexpr int h = (q - 2 * kWLoads) / kSMaxLoads, i = (q - 2 * kWLoads) % kSMaxLoads;
             if (i < a.x_loads && i * kSThreads + tid < xslots)
@@ -189,6 +215,28 @@ __global__ __launch_bounds__(kSThreads, 1) void fwd_stream_kernel(const StreamFw
     }
     // rows t * 32 + 16 f + r16 all swizzle by (r16 >> 2) & 3
     const uint32_t wlane = uint32_t(r16 * kSRow + ((g ^ sw_chunk(r16)) << 4));
+    // DG: fragment (t, f) of lane (r16, g) is output channel 16 f + r16,
+    // reduction channels 8 g .. 8 g + 7: two transposed reads of 4 rows
+    // (t * 32 + 8 g + 4 hh + r16 / 4) x 4 channels (16 f + 4 (r16 % 4)); those
+    // rows swizzle by (2 g + hh) & 3
+    uint32_t wtr[2][2];
+#pragma unroll
+    for (int f = 0; f < 2; ++f)
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+            const int q = r16 & 3;
+            wtr[f][hh] = uint32_t((8 * g + 4 * hh + (r16 >> 2)) * kSRow +
+                                  (((2 * f + (q >> 1)) ^ ((2 * g + hh) & 3)) << 4) + (q & 1) * 8);
+        }
+    auto read_w = [&](const unsigned char* sb, int t, int f) -> i32x4 {
+        if constexpr (DG) {
+            const i32x2 lo = lds_read_tr16(sb + t * kSKB * kSRow + wtr[f][0]);
+            const i32x2 hi = lds_read_tr16(sb + t * kSKB * kSRow + wtr[f][1]);
+            return i32x4{lo[0], lo[1], hi[0], hi[1]};
+        } else {
+            return *reinterpret_cast<const i32x4*>(sb + wlane + (t * 2 + f) * 16 * kSRow);
+        }
+    };
 
     f32x4 acc[2][kSSlots];
 #pragma unroll
@@ -208,7 +256,7 @@ __global__ __launch_bounds__(kSThreads, 1) void fwd_stream_kernel(const StreamFw
         // products, which update 8 different accumulators
         i32x4 wf[2][2], xf[2][kSSlots];
 #pragma unroll
-        for (int f = 0; f < 2; ++f) wf[0][f] = *reinterpret_cast<const i32x4*>(sb + wlane + f * 16 * kSRow);
+        for (int f = 0; f < 2; ++f) wf[0][f] = read_w(sb, 0, f);
 #pragma unroll
         for (int i = 0; i < kSSlots; ++i) xf[0][i] = *reinterpret_cast<const i32x4*>(sb + xaddr[i][0]);
         sfor<TAPS>([&](auto tc) {
@@ -217,7 +265,7 @@ __global__ __launch_bounds__(kSThreads, 1) void fwd_stream_kernel(const StreamFw
             if constexpr (t + 1 < TAPS) {
 #pragma unroll
                 for (int f = 0; f < 2; ++f)
-                    wf[nxt][f] = *reinterpret_cast<const i32x4*>(sb + wlane + ((t + 1) * 2 + f) * 16 * kSRow);
+                    wf[nxt][f] = read_w(sb, t + 1, f);
 #pragma unroll
                 for (int i = 0; i < kSSlots; ++i)
                     xf[nxt][i] = *reinterpret_cast<const i32x4*>(sb + xaddr[i][t + 1]);
@@ -316,6 +364,8 @@ bool stream_geometry(const Prob& p, int splits, StreamFwdArgs* a, size_t* lds) {
     a->splits = splits;
     a->csplit = int(p.c / splits);
     a->npairs = a->csplit / (2 * kSCK);
+    a->mparts = mparts;
+    a->nblocks = a->ktiles * splits * mparts;
     a->fd_win = make_fastdiv(uint32_t(IH * IW));
     a->fd_iw = make_fastdiv(uint32_t(IW));
     a->fd_hv = make_fastdiv(uint32_t(p.ho * a->VW));
@@ -324,22 +374,22 @@ bool stream_geometry(const Prob& p, int splits, StreamFwdArgs* a, size_t* lds) {
     return true;
 }
 
-template <typename T>
+template <typename T, bool DG>
 int launch_taps(int taps, const StreamFwdArgs& a, size_t lds, int blocks, hipStream_t st) {
     auto set_lds = [&](const void* fn) {
         return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, kSLdsMax) == hipSuccess;
     };
     switch (taps) {
     case 1: {
-        static bool ok = set_lds(reinterpret_cast<const void*>(&fwd_stream_kernel<T, 1>));
+        static bool ok = set_lds(reinterpret_cast<const void*>(&fwd_stream_kernel<T, 1, DG>));
         if (!ok) return CNHWC_HIP_ERROR;
-        hipLaunchKernelGGL((fwd_stream_kernel<T, 1>), dim3(blocks), dim3(kSThreads), lds, st, a);
+        hipLaunchKernelGGL((fwd_stream_kernel<T, 1, DG>), dim3(blocks), dim3(kSThreads), lds, st, a);
         return CNHWC_OK;
     }
     case 9: {
-        static bool ok = set_lds(reinterpret_cast<const void*>(&fwd_stream_kernel<T, 9>));
+        static bool ok = set_lds(reinterpret_cast<const void*>(&fwd_stream_kernel<T, 9, DG>));
         if (!ok) return CNHWC_HIP_ERROR;
-        hipLaunchKernelGGL((fwd_stream_kernel<T, 9>), dim3(blocks), dim3(kSThreads), lds, st, a);
+        hipLaunchKernelGGL((fwd_stream_kernel<T, 9, DG>), dim3(blocks), dim3(kSThreads), lds, st, a);
         return CNHWC_OK;
     }
     default: return CNHWC_UNSUPPORTED;
@@ -383,11 +433,65 @@ int launch_fwd_stream(const Prob& p, const Plan& pl, const void* x, const void* 
     a.x_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
     a.w_bytes = uint32_t(p.k * p.r * p.s * p.c * 2);
     a.ws_bytes = uint32_t(int64_t(a.splits) * a.M * p.k * 4);
-    const int blocks = a.ktiles * a.splits * stream_parts(p);
-    const int rc = p.dtype == CNHWC_BF16 ? launch_taps<BF16>(int(p.r * p.s), a, lds, blocks, st)
-                                         : launch_taps<F16>(int(p.r * p.s), a, lds, blocks, st);
+    a.wchunk_bytes = uint32_t(kSCK * 2);
+    const int blocks = a.nblocks;
+    const int rc = p.dtype == CNHWC_BF16 ? launch_taps<BF16, false>(int(p.r * p.s), a, lds, blocks, st)
+                                         : launch_taps<F16, false>(int(p.r * p.s), a, lds, blocks, st);
     if (rc != CNHWC_OK) return rc;
     return launch_split_reduce(p, a.splits, ws, y, st);
+}
+
+// ---- backward data through the same kernel ([PW] split-K: the dgrad of a
+// layer with few output pixels over a deep reduction) ----
+
+namespace {
+// The stride-1 dgrad as a forward problem: input dY (Ho x Wo x K), output dX
+// (H x W x C), padding R-1-pad, filter rotated with its channel axes swapped.
+Prob dgrad_stream_view(const Prob& p) {
+    Prob q = p;
+    q.h = p.ho; q.w = p.wo; q.ho = p.h; q.wo = p.w;
+    q.c = p.k; q.k = p.c; q.cg = p.k; q.kg = p.c;
+    q.pad_h = int(p.r) - 1 - p.pad_h;
+    q.pad_w = int(p.s) - 1 - p.pad_w;
+    return q;
+}
+
+}  // namespace
+
+int dgrad_stream_splits(const Prob& p) {
+    if (p.stride != 1 || p.groups != 1 || p.pad_h > p.r - 1 || p.pad_w > p.s - 1) return 0;
+    return fwd_stream_splits(dgrad_stream_view(p));
+}
+
+std::string dgrad_stream_reason(const Prob& p, int splits) {
+    if (p.stride != 1) return "the filter-streaming split-K dgrad needs stride 1";
+    if (p.groups != 1) return "the filter-streaming split-K dgrad needs groups == 1";
+    if (p.pad_h > p.r - 1 || p.pad_w > p.s - 1)
+        return "the filter-streaming split-K dgrad needs pad_h <= R-1 and pad_w <= S-1";
+    return fwd_stream_reason(dgrad_stream_view(p), splits);
+}
+
+bool dgrad_stream_taken(const Prob& p, const Plan& pl) {
+    return pl.variant == CNHWC_VAR_DGRAD_SPLITK && pl.split_c > 1 && pl.tune == 0 &&
+           dgrad_stream_reason(p, pl.split_c).empty();
+}
+
+int launch_dgrad_stream(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx, void* ws,
+                        hipStream_t st) {
+    const Prob q = dgrad_stream_view(p);
+    StreamFwdArgs a{};
+    size_t lds;
+    if (!stream_geometry(q, pl.split_c, &a, &lds)) return CNHWC_UNSUPPORTED;
+    a.x = dy; a.w = w; a.ws = static_cast<float*>(ws);
+    a.x_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
+    a.w_bytes = uint32_t(p.k * p.r * p.s * p.c * 2);
+    a.ws_bytes = uint32_t(int64_t(a.splits) * a.M * q.k * 4);
+    a.wchunk_bytes = uint32_t(kSCK * p.r * p.s * p.c * 2);
+    const int blocks = a.nblocks;
+    const int rc = p.dtype == CNHWC_BF16 ? launch_taps<BF16, true>(int(p.r * p.s), a, lds, blocks, st)
+                                         : launch_taps<F16, true>(int(p.r * p.s), a, lds, blocks, st);
+    if (rc != CNHWC_OK) return rc;
+    return launch_split_reduce(q, a.splits, ws, dx, st);
 }
 
 }  // namespace cnhwc

@@ -133,7 +133,11 @@ std::string plan_name(const Prob& p, const Plan& pl) {
     case CNHWC_VAR_DGRAD_IGEMM:
         std::snprintf(buf, sizeof buf, "dgrad_igemm_%s_s%d", dt(p), p.stride); break;
     case CNHWC_VAR_DGRAD_SPLITK:
-        std::snprintf(buf, sizeof buf, "dgrad_splitk%d_%s_s%d+split_reduce", pl.split_c, dt(p), p.stride); break;
+        if (dgrad_stream_taken(p, pl))
+            std::snprintf(buf, sizeof buf, "dgrad_stream_splitk%d_%s+split_reduce", pl.split_c, dt(p));
+        else
+            std::snprintf(buf, sizeof buf, "dgrad_splitk%d_%s_s%d+split_reduce", pl.split_c, dt(p), p.stride);
+        break;
     case CNHWC_VAR_DGRAD_DW_STREAM:
         std::snprintf(buf, sizeof buf, "dgrad_dw_stream_%s_f%lldx%lld_s%d_cpl%d", dt(p),
                       (long long)p.r, (long long)p.s, p.stride, pl.cpl); break;

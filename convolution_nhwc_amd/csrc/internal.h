@@ -74,6 +74,14 @@ int launch_fwd_stream(const Prob& p, const Plan& pl, const void* x, const void* 
                       hipStream_t st);
 // Whether the split-C forward of this plan runs on the filter-streaming kernel.
 bool fwd_stream_taken(const Prob& p, const Plan& pl);
+// Split-K dgrad (stride 1, groups 1) on the filter-streaming kernel: its split
+// count (0 if it does not apply), acceptance, whether a plan takes it, launch
+// (main pass + the split reduce).
+int dgrad_stream_splits(const Prob& p);
+std::string dgrad_stream_reason(const Prob& p, int splits);
+bool dgrad_stream_taken(const Prob& p, const Plan& pl);
+int launch_dgrad_stream(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx, void* ws,
+                        hipStream_t st);
 // Second pass of split-C: y = round(sum over splits of ws[split]), ascending.
 int launch_split_reduce(const Prob& p, int splits, const void* ws, void* y, hipStream_t st);
 int launch_fwd_grouped(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,

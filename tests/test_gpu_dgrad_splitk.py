@@ -9,7 +9,7 @@ import pytest
 
 import oracle
 from convolution_nhwc_amd import api, synth
-from gpu_util import check_close, from_device, full_size_parity, parity, run_gpu, to_device
+from gpu_util import check_close, from_device, full_size_parity, operands, parity, run_gpu, to_device
 
 pytestmark = pytest.mark.gpu
 
@@ -81,3 +81,36 @@ def test_splitk_dgrad_workload_full_size():
     benchmark times (automatic split), every dX element against the oracle."""
     assert api.cnhwc_plan(synth.WORKLOADS["f4_splitk_dgrad"]["prob"], api.OP_DGRAD)[1] == api.VAR_DGRAD_SPLITK
     full_size_parity("f4_splitk_dgrad")
+
+
+# split-K over a small map (stride 1, groups 1, 1x1 or 3x3): the
+# filter-streaming kernel, the automatic choice for these shapes
+DSTREAM = [
+    P(2, 7, 7, 256, 512, 3, 3, 1, 1, 1, dtype="bf16"),
+    P(3, 5, 6, 96, 256, 3, 3, 1, 1, 1),               # 90 pixels: ragged last tile, 3 channel tiles
+    P(2, 7, 7, 256, 1024, 1, 1),                      # 1x1
+    P(1, 8, 6, 64, 256, 3, 3, 1, 1, 0, dtype="bf16"), # per-axis padding
+    P(8, 7, 7, 128, 256, 3, 3, 1, 1, 1, dtype="bf16"),# 392 pixels: two groups of 4 images
+]
+
+
+@pytest.mark.parametrize("p", DSTREAM, ids=ident)
+def test_splitk_dgrad_filter_streaming_parity(p):
+    name, var = api.cnhwc_plan(p, api.OP_DGRAD)
+    assert var == api.VAR_DGRAD_SPLITK and name.startswith("dgrad_stream_splitk"), name
+    parity(p, "dgrad", 124)
+
+
+@pytest.mark.parametrize("p", DSTREAM[:3], ids=ident)
+def test_splitk_dgrad_filter_streaming_matches_ring_kernel_on_exact_inputs(p):
+    """Inputs in {-1, 0, 1}: exact partial sums, so the filter-streaming kernel
+    and the ring kernel (tune 1) agree bit for bit at the same split count."""
+    name = api.cnhwc_plan(p, api.OP_DGRAD)[0]
+    split = int(name.split("splitk")[1].split("_")[0])
+    ab, _, wb, _ = operands(p, "dgrad", 125, exact=True)
+    stream = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    with api.override(variant=api.VAR_DGRAD_SPLITK, split_c=split, tune=1):
+        assert api.cnhwc_plan(p, api.OP_DGRAD)[0].startswith("dgrad_splitk")
+        ring = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    assert np.array_equal(stream, ring)
+    parity(p, "dgrad", 125, exact=True)
