@@ -220,9 +220,10 @@ const char* cnhwc_last_error(void);
  * tune: a launch-shape knob of the chosen kernel (implicit-GEMM dgrad: 1 runs
  * every phase class on the ring kernel, 2 runs classes with two or more taps on
  * the dY-window kernel, a value of 16 or more sets the ring kernel's pixels per
- * tile; direct forward: 1 forces the register-staged kernel, 2 or 3 the
- * input-window kernel (3 also where split-C over a small map would take the
- * filter-streaming kernel); split-K wgrad: the number of pixel splits per batch
+ * tile, and for split-K any nonzero value keeps the ring kernel where the
+ * filter-streaming one applies; direct forward: 1 forces the register-staged
+ * kernel, 2 or 3 the input-window kernel (3 also where split-C over a small
+ * map would take the filter-streaming kernel); split-K wgrad: the number of pixel splits per batch
  * chunk; depthwise rotated-filter: 1 runs one tap group, 2 two groups, both
  * with 8-column filter slices even for filters narrower than 8 columns; other
  * kernels ignore it);
