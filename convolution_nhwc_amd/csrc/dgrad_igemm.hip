@@ -1654,6 +1654,9 @@ int launch_dgrad_igemm(const Prob& p, const Plan& pl, const void* dy, const void
         if (pw_rows_ok(p) && pl.tune != 3 && pl.tune < 16) return launch_pw_rows(p, dy, w, dx, st);
         if (pw_stages(p.k) > 0) return launch_pw_persist(p, pl, dy, w, dx, st);
     }
+    // strided problems whose channel counts fit its tiles: the persistent
+    // 8-wave kernel (tune 5 forces it, also at stride 1)
+    if (!pw && !sk && dgrad_persist_taken(p, pl)) return launch_dgrad_persist(p, dy, w, dx, st);
     // Stride 1: classes with two or more taps go to the window kernel, the
     // rest (and the pointwise fast path) to the ring kernel below.  Strided
     // problems split into several classes of few taps each, where the window

@@ -131,7 +131,11 @@ std::string plan_name(const Prob& p, const Plan& pl) {
     case CNHWC_VAR_DGRAD_POINTWISE:
         std::snprintf(buf, sizeof buf, "dgrad_pointwise_%s", dt(p)); break;
     case CNHWC_VAR_DGRAD_IGEMM:
-        std::snprintf(buf, sizeof buf, "dgrad_igemm_%s_s%d", dt(p), p.stride); break;
+        if (dgrad_persist_taken(p, pl))
+            std::snprintf(buf, sizeof buf, "dgrad_persist_%s_s%d", dt(p), p.stride);
+        else
+            std::snprintf(buf, sizeof buf, "dgrad_igemm_%s_s%d", dt(p), p.stride);
+        break;
     case CNHWC_VAR_DGRAD_SPLITK:
         if (dgrad_stream_taken(p, pl))
             std::snprintf(buf, sizeof buf, "dgrad_stream_splitk%d_%s+split_reduce", pl.split_c, dt(p));

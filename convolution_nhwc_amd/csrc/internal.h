@@ -77,6 +77,12 @@ bool fwd_stream_taken(const Prob& p, const Plan& pl);
 // Split-K dgrad (stride 1, groups 1) on the filter-streaming kernel: its split
 // count (0 if it does not apply), acceptance, whether a plan takes it, launch
 // (main pass + the split reduce).
+// Strided dgrad on the persistent 8-wave kernel (dgrad_persist.hip): the
+// reason it cannot run a problem ("" if it can), whether the implicit-GEMM plan
+// takes it (automatic choice for stride >= 2, or tune 5), and its launch.
+std::string dgrad_persist_reason(const Prob& p);
+bool dgrad_persist_taken(const Prob& p, const Plan& pl);
+int launch_dgrad_persist(const Prob& p, const void* dy, const void* w, void* dx, hipStream_t st);
 int dgrad_stream_splits(const Prob& p);
 std::string dgrad_stream_reason(const Prob& p, int splits);
 bool dgrad_stream_taken(const Prob& p, const Plan& pl);

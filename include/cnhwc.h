@@ -219,8 +219,9 @@ const char* cnhwc_last_error(void);
  * CNHWC_VAR_DGRAD_SPLITK (with the automatic variant it forces that split);
  * tune: a launch-shape knob of the chosen kernel (implicit-GEMM dgrad: 1 runs
  * every phase class on the ring kernel, 2 runs classes with two or more taps on
- * the dY-window kernel, a value of 16 or more sets the ring kernel's pixels per
- * tile, and for split-K any nonzero value keeps the ring kernel where the
+ * the dY-window kernel, 5 runs the persistent 8-wave kernel (taken by default
+ * at stride >= 2 when C/groups is a multiple of 256 and K/groups of 128), a
+ * value of 16 or more sets the ring kernel's pixels per tile, and for split-K any nonzero value keeps the ring kernel where the
  * filter-streaming one applies; direct forward: 1 forces the register-staged
  * kernel, 2 or 3 the input-window kernel (3 also where split-C over a small
  * map would take the filter-streaming kernel); split-K wgrad: the number of pixel splits per batch

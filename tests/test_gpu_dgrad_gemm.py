@@ -97,6 +97,61 @@ def test_igemm_parity_both_kernels(p, tune):
         parity(p, "dgrad", 108)
 
 
+PERSIST = [
+    P(2, 14, 14, 256, 128, 3, 3, 2, 1, 1),             # few tiles: shorter tiles, one per block
+    P(2, 15, 13, 256, 256, 3, 3, 2, 1, 1),             # odd extents: classes of different sizes
+    P(1, 16, 17, 256, 128, 3, 3, 3, 1, 1),             # stride 3: 9 classes
+    P(1, 12, 13, 256, 128, 5, 3, 2, 2, 1),             # non-square filter, per-axis padding
+    P(2, 10, 10, 512, 256, 3, 3, 2, 1, 1, groups=2),   # two groups of 256 channels
+    P(1, 14, 14, 512, 128, 3, 3, 2, 1, 1),             # two channel tiles
+    P(1, 15, 15, 256, 128, 4, 4, 2, 1, 2),             # even filter
+    P(1, 10, 10, 256, 384, 3, 3, 2, 1, 1),             # 12 reduction chunks per tap
+    P(1, 5, 6, 256, 128, 3, 3, 2, 1, 1),               # classes of one or two rows
+    P(2, 14, 14, 256, 256, 3, 3, 2, 1, 1, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("p", PERSIST, ids=ident)
+def test_persistent_parity_and_bitwise_equal_to_ring(p):
+    """The persistent 8-wave strided kernel (the implicit-GEMM plan's choice
+    for these shapes; small ones go to split-K by default): within tolerance
+    of the oracle, and bit-identical to the 4-wave ring kernel, which runs the
+    same MFMA chain per output."""
+    with api.override(variant=api.VAR_DGRAD_IGEMM):
+        assert api.cnhwc_plan(p, api.OP_DGRAD)[0].startswith("dgrad_persist_")
+        _, got = parity(p, "dgrad", 112)
+    with api.override(variant=api.VAR_DGRAD_IGEMM, tune=1):
+        assert api.cnhwc_plan(p, api.OP_DGRAD)[0].startswith("dgrad_igemm_")
+        _, ring = parity(p, "dgrad", 112)
+    assert np.array_equal(got.cpu().numpy(), ring.cpu().numpy())
+
+
+def test_persistent_forced_at_stride_1():
+    """tune 5 runs the persistent kernel on a stride-1 problem (one class of
+    nine taps)."""
+    p = P(2, 12, 12, 256, 128, 3, 3, 1, 1, 1)
+    with api.override(variant=api.VAR_DGRAD_IGEMM, tune=5):
+        assert api.cnhwc_plan(p, api.OP_DGRAD)[0].startswith("dgrad_persist_")
+        _, got = parity(p, "dgrad", 114)
+    with api.override(variant=api.VAR_DGRAD_IGEMM, tune=1):
+        _, ring = parity(p, "dgrad", 114)
+    assert np.array_equal(got.cpu().numpy(), ring.cpu().numpy())
+
+
+def test_persistent_multi_tile_blocks_bitwise_equal_to_ring():
+    """The 3x3 stride-2 workload at full size (blocks of the lighter classes
+    walk two or four tiles each): bit-identical to the ring kernel on the
+    same random inputs (the oracle comparison runs in the full-size test)."""
+    p = synth.WORKLOADS["c3b_3x3_s2"]["prob"]
+    assert api.cnhwc_plan(p, api.OP_DGRAD)[0].startswith("dgrad_persist_")
+    ab, _, wb, _ = operands(p, "dgrad", 113)
+    out = run_gpu(p, "dgrad", ab, wb)
+    assert np.isfinite(from_device(out, p["dtype"])).all()
+    with api.override(variant=api.VAR_DGRAD_IGEMM, tune=1):
+        ring = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    assert np.array_equal(out.cpu().numpy(), ring)
+
+
 @pytest.mark.parametrize("p", [P(1, 12, 12, 64, 64, 3, 3, 2, 1, 1), P(2, 8, 8, 32, 32, 1, 1),
                                P(1, 10, 10, 32, 64, 3, 3, 1, 1, 1, dtype="bf16")], ids=ident)
 def test_exact_small_integers_bitwise(p):
