@@ -62,6 +62,39 @@ constexpr int kPEpiWave = 16 * 128;        // epilogue staging per wave: 16 pixe
 constexpr int kPARegs = kPABytes / 1024;   // 14 one-KiB regions of 16 pixel rows
 constexpr int kPBRegs = kPBBytes / 1024;   // 16 regions of 2 k-rows
 constexpr int kPMaxClasses = 16;
+constexpr int kPPre = 2;                   // pixel tiles multiplied before a step's barrier
+constexpr int kPTail = 2;                  // dY reads left in flight across a step boundary
+static_assert((kPWMB - kPPre) * (kPWNB - 1) >= 2 * kPWNB + 4, "gaps for the W reads and the loads");
+
+// LDS reads a step issues before its first load (the schedule of the step
+// below: kPPre dY reads after the barrier, then per product a dY read after
+// the fourth product of a pixel tile and W reads in the other gaps)
+constexpr int p_lds_before_loads() {
+    int n = kPPre;
+    for (int m = kPPre * kPWNB; m < kPWMB * kPWNB; ++m) {
+        const int i = m / kPWNB, j = m % kPWNB;
+        if (j == kPWNB - 1) { ++n; continue; }
+        const int q = (i - kPPre) * (kPWNB - 1) + j;
+        if (q < 2 * kPWNB) ++n;
+        else return n;
+    }
+    return n;
+}
+// product index after which the last load of a step issues
+constexpr int p_last_load() {
+    int last = -1;
+    for (int m = kPPre * kPWNB; m < kPWMB * kPWNB; ++m) {
+        const int i = m / kPWNB, j = m % kPWNB;
+        if (j == kPWNB - 1) continue;
+        const int q = (i - kPPre) * (kPWNB - 1) + j;
+        if (q >= 2 * kPWNB && q < 2 * kPWNB + 4) last = m;
+    }
+    return last;
+}
+// the tail reads (the dY reads after the fourth product of pixel tiles
+// kPWMB-2 and kPWMB-1) are a step's last two LDS operations and come after
+// its loads
+static_assert(kPTail == 2 && (kPWMB - kPTail) * kPWNB + kPWNB - 1 > p_last_load(), "tail reads after the loads");
 static_assert(kPBRegs == 16 && kPARegs > 8 && kPARegs <= 16, "two regions of each operand per wave");
 static_assert((kPStages - 1) * kPBBytes < 65536, "stage offsets fit the LDS immediate");
 
@@ -257,15 +290,24 @@ __global__ __launch_bounds__(kPThreads, 1) void dgrad_persist_kernel(const PArgs
                      : "=v"(fb[B][R / 2][R % 2])
                      : "v"(fb_addr[R / 2]), "i"(STG * kPBBytes + (R % 2) * 4 * kPBRow));
     };
-    // the reads are asm, invisible to the compiler's wait tracking: wait here
-    // and tie the fragments to the wait
-    auto wait_frags = [&](auto bc) {
-        constexpr int B = decltype(bc)::value;
-        asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(fa[0]), "+v"(fb[B][0][0]));
+    // The reads are asm, invisible to the compiler's wait tracking: wait
+    // explicitly and tie the fragments to the wait.  At the end of a step all
+    // but the last kPTail dY reads (the newest LDS operations) must have
+    // landed; those finish during the next step's first products and are
+    // waited for before its first load (which overwrites their stage) and
+    // before their own products.
+    auto wait_frags = [&](auto bc, auto pending) {
+        constexpr int B = decltype(bc)::value, P = decltype(pending)::value;
+        asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(fa[0]), "+v"(fb[B][0][0]) : "i"(P));
 #pragma unroll
-        for (int i = 1; i < kPWMB; ++i) asm volatile("" : "+v"(fa[i]));
+        for (int i = 1; i < kPWMB - P; ++i) asm volatile("" : "+v"(fa[i]));
 #pragma unroll
         for (int j = 0; j < kPWNB; ++j) asm volatile("" : "+v"(fb[B][j][0]), "+v"(fb[B][j][1]));
+    };
+    auto wait_tail = [&](auto nc) {
+        constexpr int N = decltype(nc)::value;   // LDS operations issued since
+        (void)fa;
+        asm volatile("s_waitcnt lgkmcnt(%2)" : "+v"(fa[kPWMB - 2]), "+v"(fa[kPWMB - 1]) : "i"(N));
     };
     auto mfma_one = [&](auto bc, auto ic, auto jc) {
         constexpr int B = decltype(bc)::value, i = decltype(ic)::value, j = decltype(jc)::value;
@@ -294,8 +336,14 @@ __global__ __launch_bounds__(kPThreads, 1) void dgrad_persist_kernel(const PArgs
     // lanes of a pixel write 64 contiguous bytes.
     auto store_rows = [&](auto ic, const PTile& pt) {
         constexpr int I = decltype(ic)::value;
-        const uint32_t lane_off = uint32_t(((fgrp & 1) << 5) | ((fgrp >> 1) << 4));
-        const uint32_t off = px_off(pt, wm * (kPWMB * 16) + I * 16 + frow) + lane_off;
+        // lane-derived values recomputed here from a copy the compiler cannot
+        // hoist out of the tile loop (they would otherwise stay live in
+        // registers through every step)
+        int l;
+        asm volatile("v_mov_b32 %0, %1" : "=v"(l) : "v"(lane));
+        const int lf = l & 15, lg = l >> 4;
+        const uint32_t lane_off = uint32_t(((lg & 1) << 5) | ((lg >> 1) << 4));
+        const uint32_t off = px_off(pt, wm * (kPWMB * 16) + I * 16 + lf) + lane_off;
 #pragma unroll
         for (int jp = 0; jp < kPWNB; jp += 2) {
             const auto lo = __builtin_amdgcn_permlane16_swap(pack2<T>(acc[I][jp][0], acc[I][jp][1]),
@@ -310,48 +358,63 @@ __global__ __launch_bounds__(kPThreads, 1) void dgrad_persist_kernel(const PArgs
     };
 
     // One step out of stage STG (W fragments in buffer STG & 1, dY fragments
-    // in fa): wait for the next stage, barrier (every wave has also finished
-    // reading this stage, so it takes the loads of the step three ahead), then
-    // the MFMAs pixel-tile by pixel-tile, with the next step's W reads and
-    // the loads in the first gaps and each dY fragment re-read after its last
-    // product.  The first step of a tile (FIRST) stores the previous tile's
-    // sums from the accumulators and starts its own products from zero.
+    // in fa, all read during the previous step).  The products of the first
+    // kPPre pixel tiles need nothing new, so they issue before the wait for
+    // the next stage and the barrier (every wave has also finished reading
+    // this stage after it, so it takes the loads of the step three ahead):
+    // the matrix cores stay busy while the slower wave of each SIMD reaches
+    // the barrier.  The rest of the products follow pixel-tile by pixel-tile,
+    // with the next step's W reads and the loads in the first gaps and each
+    // dY fragment re-read after its last product.  The first step of a tile
+    // (FIRST) stores the previous tile's sums from the accumulators before
+    // anything else and starts its own products from zero.
     auto step = [&](auto stg, auto firstc, const PTile& prev) {
         constexpr int STG = decltype(stg)::value;
         constexpr bool FIRST = decltype(firstc)::value;
         constexpr int FB = STG & 1, NB = FB ^ 1, NXT = (STG + 1) % kPStages;
-        wait_steps(IC<kPStages - 2>{});
-        __builtin_amdgcn_s_barrier();
-        // the previous tile's stores go out before this step's loads: the
-        // next step's wait (which counts the stores too) then waits for no
-        // load younger than the step three ahead
         if constexpr (FIRST) {
             sfor<kPWMB>([&](auto ic) {
                 store_rows(ic, prev);
                 __builtin_amdgcn_sched_barrier(0);
             });
         }
-        __builtin_amdgcn_sched_barrier(0);
-        sfor<NM>([&](auto mc) {
-            constexpr int M = decltype(mc)::value;
-            constexpr int i = M / kPWNB, j = M % kPWNB;
+        auto product = [&](auto ic, auto jc) {
+            constexpr int i = decltype(ic)::value, j = decltype(jc)::value;
             if constexpr (FIRST) {
                 const i32x4 w4 = {fb[FB][j][0][0], fb[FB][j][0][1], fb[FB][j][1][0], fb[FB][j][1][1]};
                 acc[i][j] = mfma16x16x32<T>(w4, fa[i], f32x4{0.f, 0.f, 0.f, 0.f});
             } else {
-                mfma_one(IC<FB>{}, IC<i>{}, IC<j>{});
+                mfma_one(IC<FB>{}, ic, jc);
             }
+        };
+        sfor<kPPre * kPWNB>([&](auto mc) {
+            constexpr int M = decltype(mc)::value;
+            product(IC<M / kPWNB>{}, IC<M % kPWNB>{});
+        });
+        __builtin_amdgcn_sched_barrier(0);
+        wait_steps(IC<kPStages - 2>{});
+        __builtin_amdgcn_s_barrier();
+        __builtin_amdgcn_sched_barrier(0);
+        sfor<kPPre>([&](auto ic) { read_a(IC<NXT>{}, ic); });
+        sfor<NM - kPPre * kPWNB>([&](auto mc) {
+            constexpr int M = decltype(mc)::value + kPPre * kPWNB;
+            constexpr int i = M / kPWNB, j = M % kPWNB;
+            product(IC<i>{}, IC<j>{});
             if constexpr (j == kPWNB - 1) {
                 read_a(IC<NXT>{}, IC<i>{});
             } else {
-                constexpr int q = i * (kPWNB - 1) + j;   // gap index
-                if constexpr (q < 2 * kPWNB) read_b(IC<NXT>{}, IC<NB>{}, IC<q>{});
-                else if constexpr (q < 2 * kPWNB + 4) load_one(stg, IC<q - 2 * kPWNB>{});
+                constexpr int q = (i - kPPre) * (kPWNB - 1) + j;   // gap index
+                if constexpr (q < 2 * kPWNB) {
+                    read_b(IC<NXT>{}, IC<NB>{}, IC<q>{});
+                } else if constexpr (q < 2 * kPWNB + 4) {
+                    if constexpr (q == 2 * kPWNB) wait_tail(IC<p_lds_before_loads()>{});
+                    load_one(stg, IC<q - 2 * kPWNB>{});
+                }
             }
             __builtin_amdgcn_sched_barrier(0);
         });
         advance();
-        wait_frags(IC<NB>{});
+        wait_frags(IC<NB>{}, IC<kPTail>{});
     };
 
     // prologue: steps 0..3 into stages 0..3, then step 0's fragments
@@ -363,7 +426,7 @@ __global__ __launch_bounds__(kPThreads, 1) void dgrad_persist_kernel(const PArgs
     __builtin_amdgcn_s_barrier();
     sfor<kPWMB>([&](auto ic) { read_a(IC<0>{}, ic); });
     sfor<2 * kPWNB>([&](auto rc) { read_b(IC<0>{}, IC<0>{}, rc); });
-    wait_frags(IC<0>{});
+    wait_frags(IC<0>{}, IC<0>{});
 
     // Tiles start at stage 0 (steps per tile are a multiple of 4).  The
     // previous tile of the first one is empty: its stores fall outside dX.
@@ -387,6 +450,7 @@ __global__ __launch_bounds__(kPThreads, 1) void dgrad_persist_kernel(const PArgs
         }
         prev = p_tile(t, a.ctiles, a.G, a.bm, mc);
     }
+    wait_frags(IC<0>{}, IC<0>{});   // the last step's tail reads
     // The last tile: stored through the wave's own LDS staging area, 16
     // pixels at a time: the lanes write their 4-channel pieces (row = pixel,
     // 16-byte chunk index XOR-ed by row & 7), read back whole 128-byte rows
