@@ -166,7 +166,11 @@ std::string plan_name(const Prob& p, const Plan& pl) {
     case CNHWC_VAR_FWD_GROUPED:
         std::snprintf(buf, sizeof buf, "fwd_grouped_merge_%s", dt(p)); break;
     case CNHWC_VAR_FWD_IGEMM:
-        std::snprintf(buf, sizeof buf, "fwd_igemm_%s_f%lldx%lld", dt(p), (long long)p.r, (long long)p.s); break;
+        if (fwd_pw_rows_taken(p, pl))
+            std::snprintf(buf, sizeof buf, "fwd_pw_rows_%s", dt(p));
+        else
+            std::snprintf(buf, sizeof buf, "fwd_igemm_%s_f%lldx%lld", dt(p), (long long)p.r, (long long)p.s);
+        break;
     case CNHWC_VAR_FWD_GENERIC:
         std::snprintf(buf, sizeof buf, "fwd_generic_%s", dt(p)); break;
     case CNHWC_VAR_FWD_DW_TILED:

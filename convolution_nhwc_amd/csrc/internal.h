@@ -77,6 +77,9 @@ bool fwd_stream_taken(const Prob& p, const Plan& pl);
 // Split-K dgrad (stride 1, groups 1) on the filter-streaming kernel: its split
 // count (0 if it does not apply), acceptance, whether a plan takes it, launch
 // (main pass + the split reduce).
+// Whether the implicit-GEMM forward plan runs the pointwise row kernel
+// (fwd_igemm.hip: 1x1 stride-1 unpadded single-group, C 32/64, K 64/128/256).
+bool fwd_pw_rows_taken(const Prob& p, const Plan& pl);
 // Strided dgrad on the persistent 8-wave kernel (dgrad_persist.hip): the
 // reason it cannot run a problem ("" if it can), whether the implicit-GEMM plan
 // takes it (automatic choice for stride >= 2, or tune 5), and its launch.

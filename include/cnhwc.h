@@ -224,7 +224,9 @@ const char* cnhwc_last_error(void);
  * value of 16 or more sets the ring kernel's pixels per tile, and for split-K any nonzero value keeps the ring kernel where the
  * filter-streaming one applies; direct forward: 1 forces the register-staged
  * kernel, 2 or 3 the input-window kernel (3 also where split-C over a small
- * map would take the filter-streaming kernel); split-K wgrad: the number of pixel splits per batch
+ * map would take the filter-streaming kernel); implicit-GEMM forward: 1 keeps
+ * the filter transform and the dgrad kernels for 1x1 shapes the pointwise row
+ * kernel takes; split-K wgrad: the number of pixel splits per batch
  * chunk; depthwise rotated-filter: 1 runs one tap group, 2 two groups, both
  * with 8-column filter slices even for filters narrower than 8 columns; other
  * kernels ignore it);

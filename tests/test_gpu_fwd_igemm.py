@@ -57,6 +57,30 @@ def test_fwd_igemm_chunked_equals_unchunked():
     assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
 
 
+POINTWISE_ROWS = [
+    P(2, 9, 9, 64, 256, 1, 1),                  # 162 pixels: ragged last block
+    P(1, 7, 5, 32, 64, 1, 1),                   # 35 pixels: one wave, most rows past M
+    P(3, 10, 11, 64, 128, 1, 1),
+    P(2, 8, 8, 32, 256, 1, 1, dtype="bf16"),
+    P(4, 28, 28, 64, 256, 1, 1, dtype="bf16"),  # several blocks a wave
+]
+
+
+@pytest.mark.parametrize("p", POINTWISE_ROWS, ids=ident)
+def test_pointwise_row_kernel_parity_and_bitwise_equal_to_transform_path(p):
+    """The pointwise forward row kernel (filter read as stored, no transform)
+    against the oracle, and bit for bit against the filter transform followed
+    by the dgrad kernels' pointwise path (tune 1), which run the same MFMA
+    chain per output."""
+    with api.override(variant=api.VAR_FWD_IGEMM):
+        assert api.cnhwc_plan(p, api.OP_FWD)[0].startswith("fwd_pw_rows_")
+        _, a = parity(p, "fwd", 133)
+    with api.override(variant=api.VAR_FWD_IGEMM, tune=1):
+        assert api.cnhwc_plan(p, api.OP_FWD)[0].startswith("fwd_igemm_")
+        _, b = parity(p, "fwd", 133)
+    assert np.array_equal(a.cpu().numpy(), b.cpu().numpy())
+
+
 def test_fwd_igemm_workload_full_size():
     """The benchmarked pointwise forward at full size, in the launch
     configuration the benchmark times (automatic dispatch), every output
