@@ -382,8 +382,8 @@ __device__ __forceinline__ void tile_accumulate(const uint32_t* win, const uint3
 }
 
 // Stores a lane tile at dX (n, h .., w .., channels c, c + 1): 4 bytes a pixel.
-template <typename T, int THL>
-__device__ __forceinline__ void tile_store(const TileArgs& a, __amdgpu_buffer_rsrc_t rdx,
+template <typename T, int THL, typename Args>
+__device__ __forceinline__ void tile_store(const Args& a, __amdgpu_buffer_rsrc_t rdx,
                                            const float (&acc)[THL][kTileTWL][2], int n, int h0, int w0,
                                            int c) {
     if (c >= a.C) return;
@@ -512,6 +512,274 @@ __global__ __launch_bounds__(256, tile_occupancy(R)) void dw_tile_kernel(const T
     tile_accumulate<T, R, S, kTileTHL>(reinterpret_cast<const uint32_t*>(lds) + (lr0 * WC + lc0) * 32 + cp,
                                        wp, acc);
     tile_store<T, kTileTHL>(a, rdx, acc, n, h0 + lr0, w0 + lc0, c0 + 2 * cp);
+}
+
+// tile_accumulate over window rows WC pixels apart, with the next window row
+// read one step ahead and the steps fenced off from each other in the
+// schedule.
+template <typename T, int R, int S, int THL, int WC>
+__device__ __forceinline__ void tile_accumulate_pf(const uint32_t* win, const uint32_t (&wp)[(R + 1) / 2][S][2],
+                                                   float (&acc)[THL][kTileTWL][2]) {
+    constexpr int RV = kTileTWL + S - 1;
+    constexpr int NU = THL + R - 1;
+#pragma unroll
+    for (int h = 0; h < THL; ++h)
+#pragma unroll
+        for (int w = 0; w < kTileTWL; ++w) acc[h][w][0] = acc[h][w][1] = 0.f;
+    uint32_t prev[RV], cur[RV];
+#pragma unroll
+    for (int v = 0; v < RV; ++v) prev[v] = win[v * 32];
+#pragma unroll
+    for (int v = 0; v < RV; ++v) cur[v] = win[v * 32];
+#pragma unroll
+    for (int ul = 1; ul <= NU; ++ul) {
+        uint32_t nxt[RV];
+        if (ul < NU) {
+#pragma unroll
+            for (int v = 0; v < RV; ++v) nxt[v] = win[(ul * WC + v) * 32];
+        }
+        uint32_t p0[RV], p1[RV];
+#pragma unroll
+        for (int v = 0; v < RV; ++v) {
+            p0[v] = pair_lo(cur[v], prev[v]);
+            p1[v] = pair_hi(cur[v], prev[v]);
+        }
+#pragma unroll
+        for (int hl = 0; hl < THL; ++hl) {
+            const int r = hl + R - ul;
+            if (r < 0 || r >= R || (r & 1)) continue;
+#pragma unroll
+            for (int t = 0; t < S; ++t) {
+                const uint32_t w0 = wp[r / 2][t][0], w1 = wp[r / 2][t][1];
+#pragma unroll
+                for (int wl = 0; wl < kTileTWL; ++wl) {
+                    const int v = wl + S - 1 - t;
+                    acc[hl][wl][0] = dot2<T>(p0[v], w0, acc[hl][wl][0]);
+                    acc[hl][wl][1] = dot2<T>(p1[v], w1, acc[hl][wl][1]);
+                }
+            }
+        }
+#pragma unroll
+        for (int v = 0; v < RV; ++v) prev[v] = cur[v];
+        if (ul < NU) {
+#pragma unroll
+            for (int v = 0; v < RV; ++v) cur[v] = nxt[v];
+        }
+        // the step's products finish before the next step's reads issue (the
+        // compiler otherwise issues every row's reads first and runs out of
+        // registers holding them)
+#pragma unroll
+        for (int hl = 0; hl < THL; ++hl)
+#pragma unroll
+            for (int wl = 0; wl < kTileTWL; ++wl) asm volatile("" : "+v"(acc[hl][wl][0]), "+v"(acc[hl][wl][1]));
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// ============================ LDS-tiled, persistent (7 x 7) ==================
+//
+// The 7x7 case of the LDS-tiled dgrad with two resident blocks a CU, each
+// walking a contiguous run of the tiles of one channel block: the weight
+// pairs are built once a block, and while one block waits for its next
+// window the other multiplies.  A lane owns 4 x 7 pixels x 2 channels, so
+// every window row it reads and pairs feeds twice the outputs of the two-row
+// lane tile; a block tile is 8 x 28 pixels x 64 channels.  The products are
+// v_dot2 instructions, which a SIMD issues at about one every 6 cycles with
+// two waves resident (measured), so the kernel is bound by that issue rate.
+constexpr int kPipeTHL = 4;                       // lane tile rows
+constexpr int kPipeTH = kPipeTHL * kTilePBH;      // block tile rows
+constexpr int kPipeBlocksPerCU = 2;
+
+template <int R, int S>
+struct PipeGeo {
+    static constexpr int NL = (R + 1) / 2;
+    static constexpr int WR = kPipeTH + R - 1;                // window rows
+    static constexpr int CG = (kTileTW + S - 1 + 7) / 8;      // 8-pixel column groups a row
+    static constexpr int WC = CG * 8;                         // window row pitch (pixels)
+    static constexpr int NLD = WR * CG;                       // load instructions a window
+    static constexpr int LPW = (NLD + 3) / 4;                 // of them a wave
+    // the window, then the slots of the 4 LPW - NLD spare loads
+    static constexpr int WIN_BYTES = 4 * LPW * 1024;
+    static constexpr int RAW_BYTES = (kTileCB * R * S * 2 + 1023) / 1024 * 1024;
+    static constexpr int LDS = WIN_BYTES + RAW_BYTES;   // two blocks fit a CU
+};
+
+struct PipeArgs {
+    const void* dy;
+    const void* w;
+    void* dx;
+    uint32_t dy_bytes, w_bytes, dx_bytes;
+    int N, H, W, C, Ho, Wo, pad_h, pad_w;
+    int tiles_h, tiles_w;
+    int tiles_cb;      // tiles of one channel block: N * tiles_h * tiles_w
+    int bq, br;        // blocks a channel block: bq + 1 for the first br, bq for the rest
+    int flip;          // 1: use the filter rotated by 180 degrees (depthwise forward)
+    FastDiv fd_tw, fd_th;   // division by tiles_w, tiles_h
+};
+
+template <typename T, int R, int S>
+__global__ __launch_bounds__(256, kPipeBlocksPerCU) void dw_tilep_kernel(const PipeArgs a) {
+    using G = PipeGeo<R, S>;
+    constexpr int NL = G::NL, WC = G::WC, CG = G::CG, NLD = G::NLD, LPW = G::LPW;
+    extern __shared__ __attribute__((aligned(16))) unsigned char lds[];
+    unsigned char* const raw_b = lds + G::WIN_BYTES;
+    const unsigned short* const raw = reinterpret_cast<const unsigned short*>(raw_b);
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    // block -> channel block cb (bq or bq + 1 blocks each) and its run of tiles
+    const int bid = blockIdx.x;
+    const int big = a.br * (a.bq + 1);
+    int cb, j, nb;
+    if (bid < big) {
+        nb = a.bq + 1;
+        cb = bid / nb;
+        j = bid - cb * nb;
+    } else {
+        nb = a.bq;
+        const int b = bid - big;
+        cb = a.br + b / nb;
+        j = b - (b / nb) * nb;
+    }
+    const int t_lo = int(int64_t(j) * a.tiles_cb / nb);
+    const int t_hi = int(int64_t(j + 1) * a.tiles_cb / nb);
+    if (t_lo >= t_hi) return;   // block-uniform
+    const int c0 = cb * kTileCB;
+
+    const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
+    const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
+    const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
+
+    // tile t of the channel block: image n, rows h0 .., columns w0 .. (raster
+    // order within an image, so consecutive tiles share halo columns or rows)
+    auto tile_of = [&](int t, int& n, int& h0, int& w0) {
+        const int b1 = fdiv(t, a.fd_tw);
+        const int tw = t - b1 * a.tiles_w;
+        n = fdiv(b1, a.fd_th);
+        h0 = (b1 - n * a.tiles_h) * kPipeTH;
+        w0 = tw * kTileTW;
+    };
+    // Window load i of this wave (instruction wave + 4 i: window row r, pixels
+    // 8 g .. 8 g + 7, 8 lanes a pixel) of the tile at (n, h0, w0); window pixel
+    // (row, col) holds dY(h0 + pad_h - (R-1) + row, w0 + pad_w - (S-1) + col),
+    // zero outside the image.  The row pitch is whole 8-pixel groups, so no
+    // lane's slot belongs to another row and nothing here branches per lane
+    // (divergent branches in the unrolled tile loop cost the register file).
+    const int chunk = lane & 7, lpx = lane >> 3;
+    const bool cin = c0 + chunk * 8 < a.C;
+    const int pix_b = a.C * 2;
+    const int lane_off = lpx * pix_b + (c0 + chunk * 8) * 2;
+    // Every wave issues LPW loads; the spare ones read zeros into slots
+    // nothing reads, so no branch splits the tile loop.
+    auto issue = [&](int i, int n, int h0, int w0) {
+        // the wave index laundered per call: the scalar terms of the 4 x
+        // LPW loads are not hoisted out of the tile loop (register pressure)
+        int wv = wave;
+        asm volatile("" : "+s"(wv));
+        const int jj = wv + 4 * i;
+        const int r = jj / CG, g = jj - (jj / CG) * CG;
+        const int u = h0 + a.pad_h - (R - 1) + r;
+        const int v00 = w0 + a.pad_w - (S - 1) + 8 * g;
+        const bool ok = jj < NLD && cin && unsigned(u) < unsigned(a.Ho) && unsigned(v00 + lpx) < unsigned(a.Wo);
+        const int off = ((n * a.Ho + u) * a.Wo + v00) * pix_b + lane_off;
+        // LDS slot (r * WC + 8 g) * 128 = jj * 1024 (the row pitch is CG groups)
+        dma16(rdy, lds + jj * 1024, ok ? uint32_t(off) : kOob, 0);
+    };
+
+    // ---- the block's filters (64 channels x R*S taps, contiguous in W; rows
+    // past C read zeros) and the first tile's window ----
+    int n, h0, w0;
+    tile_of(t_lo, n, h0, w0);
+#pragma unroll
+    for (int i = 0; i < G::RAW_BYTES / 1024; ++i)
+        if ((i & 3) == wave) dma16(rw, raw_b + i * 1024, uint32_t(c0 * R * S * 2 + i * 1024 + lane * 16), 0);
+#pragma unroll
+    for (int i = 0; i < LPW; ++i) issue(i, n, h0, w0);
+    wait_vm<0>();
+    __syncthreads();
+
+    // ---- weight pairs, as in the one-tile kernel: word (i, t, ch) =
+    // (W[c][2i][t], W[c][2i+1][t]) built in place over the staged filter ----
+    constexpr int WTS = NL * S * kTileCB;
+    constexpr int WPT = (WTS + 255) / 256;
+    static_assert(WTS * 4 <= G::RAW_BYTES, "weight pairs fit over the staged filter");
+    const unsigned short* const wch = raw + (tid % kTileCB) * R * S;
+    uint32_t word[WPT];
+#pragma unroll
+    for (int k = 0; k < WPT; ++k) {
+        const int it = wave + (256 / kTileCB) * k;
+        word[k] = 0u;
+        if (it < NL * S) {
+            const int i = it / S, t = it - (it / S) * S;
+            auto tap = [&](int r) {
+                return a.flip ? uint32_t(wch[(R - 1 - r) * S + (S - 1 - t)]) : uint32_t(wch[r * S + t]);
+            };
+            const uint32_t lo = tap(2 * i);
+            const uint32_t hi = 2 * i + 1 < R ? tap(2 * i + 1) : 0u;
+            word[k] = lo | (hi << 16);
+        }
+    }
+    __syncthreads();
+    uint32_t* const wts = reinterpret_cast<uint32_t*>(raw_b);
+#pragma unroll
+    for (int k = 0; k < WPT; ++k)
+        if (wave + (256 / kTileCB) * k < NL * S) wts[tid + 256 * k] = word[k];
+    __syncthreads();
+    const int cp = lane & 31;
+    const int pb = 2 * wave + (lane >> 5);
+    const int lr0 = (pb / kTilePBW) * kPipeTHL, lc0 = (pb % kTilePBW) * kTileTWL;
+    uint32_t wp[NL][S][2];
+#pragma unroll
+    for (int i = 0; i < NL; ++i)
+#pragma unroll
+        for (int t = 0; t < S; ++t) {
+            const i32x2 v = *reinterpret_cast<const i32x2*>(wts + (i * S + t) * kTileCB + cp * 2);
+            wp[i][t][0] = uint32_t(v[0]);
+            wp[i][t][1] = uint32_t(v[1]);
+        }
+
+    // ---- the run: multiply tile t, let every wave finish reading the window,
+    // start the next window's loads over it, store tile t, and wait for the
+    // loads (the other block on the CU multiplies meanwhile) ----
+#pragma unroll 1
+    for (int t = t_lo; t < t_hi; ++t) {
+        const bool more = t + 1 < t_hi;
+        int n1 = n, h1 = h0, w1 = w0;
+        if (more) tile_of(t + 1, n1, h1, w1);
+        const uint32_t* const win = reinterpret_cast<const uint32_t*>(lds) + (lr0 * WC + lc0) * 32 + cp;
+        float acc[kPipeTHL][kTileTWL][2];
+        tile_accumulate_pf<T, R, S, kPipeTHL, WC>(win, wp, acc);
+        // the sums are complete here: otherwise the compiler sinks the last
+        // steps' products past the barrier among the stores, where they
+        // overflow the register file
+#pragma unroll
+        for (int hl = 0; hl < kPipeTHL; ++hl)
+#pragma unroll
+            for (int wl = 0; wl < kTileTWL; ++wl) asm volatile("" : "+v"(acc[hl][wl][0]), "+v"(acc[hl][wl][1]));
+        __syncthreads();
+        if (more) {
+#pragma unroll
+            for (int i = 0; i < LPW; ++i) issue(i, n1, h1, w1);
+        }
+        // stores of pixels outside dX (or channels past C) are dropped by the
+        // buffer range check
+        {
+            const int c = c0 + 2 * cp, hh = h0 + lr0, ww = w0 + lc0;
+            const uint32_t pix = uint32_t(a.C) * 2u;
+            const uint32_t off0 = uint32_t(((n * a.H + hh) * a.W + ww) * a.C + c) * 2u;
+#pragma unroll
+            for (int hl = 0; hl < kPipeTHL; ++hl)
+#pragma unroll
+                for (int wl = 0; wl < kTileTWL; ++wl) {
+                    const bool in = c < a.C && hh + hl < a.H && ww + wl < a.W;
+                    const uint32_t off = off0 + uint32_t(hl * a.W + wl) * pix;
+                    buf_store4(int(pack2<T>(acc[hl][wl][0], acc[hl][wl][1])), rdx, in ? off : kOob);
+                }
+        }
+        wait_vm<0>();
+        __syncthreads();
+        n = n1; h0 = h1; w0 = w1;
+    }
 }
 
 // ============================ rotated filter ================================
@@ -822,6 +1090,9 @@ std::string dw_stream_reason(const Prob& p, int cpl) {
     return "";
 }
 
+// 7x7 problems (in dgrad terms) run on the persistent kernel unless tune 1
+bool dw_tiled_persist_applies(const Prob& p, int tune) { return p.r == 7 && p.s == 7 && tune != 1; }
+
 std::string dw_tiled_reason(const Prob& p) {
     if (!(p.groups == p.c && p.groups == p.k)) return "depthwise kernels need groups == C == K";
     if (p.stride != 1) return "the LDS-tiled depthwise dgrad needs stride 1";
@@ -897,9 +1168,54 @@ Prob fwd_as_dgrad(const Prob& p) {
     return q;
 }
 
+template <typename T>
+int launch_tilep_t(const PipeArgs& a, int blocks, hipStream_t st) {
+    auto kern = dw_tilep_kernel<T, 7, 7>;
+    constexpr size_t lds = PipeGeo<7, 7>::LDS;
+    static bool attr_set = false;   // per instance; idempotent if raced
+    if (!attr_set) {
+        if (hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                                int(lds)) != hipSuccess)
+            return CNHWC_HIP_ERROR;
+        attr_set = true;
+    }
+    hipLaunchKernelGGL(kern, dim3(blocks), dim3(256), lds, st, a);
+    return CNHWC_OK;
+}
+
+// The persistent 7x7 kernel: two blocks a CU (more when there are more channel
+// blocks than that), each channel block's tiles dealt to its blocks in
+// contiguous runs.
+int launch_tiled_persistent(const Prob& p, int flip, const void* dy, const void* w, void* dx,
+                            hipStream_t st) {
+    PipeArgs a{};
+    a.flip = flip;
+    a.dy = dy; a.w = w; a.dx = dx;
+    a.dy_bytes = uint32_t(p.n * p.ho * p.wo * p.k * 2);
+    a.w_bytes = uint32_t(p.k * p.r * p.s * 2);
+    a.dx_bytes = uint32_t(p.n * p.h * p.w * p.c * 2);
+    a.N = int(p.n); a.H = int(p.h); a.W = int(p.w); a.C = int(p.c); a.Ho = int(p.ho); a.Wo = int(p.wo);
+    a.pad_h = p.pad_h; a.pad_w = p.pad_w;
+    a.tiles_h = int((p.h + kPipeTH - 1) / kPipeTH);
+    a.tiles_w = int((p.w + kTileTW - 1) / kTileTW);
+    const int64_t cblocks = (p.c + kTileCB - 1) / kTileCB;
+    const int64_t tiles_cb = int64_t(a.N) * a.tiles_h * a.tiles_w;
+    const int64_t blocks =
+        std::max<int64_t>(cblocks, std::min<int64_t>(kPipeBlocksPerCU * kNumCUs, tiles_cb * cblocks));
+    a.tiles_cb = int(tiles_cb);
+    a.bq = int(blocks / cblocks);
+    a.br = int(blocks % cblocks);
+    a.fd_tw = make_fastdiv(uint32_t(a.tiles_w));
+    a.fd_th = make_fastdiv(uint32_t(a.tiles_h));
+    return p.dtype == CNHWC_BF16 ? launch_tilep_t<BF16>(a, int(blocks), st)
+                                 : launch_tilep_t<F16>(a, int(blocks), st);
+}
+
 // p in dgrad terms (dy: N x Ho x Wo x C in, dx: N x H x W x C out);
-// flip: read the filter rotated by 180 degrees
-int launch_tiled(const Prob& p, int flip, const void* dy, const void* w, void* dx, hipStream_t st) {
+// flip: read the filter rotated by 180 degrees; tune 1 keeps 7x7 on the
+// one-tile-per-block kernel
+int launch_tiled(const Prob& p, int flip, int tune, const void* dy, const void* w, void* dx, hipStream_t st) {
+    if (dw_tiled_persist_applies(p, tune)) return launch_tiled_persistent(p, flip, dy, w, dx, st);
     TileArgs a{};
     a.flip = flip;
     a.dy = dy; a.w = w; a.dx = dx;
@@ -982,9 +1298,9 @@ int launch_rotated(const Prob& p, const Plan& pl, int rot, const void* dy, const
 
 }  // namespace
 
-int launch_dgrad_dw_tiled(const Prob& p, const Plan&, const void* dy, const void* w, void* dx,
+int launch_dgrad_dw_tiled(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
                           hipStream_t st) {
-    return launch_tiled(p, 0, dy, w, dx, st);
+    return launch_tiled(p, 0, pl.tune, dy, w, dx, st);
 }
 
 int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const void* w, void* dx,
@@ -992,9 +1308,15 @@ int launch_dgrad_dw_rotated(const Prob& p, const Plan& pl, const void* dy, const
     return launch_rotated(p, pl, 1, dy, w, dx, st);
 }
 
-int launch_fwd_dw_tiled(const Prob& p, const Plan&, const void* x, const void* w, void* y,
+int launch_fwd_dw_tiled(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,
                         hipStream_t st) {
-    return launch_tiled(fwd_as_dgrad(p), 1, x, w, y, st);
+    return launch_tiled(fwd_as_dgrad(p), 1, pl.tune, x, w, y, st);
+}
+
+bool dw_tiled_persist_taken(const Prob& p, const Plan& pl) {
+    if (pl.variant == CNHWC_VAR_DGRAD_DW_TILED) return dw_tiled_persist_applies(p, pl.tune);
+    if (pl.variant == CNHWC_VAR_FWD_DW_TILED) return dw_tiled_persist_applies(fwd_as_dgrad(p), pl.tune);
+    return false;
 }
 
 int launch_fwd_dw_rotated(const Prob& p, const Plan& pl, const void* x, const void* w, void* y,

@@ -149,7 +149,8 @@ std::string plan_name(const Prob& p, const Plan& pl) {
         std::snprintf(buf, sizeof buf, "dgrad_dw_rot_%s_f%lldx%lld_p%dx%d", dt(p),
                       (long long)p.r, (long long)p.s, p.pad_h, p.pad_w); break;
     case CNHWC_VAR_DGRAD_DW_TILED:
-        std::snprintf(buf, sizeof buf, "dgrad_dw_tiled_%s_f%lldx%lld", dt(p), (long long)p.r,
+        std::snprintf(buf, sizeof buf, "dgrad_dw_tiled%s_%s_f%lldx%lld",
+                      dw_tiled_persist_taken(p, pl) ? "_persist" : "", dt(p), (long long)p.r,
                       (long long)p.s); break;
     case CNHWC_VAR_DGRAD_GENERIC:
         std::snprintf(buf, sizeof buf, "dgrad_generic_%s", dt(p)); break;
@@ -174,7 +175,8 @@ std::string plan_name(const Prob& p, const Plan& pl) {
     case CNHWC_VAR_FWD_GENERIC:
         std::snprintf(buf, sizeof buf, "fwd_generic_%s", dt(p)); break;
     case CNHWC_VAR_FWD_DW_TILED:
-        std::snprintf(buf, sizeof buf, "fwd_dw_tiled_%s_f%lldx%lld", dt(p), (long long)p.r,
+        std::snprintf(buf, sizeof buf, "fwd_dw_tiled%s_%s_f%lldx%lld",
+                      dw_tiled_persist_taken(p, pl) ? "_persist" : "", dt(p), (long long)p.r,
                       (long long)p.s); break;
     case CNHWC_VAR_FWD_DW_ROTATED:
         std::snprintf(buf, sizeof buf, "fwd_dw_rot_%s_f%lldx%lld_p%dx%d", dt(p),

@@ -126,6 +126,9 @@ std::string dgrad_igemm_reason(const Prob& p, bool pointwise);
 std::string dw_stream_reason(const Prob& p, int cpl);
 std::string dw_rotated_reason(const Prob& p);
 std::string dw_tiled_reason(const Prob& p);
+// the LDS-tiled depthwise variant (dgrad or forward) runs the persistent 7x7 kernel
+bool dw_tiled_persist_taken(const Prob& p, const Plan& pl);
+bool dw_tiled_persist_applies(const Prob& p, int tune);
 std::string fwd_dw_tiled_reason(const Prob& p);
 std::string dgrad_grouped_reason(const Prob& p);
 std::string fwd_dw_rotated_reason(const Prob& p);

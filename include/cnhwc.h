@@ -228,8 +228,10 @@ const char* cnhwc_last_error(void);
  * the filter transform and the dgrad kernels for 1x1 shapes the pointwise row
  * kernel takes; split-K wgrad: the number of pixel splits per batch
  * chunk; depthwise rotated-filter: 1 runs one tap group, 2 two groups, both
- * with 8-column filter slices even for filters narrower than 8 columns; other
- * kernels ignore it);
+ * with 8-column filter slices even for filters narrower than 8 columns;
+ * depthwise LDS-tiled (dgrad and forward): 1 keeps 7x7 filters on the
+ * one-tile-per-block kernel instead of the persistent one; other kernels
+ * ignore it);
  * chunk_limit_bytes: the per-view byte limit of the chunk planner.  Pass NULL
  * to clear. */
 typedef struct cnhwc_override {

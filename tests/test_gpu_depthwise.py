@@ -127,6 +127,32 @@ def test_tiled_7x7(p):
         parity(p, "dgrad", 308)
 
 
+# the persistent 7x7 kernel: runs of several tiles a block (the C5 shape at
+# one image), a channel block with more blocks than tiles, ragged tiles
+PERSIST7 = [
+    DW(2, 37, 61, 200, 7, 7, 1, 3, 3),
+    DW(1, 56, 56, 384, 7, 7, 1, 3, 3),
+    DW(1, 9, 12, 16, 7, 7, 1, 2, 5),
+    DW(3, 30, 33, 136, 7, 7, 1, 3, 3, dtype="bf16"),
+]
+
+
+@pytest.mark.parametrize("p", PERSIST7, ids=ident)
+def test_tiled_7x7_persistent_matches_one_tile_kernel_bitwise(p):
+    """The persistent kernel adds every product in the one-tile kernel's order
+    (filter row pairs from the last, columns ascending), so the two agree bit
+    for bit; both against the oracle."""
+    ab, af, wb, wf = operands(p, "dgrad", 309)
+    with api.override(variant=api.VAR_DGRAD_DW_TILED):
+        assert "dw_tiled_persist" in api.cnhwc_plan(p, api.OP_DGRAD)[0]
+        a = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    with api.override(variant=api.VAR_DGRAD_DW_TILED, tune=1):
+        assert "dw_tiled_persist" not in api.cnhwc_plan(p, api.OP_DGRAD)[0]
+        b = run_gpu(p, "dgrad", ab, wb).cpu().numpy()
+    assert np.array_equal(a, b)
+    parity(p, "dgrad", 309)
+
+
 @pytest.mark.parametrize("p,var,cpl", [(DW(1, 17, 19, 32, 3, 3, 1, 1, 1), api.VAR_DGRAD_DW_STREAM, 8),
                                        (DW(1, 17, 30, 64, 5, 5, 1, 2, 2), api.VAR_DGRAD_DW_TILED, 0),
                                        (DW(1, 17, 19, 32, 7, 7, 2, 3, 3), api.VAR_DGRAD_DW_STREAM, 2),
