@@ -831,18 +831,18 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
     const __amdgpu_buffer_rsrc_t rdx = make_rsrc(a.dx, a.dx_bytes);
 
-    // ---- stage the dY window as row-pair words: pair row m, column v holds
+    // The dY window is staged as row-pair words: pair row m, column v holds
     // for each of the 8 channels (dY(h0 - ph2 + 2m, w0 - pw2 + v), the row
     // below) in one word.  Layout [m][v][8 channels] with 8 pad words after
     // every 8 columns and a pair-row stride of a.row_dw words (= 32 mod 64):
     // a 64-bit read of 32 lanes (4 channel pairs x 4 column groups 8 columns
     // apart x 2 row groups one pair row apart) then covers the 64 banks once.
-    // Every lane issues a batch of its loads before writing any of them.
+    // A lane loads a batch of its window positions before writing any.
     uint32_t* win = smem;
     const int npp = (a.IHB / 2) * a.IWB;
     constexpr int kWinBatch = 4;
-    for (int q0 = tid; q0 < npp; q0 += kWinBatch * NT) {
-        i32x4 top[kWinBatch], bot[kWinBatch];
+    i32x4 top[kWinBatch], bot[kWinBatch];
+    auto win_load = [&](int q0) {
 #pragma unroll
         for (int b = 0; b < kWinBatch; ++b) {
             const int q = q0 + b * NT;
@@ -853,6 +853,8 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
             top[b] = buf_load16(rdy, vin && u >= 0 && u < a.Ho ? off : kOob);
             bot[b] = buf_load16(rdy, vin && u + 1 >= 0 && u + 1 < a.Ho ? off + uint32_t(a.Wo * a.C * 2) : kOob);
         }
+    };
+    auto win_write = [&](int q0) {
 #pragma unroll
         for (int b = 0; b < kWinBatch; ++b) {
             const int q = q0 + b * NT;
@@ -871,41 +873,58 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
                 dst[1] = hi;
             }
         }
+    };
+
+    // ---- the block's filter slice (8 channels x R x S halves, contiguous in
+    // W: R*S 16-byte pieces) and the window's first batch go out together;
+    // the slice lands in the window's LDS, where the pair words are built
+    // from it before the window overwrites it (the window region holds at
+    // least 18 R S bytes, the slice 16 R S) ----
+    constexpr int kRawPT = (kRotMaxF * kRotMaxF + NT - 1) / NT;
+    const int nraw = a.R * a.S;
+    const int nraw_pt = (nraw + NT - 1) / NT;
+    i32x4 rawv[kRawPT];
+#pragma unroll
+    for (int k = 0; k < kRawPT; ++k) {
+        const int q = tid + k * NT;
+        if (k < nraw_pt) rawv[k] = buf_load16(rw, q < nraw ? uint32_t(c0 * nraw * 2 + q * 16) : kOob);
     }
-    // ---- stage the filter pair words: even set [k][t][8 channels] =
-    // (W'(2k, t), W'(2k+1, t)), odd set = (W'(2k-1, t), W'(2k, t)), with W'
-    // the correlation's filter (rotated for the dgrad), zero outside it ----
+    win_load(tid);
+    wait_vm<2 * kWinBatch>();   // the slice (the window batch stays in flight)
+#pragma unroll
+    for (int k = 0; k < kRawPT; ++k) {
+        const int q = tid + k * NT;
+        if (k < nraw_pt && q < nraw) reinterpret_cast<i32x4*>(win)[q] = rawv[k];
+    }
+    __syncthreads();
+    // ---- filter pair words: even set [k][t][8 channels] = (W'(2k, t),
+    // W'(2k+1, t)), odd set = (W'(2k-1, t), W'(2k, t)), with W' the
+    // correlation's filter (rotated for the dgrad), zero outside it ----
+    const unsigned short* raw = reinterpret_cast<const unsigned short*>(win);
     uint32_t* wpe = smem + (a.IHB / 2) * a.row_dw;
     const int tpad = a.tslices * TB;
     const int nwp = a.rpairs * tpad * kRotCB;
     uint32_t* wpo = wpe + nwp;
-    constexpr int kWBatch = 8;
-    for (int q0 = tid; q0 < nwp; q0 += kWBatch * NT) {
-        uint32_t t0[kWBatch], t1[kWBatch], t2[kWBatch];   // rows 2k-1, 2k, 2k+1
-#pragma unroll
-        for (int b = 0; b < kWBatch; ++b) {
-            const int q = q0 + b * NT;
-            const int ch = q % kRotCB;
-            const int t = (q / kRotCB) % tpad;
-            const int k = q / (kRotCB * tpad);
-            const uint32_t base = uint32_t(c0 + ch) * (a.R * a.S);
-            auto tap_off = [&](int r) {
-                if (q >= nwp || t >= a.S || r < 0 || r >= a.R) return kOob;
-                const uint32_t e = a.rot ? (a.R - 1 - r) * a.S + (a.S - 1 - t) : r * a.S + t;
-                return (base + e) * 2u;
-            };
-            t0[b] = buf_load2(rw, tap_off(2 * k - 1));
-            t1[b] = buf_load2(rw, tap_off(2 * k));
-            t2[b] = buf_load2(rw, tap_off(2 * k + 1));
-        }
-#pragma unroll
-        for (int b = 0; b < kWBatch; ++b) {
-            const int q = q0 + b * NT;
-            if (q < nwp) {
-                wpe[q] = t1[b] | (t2[b] << 16);
-                wpo[q] = t0[b] | (t1[b] << 16);
-            }
-        }
+    for (int q = tid; q < nwp; q += NT) {
+        const int ch = q % kRotCB;
+        const int t = (q / kRotCB) % tpad;
+        const int k = q / (kRotCB * tpad);
+        auto tap = [&](int r) -> uint32_t {
+            if (t >= a.S || r < 0 || r >= a.R) return 0u;
+            const int e = a.rot ? (a.R - 1 - r) * a.S + (a.S - 1 - t) : r * a.S + t;
+            return raw[ch * nraw + e];
+        };
+        const uint32_t t0 = tap(2 * k - 1), t1 = tap(2 * k), t2 = tap(2 * k + 1);
+        wpe[q] = t1 | (t2 << 16);
+        wpo[q] = t0 | (t1 << 16);
+    }
+    __syncthreads();   // the slice is read: the window goes over it
+    wait_vm<0>();
+    win_write(tid);
+    for (int q0 = tid + kWinBatch * NT; q0 < npp; q0 += kWinBatch * NT) {
+        win_load(q0);
+        wait_vm<0>();
+        win_write(q0);
     }
     __syncthreads();
 
