@@ -969,6 +969,21 @@ static bool grow_geometry(const Prob& p, GrowArgs* a, size_t* lds) {
     while (TH > 1 && need(TH, TW).second > 160 * 1024) --TH;
     while (TW > 8 && need(TH, TW).second > 160 * 1024) TW -= 8;
     if (need(TH, TW).second > 160 * 1024) return false;
+    {
+        // fewer tiles than CUs: halve the tile width and even out the rows
+        const int64_t tiles = p.n * ((p.ho + TH - 1) / TH) * ((p.wo + TW - 1) / TW);
+        if (tiles < kNumCUs && TW >= 16) {
+            const int64_t tw2 = (TW + 1) / 2;
+            const int64_t th_max = std::min<int64_t>(p.ho, kBM / tw2);
+            const int64_t nth = (p.ho + th_max - 1) / th_max;
+            const int64_t th2 = (p.ho + nth - 1) / nth;
+            const int64_t tiles2 = p.n * nth * ((p.wo + tw2 - 1) / tw2);
+            if (tiles2 <= kNumCUs && tiles2 > tiles && need(th2, tw2).second <= 160 * 1024) {
+                TH = th2;
+                TW = tw2;
+            }
+        }
+    }
     a->TH = int(TH); a->TW = int(TW);
     a->IH = int((TH - 1) * s + p.r); a->IW = int((TW - 1) * s + p.s);
     a->ptiles_h = int((p.ho + TH - 1) / TH);
