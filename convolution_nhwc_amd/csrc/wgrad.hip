@@ -62,7 +62,7 @@ struct WgArgs {
     int P;                       // output pixels of the chunk
     int kblocks, jblocks, tiles; // per group: ceil(Kg/128), ceil(Cg/BJ); all tiles
     int splits;                  // pixel splits of the chunk
-    int remap;                   // 1: deal logical blocks to XCDs in contiguous runs
+    int remap;                   // 1: deal logical blocks to XCDs in contiguous runs (any block count)
     FastDiv div_hw, div_w;       // by Ho*Wo, by Wo
     int step_ho, step_wo;        // 32 output pixels = step_ho rows + step_wo columns (32 / Wo, 32 % Wo)
     int64_t split_elems;         // K*R*S*Cg (workspace stride of one split)
@@ -107,7 +107,14 @@ __global__ __launch_bounds__(NW * 64, 2) void wgrad_splitk_kernel(const WgArgs a
 
     // ---- block -> (split, group, k block, tap, j block) ----
     int bid = blockIdx.x;
-    if (a.remap) bid = (bid & 7) * (gridDim.x >> 3) + (bid >> 3);
+    if (a.remap) {
+        // XCD x = bid % 8 runs blocks x, x + 8, ...; give it the contiguous
+        // logical run [x q + min(x, r), ...) (q + 1 blocks for x < r), so the
+        // taps and j blocks of one pixel split -- which read the same dY rows
+        // -- share an L2
+        const int q = int(gridDim.x >> 3), rr = int(gridDim.x & 7), x = bid & 7;
+        bid = x * q + min(x, rr) + (bid >> 3);
+    }
     const int split = bid / a.tiles;
     int tile = bid - split * a.tiles;
     const int jb = tile % a.jblocks;
@@ -461,7 +468,7 @@ int launch_wgrad_splitk(const Prob& p, const Plan& pl, const void* x, const void
     a.split_elems = wgrad_split_elems(p);
     const int64_t blocks = int64_t(a.tiles) * splits;
     if (blocks > (int64_t(1) << 31) - 1) return CNHWC_UNSUPPORTED;
-    a.remap = blocks % 8 == 0 ? 1 : 0;
+    a.remap = 1;
     const bool pw = pl.variant == CNHWC_VAR_WGRAD_POINTWISE;
     const bool bf = p.dtype == CNHWC_BF16;
 #define CNHWC_WG(T, BJ, PW, NW) hipLaunchKernelGGL((wgrad_splitk_kernel<T, BJ, PW, NW>), dim3(unsigned(blocks)), \
