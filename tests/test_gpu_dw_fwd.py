@@ -63,6 +63,22 @@ def test_fwd_tiled_7x7_several_channel_blocks():
         parity(p, "fwd", 402)
 
 
+@pytest.mark.parametrize("p", [DW(2, 30, 33, 136, 7, 7, 3, 3), DW(1, 56, 56, 128, 7, 7, 2, 4, dtype="bf16")],
+                         ids=ident)
+def test_fwd_tiled_7x7_persistent_matches_one_tile_kernel_bitwise(p):
+    """The forward 7x7 (rotated filter) on the persistent kernel equals the
+    one-tile kernel (tune 1) bit for bit: same products in the same order."""
+    ab, af, wb, wf = operands(p, "fwd", 403)
+    with api.override(variant=api.VAR_FWD_DW_TILED):
+        assert "dw_tiled_persist" in api.cnhwc_plan(p, api.OP_FWD)[0]
+        a = run_gpu(p, "fwd", ab, wb).cpu().numpy()
+    with api.override(variant=api.VAR_FWD_DW_TILED, tune=1):
+        assert "dw_tiled_persist" not in api.cnhwc_plan(p, api.OP_FWD)[0]
+        b = run_gpu(p, "fwd", ab, wb).cpu().numpy()
+    assert np.array_equal(a, b)
+    parity(p, "fwd", 403)
+
+
 @pytest.mark.parametrize("tune", [0, 1, 2], ids=["split", "onegroup", "wideslice"])
 @pytest.mark.parametrize("p", ROT, ids=ident)
 def test_fwd_rotated_parity(p, tune):
