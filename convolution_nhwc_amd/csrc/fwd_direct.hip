@@ -577,6 +577,25 @@ __global__ __launch_bounds__(kGrThreads, 1) void fwd_grouped_rows_kernel(const G
     const __amdgpu_buffer_rsrc_t rw = make_rsrc(a.w, a.w_bytes);
     const __amdgpu_buffer_rsrc_t ry = make_rsrc(a.y, a.y_bytes);
 
+    // DG 2: the first batch of this wave's filter slice (set `wave`, one set a
+    // wave) goes out before the halo, so it is not queued behind the halo's
+    // loads; its elements are placed while the halo streams in.  The slice
+    // is contiguous in W and a multiple of 8 elements (each set's slice
+    // starts on a 16-byte boundary): 16-byte chunks, kGrFB a lane a batch.
+    constexpr int kGrFB = 8;
+    const int dg_nel = a.bn * TAPS * a.Cg;
+    const int dg_nch = DG == 2 && wave < a.gsets ? dg_nel / 8 : 0;
+    i32x4 fv[kGrFB];
+    auto dg_issue = [&](int c0) {
+        const uint32_t gbase = uint32_t(wave) * uint32_t(dg_nel);
+#pragma unroll
+        for (int u = 0; u < kGrFB; ++u) {
+            const int ch = c0 + u * 64 + lane;
+            fv[u] = buf_load16(rw, ch < dg_nch ? (gbase + uint32_t(ch) * 8u) * 2u : kOob);
+        }
+    };
+    if constexpr (DG == 2) dg_issue(0);
+
     // ---- halo: element e = pixel * cpr + stored chunk, holding source chunk
     // (stored ^ (pixel & 7)); pixels outside the image read zeros ----
     const int hchunks = a.IH * a.IW * cpr;
@@ -608,30 +627,28 @@ __global__ __launch_bounds__(kGrThreads, 1) void fwd_grouped_rows_kernel(const G
     auto load_w = [&](int gs, i32x4 (&wf)[TAPS][FN]) {
         if constexpr (DG == 2) {
             {
-                // The set's filter slice is contiguous in W (stored rows g*Cg + i of
-                // its groups, each TAPS x Kg): coalesced 2-byte loads, written into
-                // this wave's part of the (not yet used) output tile in fragment
-                // order [o][tap][i] (i contiguous, tap rotated).
-                const int nel = a.bn * TAPS * a.Cg;
-                unsigned short* wl = reinterpret_cast<unsigned short*>(os) + wave * nel;
-                const uint32_t gbase = uint32_t(gs) * uint32_t(nel);
+                // Each element of the slice (batches of chunks issued by
+                // dg_issue, the first before the halo) goes into this wave's
+                // part of the (not yet used) output tile in fragment order
+                // [o][tap][i] (i contiguous, tap rotated).
+                unsigned short* wl = reinterpret_cast<unsigned short*>(os) + wave * dg_nel;
 #pragma unroll 1
-                for (int e0 = 0; e0 < nel; e0 += 4 * 64) {
-                    unsigned short v[4];
+                for (int c0 = 0; c0 < dg_nch; c0 += kGrFB * 64) {
+                    if (c0 > 0) dg_issue(c0);
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int e = e0 + u * 64 + lane;
-                        v[u] = buf_load2(rw, e < nel ? (gbase + uint32_t(e)) * 2u : kOob);
-                    }
+                    for (int u = 0; u < kGrFB; ++u) {
+                        const int ch = c0 + u * 64 + lane;
+                        if (ch < dg_nch) {
 #pragma unroll
-                    for (int u = 0; u < 4; ++u) {
-                        const int e = e0 + u * 64 + lane;
-                        if (e < nel) {
-                            // stored order: ((gl*Cg + i)*TAPS + tap_st)*Kg + ol
-                            const int q = fdiv(e, a.fd_kg), ol = e - q * a.Kg;
-                            const int q2 = q / TAPS, tap_st = q - q2 * TAPS;
-                            const int gl = fdiv(q2, a.fd_cg), i = q2 - gl * a.Cg;
-                            wl[((gl * a.Kg + ol) * TAPS + (TAPS - 1 - tap_st)) * a.Cg + i] = v[u];
+                            for (int k = 0; k < 8; ++k) {
+                                // stored order: ((gl*Cg + i)*TAPS + tap_st)*Kg + ol
+                                const int e = ch * 8 + k;
+                                const int q = fdiv(e, a.fd_kg), ol = e - q * a.Kg;
+                                const int q2 = q / TAPS, tap_st = q - q2 * TAPS;
+                                const int gl = fdiv(q2, a.fd_cg), i = q2 - gl * a.Cg;
+                                wl[((gl * a.Kg + ol) * TAPS + (TAPS - 1 - tap_st)) * a.Cg + i] =
+                                    static_cast<unsigned short>(uint32_t(fv[u][k >> 1]) >> (16 * (k & 1)));
+                            }
                         }
                     }
                 }
