@@ -818,7 +818,16 @@ __global__ __launch_bounds__(256 * SPLIT, 1) void dw_rotated_kernel(const RotArg
     const int tid = threadIdx.x;
     const int lt = tid & 255, grp = tid >> 8;      // lane role within its group; tap group
     const int cp = lt & 3, cg = (lt >> 2) & 3, rg = lt >> 4;
+    // Blocks are dealt to the 8 XCDs round-robin (XCD = blockIdx % 8); remap
+    // so each XCD takes a contiguous run of the order below, channel block
+    // fastest: the blocks whose 16-byte channel slices share a pixel's
+    // 128-byte lines then share one L2, which fetches those dY lines once and
+    // merges their dX writes into whole lines
     int bid = blockIdx.x;
+    {
+        const int q = int(gridDim.x >> 3), rr = int(gridDim.x & 7), x = bid & 7;
+        bid = x * q + min(x, rr) + (bid >> 3);
+    }
     const int cb = bid % a.cblocks;
     bid /= a.cblocks;
     const int tw_ = bid % a.tiles_w;
