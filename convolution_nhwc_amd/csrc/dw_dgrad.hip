@@ -89,7 +89,14 @@ __global__ __launch_bounds__(256, 2) void dw_stream_kernel(const StreamArgs a) {
     constexpr int ND = CPL > 1 ? CPL / 2 : 1;        // 32-bit words per vector
     using V = typename VecT<CPL>::type;
 
-    const int64_t gid = int64_t(blockIdx.x) * blockDim.x + threadIdx.x;
+    // each XCD (blockIdx % 8) takes a contiguous run of blocks: neighbouring
+    // bands of a strip, which read the same halo rows of dY, share its L2
+    int bid = blockIdx.x;
+    {
+        const int q = int(gridDim.x >> 3), rr = int(gridDim.x & 7), x = bid & 7;
+        bid = x * q + min(x, rr) + (bid >> 3);
+    }
+    const int64_t gid = int64_t(bid) * blockDim.x + threadIdx.x;
     if (gid >= a.nthreads) return;
     const int cv = int(gid % a.ncv);
     int64_t rest = gid / a.ncv;

@@ -567,8 +567,15 @@ __global__ __launch_bounds__(kGrThreads, 1) void fwd_grouped_rows_kernel(const G
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int per_img = a.ptiles_h * a.ptiles_w;
-    const int n = blockIdx.x / per_img;
-    const int pt = blockIdx.x - n * per_img;
+    // each XCD (blockIdx % 8) takes a contiguous run of tiles: neighbouring
+    // tiles of an image, which read the same halo rows, share its L2
+    int bid = blockIdx.x;
+    {
+        const int q = int(gridDim.x >> 3), rr = int(gridDim.x & 7), x = bid & 7;
+        bid = x * q + min(x, rr) + (bid >> 3);
+    }
+    const int n = bid / per_img;
+    const int pt = bid - n * per_img;
     const int ho0 = (pt / a.ptiles_w) * a.TH, wo0 = (pt % a.ptiles_w) * a.TW;
     const int s = a.stride;
     const int cpr = a.C / 8;                       // 16-byte chunks per input pixel
