@@ -634,8 +634,16 @@ __global__ __launch_bounds__(256, kPipeBlocksPerCU) void dw_tilep_kernel(const P
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    // block -> channel block cb (bq or bq + 1 blocks each) and its run of tiles
-    const int bid = blockIdx.x;
+    // block -> channel block cb (bq or bq + 1 blocks each) and its tiles j,
+    // j + nb, j + 2 nb, ...: the nb blocks of a channel block take consecutive
+    // tiles at the same time, and each XCD (blockIdx % 8) a contiguous run of
+    // blocks, so the tiles that share halo rows and columns are loaded
+    // through one L2 at about the same time
+    int bid = blockIdx.x;
+    {
+        const int q = int(gridDim.x >> 3), rr = int(gridDim.x & 7), x = bid & 7;
+        bid = x * q + min(x, rr) + (bid >> 3);
+    }
     const int big = a.br * (a.bq + 1);
     int cb, j, nb;
     if (bid < big) {
@@ -648,9 +656,7 @@ __global__ __launch_bounds__(256, kPipeBlocksPerCU) void dw_tilep_kernel(const P
         cb = a.br + b / nb;
         j = b - (b / nb) * nb;
     }
-    const int t_lo = int(int64_t(j) * a.tiles_cb / nb);
-    const int t_hi = int(int64_t(j + 1) * a.tiles_cb / nb);
-    if (t_lo >= t_hi) return;   // block-uniform
+    if (j >= a.tiles_cb) return;   // block-uniform
     const int c0 = cb * kTileCB;
 
     const __amdgpu_buffer_rsrc_t rdy = make_rsrc(a.dy, a.dy_bytes);
@@ -696,7 +702,7 @@ __global__ __launch_bounds__(256, kPipeBlocksPerCU) void dw_tilep_kernel(const P
     // ---- the block's filters (64 channels x R*S taps, contiguous in W; rows
     // past C read zeros) and the first tile's window ----
     int n, h0, w0;
-    tile_of(t_lo, n, h0, w0);
+    tile_of(j, n, h0, w0);
 #pragma unroll
     for (int i = 0; i < G::RAW_BYTES / 1024; ++i)
         if ((i & 3) == wave) dma16(rw, raw_b + i * 1024, uint32_t(c0 * R * S * 2 + i * 1024 + lane * 16), 0);
@@ -749,10 +755,10 @@ __global__ __launch_bounds__(256, kPipeBlocksPerCU) void dw_tilep_kernel(const P
     // start the next window's loads over it, store tile t, and wait for the
     // loads (the other block on the CU multiplies meanwhile) ----
 #pragma unroll 1
-    for (int t = t_lo; t < t_hi; ++t) {
-        const bool more = t + 1 < t_hi;
+    for (int t = j; t < a.tiles_cb; t += nb) {
+        const bool more = t + nb < a.tiles_cb;
         int n1 = n, h1 = h0, w1 = w0;
-        if (more) tile_of(t + 1, n1, h1, w1);
+        if (more) tile_of(t + nb, n1, h1, w1);
         const uint32_t* const win = reinterpret_cast<const uint32_t*>(lds) + (lr0 * WC + lc0) * 32 + cp;
         float acc[kPipeTHL][kTileTWL][2];
         tile_accumulate_pf<T, R, S, kPipeTHL, WC>(win, wp, acc);
@@ -1219,8 +1225,8 @@ int launch_tilep_t(const PipeArgs& a, int blocks, hipStream_t st) {
 }
 
 // The persistent 7x7 kernel: two blocks a CU (more when there are more channel
-// blocks than that), each channel block's tiles dealt to its blocks in
-// contiguous runs.
+// blocks than that), each channel block's tiles dealt to its blocks in turn
+// (block j of nb takes tiles j, j + nb, ...).
 int launch_tiled_persistent(const Prob& p, int flip, const void* dy, const void* w, void* dx,
                             hipStream_t st) {
     PipeArgs a{};
